@@ -1,0 +1,142 @@
+/*
+ * kda_oracle.c -- plain fp64 CPU reference of the Kimi Delta Attention (KDA)
+ * recurrence.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load it; the library path never does.  It
+ * shares no source, header or table with the HIP implementation.
+ *
+ * What it computes, for every (sequence, head) independently, token by token,
+ * with a state S of dk rows (key channels) by dv columns (value channels):
+ *
+ *   1. decay   S[c][j] *= alpha_t[c]                 for every key channel c
+ *   2. recall  r[j]     = sum_c k_t[c] * S[c][j]      on the decayed state
+ *   3. correct S[c][j] += beta_t * k_t[c] * (v_t[j] - r[j])
+ *   4. read    o_t[j]   = scale * sum_c q_t[c] * S[c][j]   on the updated state
+ *
+ * Sources (the fact each step follows):
+ *  - "Kimi K3 architecture: KDA, MLA and MoE", section "KDA is a writable
+ *    state, not a smaller KV cache": the delta rule measures what the state
+ *    already holds for a key and writes the correction towards the new value;
+ *    the decay gate is per channel, so channels fade at different rates.
+ *  - "Kimi K3 Architecture Teardown", section "Hybrid Attention for 1M Tokens"
+ *    and Visual 5 ("One KDA step"): per token the state is decayed in every
+ *    channel, then a beta-scaled share of what is stored under the key is
+ *    erased, then the new key-value pair is written scaled by beta; the state
+ *    has a fixed size.
+ *  - "Kimi K3 Architecture: KDA, MoE, and Attention", section "Memory as a
+ *    First-Class Problem: Kimi Delta Attention": alpha is a channel-wise decay,
+ *    beta is one scalar used both to erase and to write, and the output is the
+ *    query read from the updated state.
+ * Readings where the pages are silent or disagree: erase and write are one
+ * correction computed from the decayed state (steps 2-3); the read happens
+ * after the correction; alpha scales rows (key channels); scale defaults to 1;
+ * no decay floor; inputs are taken exactly as stored (bf16 or fp32 upcast to
+ * fp64).
+ *
+ * Layouts (row-major, token-major): q,k [Ttot][H][dk], v [Ttot][H][dv],
+ * alpha [Ttot][H][dk], beta [Ttot][H], S0 [N][H][dk][dv].  Sequence n covers
+ * tokens [cu[n], cu[n+1]) of the packed token axis.  Only heads
+ * [h_begin, h_end) are computed; outputs hold those heads only:
+ * o [Ttot][nh][dv] and s_final [N][nh][dk][dv] (fp64), nh = h_end - h_begin.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { KDA_ORACLE_F32 = 0, KDA_ORACLE_BF16 = 1, KDA_ORACLE_F64 = 2 };
+
+/* Read element i of an array stored as fp32, bf16 (raw 16-bit pattern) or fp64. */
+static double load_elem(const void* p, int dtype, int64_t i)
+{
+    if (dtype == KDA_ORACLE_F32) return (double)((const float*)p)[i];
+    if (dtype == KDA_ORACLE_BF16) {
+        uint32_t bits = (uint32_t)((const uint16_t*)p)[i] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    return ((const double*)p)[i];
+}
+
+static int valid_dtype(int d) { return d == KDA_ORACLE_F32 || d == KDA_ORACLE_BF16 || d == KDA_ORACLE_F64; }
+
+/* Returns 0 on success, -1 on a bad argument, -2 if memory ran out. */
+int kda_oracle_forward(int64_t num_seqs, const int64_t* cu_seqlens,
+                       int32_t H, int32_t dk, int32_t dv,
+                       int32_t h_begin, int32_t h_end, double scale,
+                       const void* q, const void* k, const void* v, int32_t qkv_dtype,
+                       const void* alpha, int32_t alpha_dtype,
+                       const void* beta, int32_t beta_dtype,
+                       const void* s0, int32_t s0_dtype,
+                       double* o, double* s_final)
+{
+    if (num_seqs < 0 || !cu_seqlens || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    if (h_begin < 0 || h_end > H || h_begin >= h_end) return -1;
+    if (!q || !k || !v || !alpha || !beta || !o) return -1;
+    if (!valid_dtype(qkv_dtype) || !valid_dtype(alpha_dtype) || !valid_dtype(beta_dtype)) return -1;
+    if (s0 && !valid_dtype(s0_dtype)) return -1;
+    for (int64_t n = 0; n < num_seqs; ++n)
+        if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+
+    const int64_t nh = h_end - h_begin;
+    const int64_t units = num_seqs * nh;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < units; ++u) {
+        const int64_t n = u / nh;
+        const int64_t hl = u % nh;          /* head index within the output */
+        const int64_t h = h_begin + hl;     /* head index within the inputs */
+        double* S = (double*)malloc(sizeof(double) * (size_t)dk * (size_t)dv);
+        double* r = (double*)malloc(sizeof(double) * (size_t)dv);
+        if (!S || !r) {
+            free(S);
+            free(r);
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        /* initial state: S0 of this (sequence, head), or zeros */
+        for (int64_t c = 0; c < dk; ++c)
+            for (int64_t j = 0; j < dv; ++j)
+                S[c * dv + j] = s0 ? load_elem(s0, s0_dtype, ((n * H + h) * dk + c) * dv + j) : 0.0;
+
+        for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
+            const int64_t qk_base = (t * H + h) * dk;
+            const int64_t v_base = (t * H + h) * dv;
+            const double b = load_elem(beta, beta_dtype, t * H + h);
+
+            /* 1. decay every key channel (row) by its own alpha */
+            for (int64_t c = 0; c < dk; ++c) {
+                const double a = load_elem(alpha, alpha_dtype, qk_base + c);
+                for (int64_t j = 0; j < dv; ++j) S[c * dv + j] *= a;
+            }
+            /* 2. recall: what the decayed state associates with k_t */
+            for (int64_t j = 0; j < dv; ++j) r[j] = 0.0;
+            for (int64_t c = 0; c < dk; ++c) {
+                const double kc = load_elem(k, qkv_dtype, qk_base + c);
+                for (int64_t j = 0; j < dv; ++j) r[j] += kc * S[c * dv + j];
+            }
+            /* 3. erase and write as one correction scaled by the same beta */
+            for (int64_t c = 0; c < dk; ++c) {
+                const double kc = load_elem(k, qkv_dtype, qk_base + c);
+                for (int64_t j = 0; j < dv; ++j)
+                    S[c * dv + j] += b * kc * (load_elem(v, qkv_dtype, v_base + j) - r[j]);
+            }
+            /* 4. read the updated state with the query */
+            double* ot = o + (t * nh + hl) * dv;
+            for (int64_t j = 0; j < dv; ++j) ot[j] = 0.0;
+            for (int64_t c = 0; c < dk; ++c) {
+                const double qc = load_elem(q, qkv_dtype, qk_base + c);
+                for (int64_t j = 0; j < dv; ++j) ot[j] += qc * S[c * dv + j];
+            }
+            for (int64_t j = 0; j < dv; ++j) ot[j] *= scale;
+        }
+        if (s_final)
+            memcpy(s_final + (size_t)u * (size_t)dk * (size_t)dv, S,
+                   sizeof(double) * (size_t)dk * (size_t)dv);
+        free(S);
+        free(r);
+    }
+    return failed ? -2 : 0;
+}
