@@ -1,0 +1,140 @@
+/*
+ * kda.h -- C ABI of libkda.so, the MI355X (gfx950) implementation of the
+ * Kimi Delta Attention (KDA) token mixer.
+ *
+ * The operation.  Each (sequence, head) carries a fixed-size fp32 state S of
+ * dk rows (key channels) by dv columns (value channels).  For every token t:
+ *   S'  = diag(alpha_t) S            decay each key channel by its own gate
+ *   r   = S'^T k_t                   what the decayed state holds for k_t
+ *   S   = S' + beta_t k_t (v_t - r)^T   erase and write with the same beta
+ *   o_t = scale * S^T q_t            read the updated state with the query
+ * Sources: "Kimi K3 architecture: KDA, MLA and MoE", section "KDA is a
+ * writable state, not a smaller KV cache" (delta-rule correction, per-channel
+ * decay, queries read the current matrix); "Kimi K3 Architecture Teardown",
+ * section "Hybrid Attention for 1M Tokens" and Visual 5 (decay, erase, write;
+ * fixed-size state); "Kimi K3 Architecture: KDA, MoE, and Attention", section
+ * "Memory as a First-Class Problem: Kimi Delta Attention" (channel-wise
+ * alpha, one scalar beta for erase and write, output read from the updated
+ * state).  Prefix-cache resume (initial/final state) follows "Kimi K3
+ * architecture: KDA, MLA and MoE", section "Serving K3 means managing two
+ * cache lifecycles", and "Kimi K3 Architecture Teardown", section "Scale".
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor argument is a DEVICE pointer owned by the caller.  The
+ *    library allocates no device memory, keeps no pointer after returning and
+ *    takes scratch only through the caller's workspace.
+ *  - Tensors are dense, row-major, last index fastest, with the shapes given
+ *    below.  q, k, v, o, alpha and states must be 16-byte aligned; beta and
+ *    cu_seqlens 4-byte aligned; workspace 256-byte aligned.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream) and never synchronise the host.
+ *  - Arguments are validated before anything is launched: a call that
+ *    returns an error has touched no output.  KDA_ERR_HIP reports a launch
+ *    failure (the HIP error is consumed).  No C++ exception crosses the ABI.
+ *  - Inputs must be finite.  The library holds no mutable global state;
+ *    calls on different streams may run concurrently if their outputs and
+ *    workspaces do not overlap.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of q, k, v and o.  alpha, beta and the states are always fp32. */
+typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or shape    */
+    KDA_ERR_UNSUPPORTED = 2, /* head dim, chunk size or dtype not built       */
+    KDA_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned    */
+    KDA_ERR_HIP = 4          /* a HIP launch or runtime call failed           */
+} kda_status_t;
+
+/* Shape of one chunked-prefill call.  All fields are plain int32/int64/float
+ * so the struct layout is fixed: {int32 batch; [pad]; int64 seqlen; int32
+ * num_seqs, num_heads, head_dim_k, head_dim_v, chunk_size; float scale;
+ * int32 qkv_dtype, o_dtype}. */
+typedef struct {
+    int32_t batch;      /* B rows; must be 1 when cu_seqlens is given          */
+    int64_t seqlen;     /* T tokens per row, or total packed tokens (>= 0)      */
+    int32_t num_seqs;   /* N: == batch without cu_seqlens, else len(cu)-1 >= 1  */
+    int32_t num_heads;  /* H >= 1                                               */
+    int32_t head_dim_k; /* dk in {16, 32, 64, 128}                              */
+    int32_t head_dim_v; /* dv in {16, 32, 64, 128}                              */
+    int32_t chunk_size; /* C in {16, 32, 64}; the result does not depend on it  */
+                        /* beyond rounding.  fp32 inputs with dk = 128 run with */
+                        /* chunks of at most 32 (on-chip memory).               */
+    float scale;        /* query scale; 1.0 reproduces the pages' read          */
+    int32_t qkv_dtype;  /* kda_dtype_t of q, k, v                               */
+    int32_t o_dtype;    /* kda_dtype_t of o (fp32, or bf16 rounded to nearest   */
+                        /* even from the fp32 result)                           */
+} kda_chunk_params_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kda_status_string(kda_status_t status);
+
+/* Bytes of workspace kda_chunk_fwd needs for `params` (written to *bytes).
+ * The size depends only on the shape, not on the cu_seqlens values: it covers
+ * the worst case ceil(T / C) + N chunks per head for packed input.
+ * Errors: KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED as for kda_chunk_fwd. */
+kda_status_t kda_chunk_fwd_workspace_size(const kda_chunk_params_t* params, size_t* bytes);
+
+/* Chunked prefill: run the recurrence over every token of every sequence.
+ *
+ * Layout (D = params->qkv_dtype, B = batch, T = seqlen, H = num_heads):
+ *   q, k        [B, T, H, dk]  D
+ *   v           [B, T, H, dv]  D
+ *   alpha       [B, T, H, dk]  fp32, per-key-channel decay in [0, 1]
+ *   beta        [B, T, H]      fp32, one update strength per token and head
+ *   initial_state [N, H, dk, dv] fp32, or NULL for zeros
+ *   cu_seqlens  [N + 1] int32 on the device, or NULL.  NULL: each of the B rows
+ *               is one sequence (N == B).  Non-NULL: B == 1 and sequence n is
+ *               tokens [cu[n], cu[n+1]) of the row; requires cu[0] == 0,
+ *               non-decreasing, cu[N] == T.  It is not checked on the host (that
+ *               would need a device-to-host copy); violating it is undefined.
+ *               Empty sequences are allowed: their final state is the initial one.
+ *   o           [B, T, H, dv]  params->o_dtype (written for every token of every
+ *               sequence)
+ *   final_state [N, H, dk, dv] fp32, or NULL (not written).  May alias
+ *               initial_state exactly (in-place resume).
+ *   workspace   device scratch of at least kda_chunk_fwd_workspace_size bytes.
+ * The chunk form evaluates the same recurrence with intra-chunk products on
+ * the matrix cores; results agree with the token-by-token recurrence up to
+ * rounding.  fp32 inputs: fp32 arithmetic throughout.  bf16 inputs: matrix-
+ * core operands and chunk intermediates in fp16 (11-bit mantissa) with fp32
+ * accumulation and an fp32 state, so |v| and the state must stay well inside
+ * the fp16 range (below about 1e4 in magnitude). */
+kda_status_t kda_chunk_fwd(const kda_chunk_params_t* params,
+                           const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta,
+                           const float* initial_state, const int32_t* cu_seqlens,
+                           void* o, float* final_state,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* One decode step: every (sequence, head) consumes a single token and its
+ * state is updated in place.
+ *   q, k   [N, H, dk]  D        v  [N, H, dv]  D      o  [N, H, dv]  o_dtype
+ *   alpha  [N, H, dk]  fp32     beta  [N, H]      fp32
+ *   state  [N, H, dk, dv] fp32, read and overwritten in place.
+ * dk, dv in {16, 32, 64, 128}; num_seqs >= 1; num_heads >= 1.  The step is
+ * computed in fp32.  The state is streamed through the GPU once: each element
+ * is read once and written once. */
+kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads,
+                             int32_t head_dim_k, int32_t head_dim_v,
+                             float scale, int32_t qkv_dtype, int32_t o_dtype,
+                             const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta,
+                             float* state, void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,187 @@
+"""ctypes binding of libkda.so: argument marshalling only.
+
+Every step of the KDA path runs in the library's HIP kernels; this module
+checks tensor shapes, allocates outputs and the workspace through PyTorch
+(device memory and streams are all PyTorch is used for here) and forwards
+raw pointers to the C ABI declared in include/kda.h.  There is no fallback:
+if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+from . import build as _build
+
+KDA_DTYPE_F32 = 0
+KDA_DTYPE_BF16 = 1
+_STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
+           4: "KDA_ERR_HIP"}
+
+# Every symbol include/kda.h declares.
+EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg}")
+        self.status = status
+
+
+class ChunkParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int64), ("num_seqs", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32),
+                ("head_dim_v", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("qkv_dtype", ctypes.c_int32), ("o_dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def load() -> ctypes.CDLL:
+    """Load libkda.so (built in-tree); raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = _build.LIB
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
+                          "(python -m linear_attention_sequence_gated_amd.build)")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_int
+    lib.kda_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(ChunkParams), ctypes.POINTER(sz)]
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(ChunkParams), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  vp, sz, vp]
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().kda_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise KdaError(fn, status, status_string(status))
+
+
+def _code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    if dtype == torch.float32:
+        return KDA_DTYPE_F32
+    raise TypeError(f"q/k/v and o must be bfloat16 or float32, got {dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(cond: bool, what: str) -> None:
+    if not cond:
+        raise ValueError(what)
+
+
+def chunk_params(q: torch.Tensor, v: torch.Tensor, cu_seqlens: Optional[torch.Tensor],
+                 chunk_size: int, scale: float, o_dtype: Optional[torch.dtype] = None) -> ChunkParams:
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    n = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    return ChunkParams(B, T, n, H, dk, dv, chunk_size, scale, _code(q.dtype),
+                       _code(q.dtype if o_dtype is None else o_dtype))
+
+
+def workspace_size(q: torch.Tensor, v: torch.Tensor, cu_seqlens=None, chunk_size: int = 64,
+                   scale: float = 1.0) -> int:
+    p = chunk_params(q, v, cu_seqlens, chunk_size, scale)
+    out = ctypes.c_size_t(0)
+    _check("kda_chunk_fwd_workspace_size", load().kda_chunk_fwd_workspace_size(ctypes.byref(p),
+                                                                              ctypes.byref(out)))
+    return out.value
+
+
+def chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_size: int = 64,
+              scale: float = 1.0, output_final_state: bool = True, o=None, final_state=None,
+              workspace=None, stream=None, o_dtype: Optional[torch.dtype] = None):
+    """Chunked KDA prefill through kda_chunk_fwd.  Returns (o, final_state or None).
+
+    q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32, same dtype), alpha [B,T,H,dk] fp32,
+    beta [B,T,H] fp32, initial_state [N,H,dk,dv] fp32 or None, cu_seqlens int32 [N+1] or
+    None (device tensors).  ``final_state`` may be ``initial_state`` (in-place resume).
+    ``o_dtype`` (default: the dtype of q) is bf16 or fp32.
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(k.shape == q.shape and alpha.shape == q.shape, "q, k and alpha must share [B,T,H,dk]")
+    _need(v.shape == (B, T, H, dv) and beta.shape == (B, T, H), "v/beta shapes")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
+    _need(alpha.dtype == torch.float32 and beta.dtype == torch.float32, "alpha, beta must be fp32")
+    for t in (q, k, v, alpha, beta):
+        _need(t.is_cuda and t.is_contiguous(), "inputs must be contiguous device tensors")
+    n = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None:
+        _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda, "cu_seqlens: int32 device")
+    if initial_state is not None:
+        _need(initial_state.shape == (n, H, dk, dv) and initial_state.dtype == torch.float32
+              and initial_state.is_contiguous(), "initial_state must be fp32 [N,H,dk,dv]")
+    o_dtype = q.dtype if o_dtype is None else o_dtype
+    if o is None:
+        o = torch.empty(v.shape, dtype=o_dtype, device=v.device)
+    _need(o.shape == v.shape and o.dtype == o_dtype and o.is_contiguous(), "o shape/dtype")
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
+    p = chunk_params(q, v, cu_seqlens, chunk_size, scale, o_dtype)
+    need = workspace_size(q, v, cu_seqlens, chunk_size, scale)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = load().kda_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                              _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(final_state),
+                              _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
+    _check("kda_chunk_fwd", st)
+    return o, final_state
+
+
+def decode_step(q, k, v, alpha, beta, state, scale: float = 1.0, o=None, stream=None,
+                o_dtype: Optional[torch.dtype] = None):
+    """One decode step through kda_decode_step; ``state`` [N,H,dk,dv] is updated in place.
+
+    q, k, alpha [N,H,dk], v [N,H,dv], beta [N,H].  Returns o [N,H,dv] (``o_dtype``,
+    default the dtype of q).
+    """
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(k.shape == q.shape and alpha.shape == q.shape and v.shape == (N, H, dv)
+          and beta.shape == (N, H) and state.shape == (N, H, dk, dv), "decode shapes")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
+    _need(alpha.dtype == torch.float32 and beta.dtype == torch.float32
+          and state.dtype == torch.float32, "alpha, beta, state must be fp32")
+    for t in (q, k, v, alpha, beta, state):
+        _need(t.is_cuda and t.is_contiguous(), "inputs must be contiguous device tensors")
+    o_dtype = q.dtype if o_dtype is None else o_dtype
+    if o is None:
+        o = torch.empty(v.shape, dtype=o_dtype, device=v.device)
+    _need(o.shape == v.shape and o.dtype == o_dtype and o.is_contiguous(), "o shape/dtype")
+    st = load().kda_decode_step(N, H, dk, dv, float(scale), _code(q.dtype), _code(o_dtype),
+                                _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o), _stream(stream))
+    _check("kda_decode_step", st)
+    return o

@@ -1,0 +1,179 @@
+// kda_api.cpp -- the C ABI of libkda.so: argument validation, workspace
+// sizing and kernel launches.  Declarations and the contract of every entry
+// point are in include/kda.h.
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kda_kernels.h"
+
+namespace {
+
+constexpr size_t kWsAlign = 256;
+
+bool head_dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct PrefillPlan {
+    int64_t max_chunks;     // per head, worst case
+    int64_t block_bytes;    // per (chunk, head)
+    size_t off_bytes;       // chunk-offset table (packed input only)
+    size_t total;
+};
+
+bool dtype_ok(int32_t d) { return d == KDA_DTYPE_F32 || d == KDA_DTYPE_BF16; }
+
+kda_status_t check_params(const kda_chunk_params_t* p) {
+    if (!p) return KDA_ERR_INVALID_ARG;
+    if (p->batch < 1 || p->seqlen < 0 || p->num_seqs < 1 || p->num_heads < 1) return KDA_ERR_INVALID_ARG;
+    if (!dtype_ok(p->qkv_dtype) || !dtype_ok(p->o_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (!head_dim_ok(p->head_dim_k) || !head_dim_ok(p->head_dim_v)) return KDA_ERR_UNSUPPORTED;
+    if (p->chunk_size != 16 && p->chunk_size != 32 && p->chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+    if (!(p->scale == p->scale)) return KDA_ERR_INVALID_ARG;  // NaN
+    // every flattened index must fit comfortably in int64 and the chunk
+    // counts in int32
+    const int64_t tokens = (int64_t)p->batch * p->seqlen;
+    if (p->seqlen > 0 && tokens / p->seqlen != p->batch) return KDA_ERR_INVALID_ARG;
+    if (tokens > (int64_t)1 << 40) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)p->num_seqs * p->num_heads > ((int64_t)1 << 31) - 1) return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
+}
+
+int chunk_of(const kda_chunk_params_t* p) {
+    return kda::effective_chunk(p->head_dim_k, p->chunk_size, p->qkv_dtype == KDA_DTYPE_BF16);
+}
+
+PrefillPlan plan_prefill(const kda_chunk_params_t* p, bool packed) {
+    PrefillPlan pl{};
+    const int64_t C = chunk_of(p);
+    if (packed)
+        pl.max_chunks = p->seqlen / C + p->num_seqs + 1;
+    else
+        pl.max_chunks = (int64_t)p->batch * ((p->seqlen + C - 1) / C);
+    pl.block_bytes = kda::chunk_block_bytes(p->head_dim_k, (int)C, p->head_dim_v,
+                                            p->qkv_dtype == KDA_DTYPE_BF16);
+    pl.off_bytes = packed ? round_up(sizeof(int32_t) * ((size_t)p->num_seqs + 1), kWsAlign) : 0;
+    pl.total = pl.off_bytes + (size_t)pl.max_chunks * (size_t)p->num_heads * (size_t)pl.block_bytes;
+    return pl;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status_t s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument (pointer, size or shape)";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: head dim, chunk size or dtype not supported";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing, too small or misaligned";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch or runtime call failed";
+    }
+    return "KDA: unknown status";
+}
+
+kda_status_t kda_chunk_fwd_workspace_size(const kda_chunk_params_t* p, size_t* bytes) {
+    if (!bytes) return KDA_ERR_INVALID_ARG;
+    const kda_status_t st = check_params(p);
+    if (st != KDA_OK) return st;
+    // the size is quoted for the worst case of either layout so that one
+    // buffer serves packed and fixed-length calls of the same shape
+    const PrefillPlan a = plan_prefill(p, true), b = plan_prefill(p, false);
+    *bytes = a.total > b.total ? a.total : b.total;
+    return KDA_OK;
+}
+
+kda_status_t kda_chunk_fwd(const kda_chunk_params_t* p, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const float* initial_state,
+                           const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    kda_status_t st = check_params(p);
+    if (st != KDA_OK) return st;
+    const bool packed = cu_seqlens != nullptr;
+    if (packed && p->batch != 1) return KDA_ERR_INVALID_ARG;
+    if (!packed && p->num_seqs != p->batch) return KDA_ERR_INVALID_ARG;
+    const bool has_tokens = p->seqlen > 0;
+    if (has_tokens) {
+        if (!q || !k || !v || !alpha || !beta || !o) return KDA_ERR_INVALID_ARG;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(alpha, 16) ||
+            !aligned(beta, 4))
+            return KDA_ERR_INVALID_ARG;
+    }
+    if (initial_state && !aligned(initial_state, 16)) return KDA_ERR_INVALID_ARG;
+    if (final_state && !aligned(final_state, 16)) return KDA_ERR_INVALID_ARG;
+    if (packed && !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARG;
+    if (initial_state && final_state && initial_state != final_state) {
+        // partial overlap would race between slices; exact aliasing is fine
+        const size_t sb = (size_t)p->num_seqs * p->num_heads * p->head_dim_k * p->head_dim_v * sizeof(float);
+        const char* a0 = reinterpret_cast<const char*>(initial_state);
+        const char* b0 = reinterpret_cast<const char*>(final_state);
+        if (a0 < b0 + sb && b0 < a0 + sb) return KDA_ERR_INVALID_ARG;
+    }
+    const PrefillPlan pl = plan_prefill(p, packed);
+    if (pl.total > 0) {
+        if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_WORKSPACE;
+        if (workspace_bytes < pl.total) return KDA_ERR_WORKSPACE;
+    }
+    if (!final_state && !has_tokens) return KDA_OK;  // nothing to compute or write
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = reinterpret_cast<char*>(workspace);
+    kda::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.s0 = initial_state;
+    a.s_final = final_state;
+    a.cu_seqlens = cu_seqlens;
+    a.chunk_off = packed ? reinterpret_cast<const int32_t*>(ws) : nullptr;
+    a.o = o;
+    a.ws_chunks = ws + pl.off_bytes;
+    a.T = p->seqlen;
+    a.N = p->num_seqs;
+    a.H = p->num_heads;
+    a.DV = p->head_dim_v;
+    const int C = chunk_of(p);
+    a.chunks_per_seq = (int32_t)((p->seqlen + C - 1) / C);
+    a.scale = p->scale;
+    a.o_f32 = p->o_dtype == KDA_DTYPE_F32;
+
+    hipError_t e = hipSuccess;
+    if (packed) {
+        e = kda::launch_chunk_offsets(cu_seqlens, p->num_seqs, C, reinterpret_cast<int32_t*>(ws), s);
+        if (e != hipSuccess) return KDA_ERR_HIP;
+    }
+    e = kda::launch_prefill(a, p->head_dim_k, C, p->qkv_dtype == KDA_DTYPE_BF16, (int)pl.max_chunks, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t dk, int32_t dv, float scale,
+                             int32_t qkv_dtype, int32_t o_dtype, const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, float* state, void* o, void* stream) {
+    if (num_seqs < 1 || num_heads < 1) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)num_seqs * num_heads > ((int64_t)1 << 31) - 1) return KDA_ERR_INVALID_ARG;
+    if (!dtype_ok(qkv_dtype) || !dtype_ok(o_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return KDA_ERR_INVALID_ARG;
+    if (!q || !k || !v || !alpha || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(alpha, 16) ||
+        !aligned(state, 16) || !aligned(beta, 4))
+        return KDA_ERR_INVALID_ARG;
+    kda::DecodeArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.state = state;
+    a.o = o;
+    a.units = num_seqs * num_heads;
+    a.scale = scale;
+    a.o_f32 = o_dtype == KDA_DTYPE_F32;
+    const hipError_t e = kda::launch_decode(a, dk, dv, qkv_dtype == KDA_DTYPE_BF16, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

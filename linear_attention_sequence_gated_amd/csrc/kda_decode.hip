@@ -1,0 +1,148 @@
+// kda_decode.hip -- one KDA decode step on gfx950.
+//
+// Per (sequence, head), with the state S (dk x dv, fp32) updated in place:
+//   S' = diag(alpha) S ;  r = S'^T k ;  S = S' + beta k (v - r)^T ;  o = scale S^T q
+// ("Kimi K3 Architecture Teardown", Visual 5: decay, erase, write;
+// "Kimi K3 architecture: KDA, MLA and MoE", section "KDA is a writable state,
+// not a smaller KV cache": a query reads the current matrix instead of a
+// growing cache).  Since S^T q = S'^T q + beta (q.k) (v - r), the output
+// needs only the decayed state and two column reductions, so every state
+// element is read once and written once: the step is bound by HBM bandwidth.
+//
+// One workgroup per (sequence, head).  Thread (row group r0, column group cg)
+// owns float4 columns [4cg, 4cg+4) of rows r0, r0 + RPP, ... and keeps them in
+// registers between the reduction and the write-back.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_kernels.h"
+#include "kda_quads.h"
+
+namespace kda {
+
+template <int DK, int DV> struct DecodeShape {
+    static constexpr int CG = DV / 4;                                  // threads per state row
+    static constexpr int NT = (DK * DV / 4) < 256 ? (DK * DV / 4) : 256;  // threads
+    static constexpr int RPP = NT / CG;                                // rows per pass
+    static constexpr int PASSES = DK / RPP;
+    static constexpr int NW = NT / 64;
+    static_assert(NT % 64 == 0 && CG <= 32 && RPP * PASSES == DK, "decode thread mapping");
+};
+
+template <int DK, int DV, typename T>
+__global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void kda_decode_kernel(const DecodeArgs a) {
+    using D = DecodeShape<DK, DV>;
+    constexpr int CG = D::CG, RPP = D::RPP, PASSES = D::PASSES, NW = D::NW;
+    __shared__ float sq[DK], sk[DK], sa[DK], sv[DV];
+    __shared__ f32x4 red_r[NW][CG], red_y[NW][CG];
+    __shared__ float sqk;
+
+    const int unit = blockIdx.x;  // n * H + h
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cg = tid % CG, r0 = tid / CG;
+    float* __restrict__ S = a.state + (int64_t)unit * DK * DV;
+
+    // state rows of this thread: issue every load before anything else
+    f32x4 s[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+        s[p] = *reinterpret_cast<const f32x4*>(S + (r0 + p * RPP) * DV + 4 * cg);
+
+    const T* __restrict__ q = reinterpret_cast<const T*>(a.q) + (int64_t)unit * DK;
+    const T* __restrict__ k = reinterpret_cast<const T*>(a.k) + (int64_t)unit * DK;
+    const T* __restrict__ v = reinterpret_cast<const T*>(a.v) + (int64_t)unit * DV;
+    for (int i = tid; i < DK; i += D::NT) {
+        sq[i] = load_as_float(q, i);
+        sk[i] = load_as_float(k, i);
+        sa[i] = a.alpha[(int64_t)unit * DK + i];
+    }
+    for (int i = tid; i < DV; i += D::NT) sv[i] = load_as_float(v, i);
+    const float beta = a.beta[unit];
+    __syncthreads();
+    if (wave == 0) {
+        float t = 0.f;
+        for (int i = lane; i < DK; i += 64) t += sq[i] * sk[i];
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) t += __shfl_xor(t, m, 64);
+        if (lane == 0) sqk = t;
+    }
+
+    // decay, then the two column reductions r = S'^T k and y = S'^T q
+    f32x4 racc = zero4(), yacc = zero4();
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int c = r0 + p * RPP;
+        s[p] = s[p] * sa[c];
+        racc += sk[c] * s[p];
+        yacc += sq[c] * s[p];
+    }
+#pragma unroll
+    for (int m = CG; m < 64; m <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            racc[j] += __shfl_xor(racc[j], m, 64);
+            yacc[j] += __shfl_xor(yacc[j], m, 64);
+        }
+    }
+    if (lane < CG) {
+        red_r[wave][cg] = racc;
+        red_y[wave][cg] = yacc;
+    }
+    __syncthreads();
+    f32x4 r = zero4(), y = zero4();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        r += red_r[w][cg];
+        y += red_y[w][cg];
+    }
+    const f32x4 vv{sv[4 * cg], sv[4 * cg + 1], sv[4 * cg + 2], sv[4 * cg + 3]};
+    const f32x4 e = vv - r;  // correction towards the new value
+
+    // erase and write with the same beta, back to the same addresses
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int c = r0 + p * RPP;
+        const f32x4 ns = s[p] + (beta * sk[c]) * e;
+        *reinterpret_cast<f32x4*>(S + c * DV + 4 * cg) = ns;
+    }
+    if (r0 == 0) {
+        const f32x4 o4 = (y + (beta * sqk) * e) * a.scale;
+        const int64_t oi = (int64_t)unit * DV + 4 * cg;
+        if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + oi, o4);
+        else store4(reinterpret_cast<__bf16*>(a.o) + oi, o4);
+    }
+}
+
+template <int DK, int DV, typename T>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((kda_decode_kernel<DK, DV, T>), dim3(a.units), dim3(DecodeShape<DK, DV>::NT), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int DK, typename T>
+static hipError_t launch_decode_v(const DecodeArgs& a, int DV, hipStream_t s) {
+    switch (DV) {
+        case 16: return launch_decode_t<DK, 16, T>(a, s);
+        case 32: return launch_decode_t<DK, 32, T>(a, s);
+        case 64: return launch_decode_t<DK, 64, T>(a, s);
+        case 128: return launch_decode_t<DK, 128, T>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t launch_decode_k(const DecodeArgs& a, int DK, int DV, hipStream_t s) {
+    switch (DK) {
+        case 16: return launch_decode_v<16, T>(a, DV, s);
+        case 32: return launch_decode_v<32, T>(a, DV, s);
+        case 64: return launch_decode_v<64, T>(a, DV, s);
+        case 128: return launch_decode_v<128, T>(a, DV, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int DK, int DV, bool bf16, hipStream_t s) {
+    return bf16 ? launch_decode_k<__bf16>(a, DK, DV, s) : launch_decode_k<float>(a, DK, DV, s);
+}
+
+}  // namespace kda

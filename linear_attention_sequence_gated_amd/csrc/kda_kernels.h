@@ -1,0 +1,50 @@
+// kda_kernels.h -- launch interface between the C ABI (kda_api.cpp) and the
+// HIP kernels.  Internal to libkda.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    const float* s0;             // [N, H, dk, dv] or null
+    float* s_final;              // [N, H, dk, dv] or null
+    const int32_t* cu_seqlens;   // [N + 1] or null (fixed length rows)
+    const int32_t* chunk_off;    // [N + 1] chunk index of each sequence (packed input)
+    void* o;
+    char* ws_chunks;             // per-(chunk, head) blocks
+    int64_t T;                   // tokens per row, or total packed tokens
+    int32_t N, H, DV;
+    int32_t chunks_per_seq;      // fixed length: ceil(T / C)
+    float scale;
+    int32_t o_f32;               // 1: o is fp32, 0: o is bf16
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    float* state;
+    void* o;
+    int32_t units;               // N * H
+    float scale;
+    int32_t o_f32;               // 1: o is fp32, 0: o is bf16
+};
+
+hipError_t launch_chunk_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t* chunk_off, hipStream_t s);
+// C is the requested chunk size; the chunk the kernels use is
+// effective_chunk(DK, C, bf16) (fp32 operands with dk = 128 use at most 32).
+int effective_chunk(int DK, int C, bool bf16);
+hipError_t launch_prefill(const PrefillArgs& a, int DK, int C, bool bf16, int max_chunks, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int DK, int DV, bool bf16, hipStream_t s);
+int64_t chunk_block_bytes(int DK, int C, int DV, bool bf16);
+
+}  // namespace kda

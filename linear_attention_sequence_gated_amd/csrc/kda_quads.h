@@ -1,0 +1,152 @@
+// kda_quads.h -- matrix-core building blocks for the KDA kernels (gfx950).
+//
+// Every contraction in the chunked KDA form is expressed on 16x16 output
+// tiles with the CDNA4 MFMA instructions.  One lane of a wave64 holds, for
+// the row (A operand) or column (B operand) l % 16 of its tile, "quads": four
+// consecutive k-indices 16*u + 4*(l/16) + {0,1,2,3} of the u-th 16-wide slice
+// of the contraction axis.  This is exactly what the accumulator of a 16x16
+// MFMA tile holds per lane (rows 4*(l/16) + i of column l % 16), so a result
+// tile can feed the next contraction as a B operand (or as the A operand of
+// the transposed product) without moving data between lanes.
+//
+// Operand precision.  bf16 inputs are computed with fp16 operands: the
+// max-abs/RMS parity bound of 2e-2 leaves no room for the 8-bit bf16
+// mantissa in the intermediates (every bf16 rounding of an intermediate costs
+// about 1-3e-2 in that measure on its own), while fp16's 11 bits keep the
+// whole chain near 1e-2 and run at the same MFMA rate on gfx950.  fp32 inputs
+// are computed in fp32 throughout.
+//  * fp16 operands: two quads (u, u+1) form the 8 halves of one
+//    v_mfma_f32_16x16x32_f16 k-step; a trailing single quad uses
+//    v_mfma_f32_16x16x16_f16.
+//  * fp32 operands: one quad is four v_mfma_f32_16x16x4_f32 k-steps.
+// Accumulation is fp32 in both cases.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef _Float16 f16x4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+
+template <typename T> struct QuadOf;
+template <> struct QuadOf<float> { using type = f32x4; static constexpr int kPerStep = 1; };
+template <> struct QuadOf<_Float16> { using type = f16x4; static constexpr int kPerStep = 2; };
+template <typename T> using quad_t = typename QuadOf<T>::type;
+
+// Storage type of the inputs q, k, v and the operand type they are computed in.
+template <typename In> struct OperandOf;
+template <> struct OperandOf<float> { using type = float; };
+template <> struct OperandOf<__bf16> { using type = _Float16; };
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// fp32 -> quad (round to nearest even).
+__device__ __forceinline__ void to_quad(const f32x4& x, f32x4& q) { q = x; }
+__device__ __forceinline__ void to_quad(const f32x4& x, f16x4& q) {
+    q = f16x4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+}
+__device__ __forceinline__ void to_quad(const f32x4& x, bf16x4& q) {
+    q = bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+}
+template <typename T> __device__ __forceinline__ quad_t<T> make_quad(const f32x4& x) {
+    quad_t<T> q;
+    to_quad(x, q);
+    return q;
+}
+__device__ __forceinline__ f32x4 from_quad(const f32x4& q) { return q; }
+__device__ __forceinline__ f32x4 from_quad(const f16x4& q) {
+    return f32x4{(float)q[0], (float)q[1], (float)q[2], (float)q[3]};
+}
+
+// c += A(quads a[0..n)) * B(quads b[0..n)) over one 16x16 tile.
+__device__ __forceinline__ f32x4 mma_step(const f32x4& a, const f32x4& b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    return c;
+}
+__device__ __forceinline__ f32x4 mma_step(const f16x4& a, const f16x4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_step2(const f16x4& a0, const f16x4& a1, const f16x4& b0,
+                                           const f16x4& b1, f32x4 c) {
+    const f16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+    const f16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_step2(const f32x4& a0, const f32x4& a1, const f32x4& b0,
+                                           const f32x4& b1, f32x4 c) {
+    return mma_step(a1, b1, mma_step(a0, b0, c));
+}
+
+// c += sum over quads u in [0, N) of A_u * B_u, with N a compile-time count.
+template <int N, typename Q>
+__device__ __forceinline__ f32x4 mma_quads(const Q (&a)[N], const Q (&b)[N], f32x4 c) {
+#pragma unroll
+    for (int u = 0; u + 1 < N; u += 2) c = mma_step2(a[u], a[u + 1], b[u], b[u + 1], c);
+    if constexpr (N % 2 == 1) c = mma_step(a[N - 1], b[N - 1], c);
+    return c;
+}
+
+// Same, but only quads u <= last contribute (lower-triangular operands whose
+// quads above `last` are zero in memory; pairs are kept whole).
+template <int N, typename Q>
+__device__ __forceinline__ f32x4 mma_quads_upto(const Q (&a)[N], const Q (&b)[N], int last, f32x4 c) {
+#pragma unroll
+    for (int u = 0; u + 1 < N; u += 2)
+        if (u <= last) c = mma_step2(a[u], a[u + 1], b[u], b[u + 1], c);
+    if constexpr (N % 2 == 1) {
+        if (N - 1 <= last) c = mma_step(a[N - 1], b[N - 1], c);
+    }
+    return c;
+}
+
+// Fragment storage in global memory: a matrix of `rows` (multiple of 16) by
+// K (multiple of 16) stored so that lane l of the wave that consumes row tile
+// rt reads its quads of k-slices [kPerStep*gq, kPerStep*gq + kPerStep) as one
+// contiguous 8- or 16-byte vector.  Offsets are in elements of T.
+template <typename T> struct Frag {
+    static constexpr int kPerStep = QuadOf<T>::kPerStep;
+    __host__ __device__ static constexpr int groups(int K) { return (K / 16 + kPerStep - 1) / kPerStep; }
+    __host__ __device__ static constexpr int64_t elems(int rows, int K) {
+        return (int64_t)(rows / 16) * groups(K) * 64 * 4 * kPerStep;
+    }
+    __host__ __device__ static constexpr int64_t off(int rt, int u, int lane, int K) {
+        return (((int64_t)rt * groups(K) + u / kPerStep) * 64 + lane) * (4 * kPerStep) + (u % kPerStep) * 4;
+    }
+};
+
+// Per-(chunk, head) block that the intra-chunk kernel writes and the
+// inter-chunk kernel reads.  All offsets in bytes, all multiples of 16.
+template <typename T> struct ChunkBlock {
+    int64_t w, q, kb, p, u, gam, bytes;
+    __host__ __device__ ChunkBlock(int DK, int C, int DV) {
+        const int64_t s = sizeof(T);
+        w = 0;                                   // W = T Ktilde      : C x DK frag
+        q = w + Frag<T>::elems(C, DK) * s;       // Qtilde            : C x DK frag
+        kb = q + Frag<T>::elems(C, DK) * s;      // Kbar^T            : DK x C frag
+        p = kb + Frag<T>::elems(DK, C) * s;      // P (as P^T B-frag) : C x C frag
+        u = p + Frag<T>::elems(C, C) * s;        // Utilde = T V      : [DV/16][64][C/16][4]
+        gam = u + (int64_t)DV * C * s;           // gamma_C           : DK fp32
+        bytes = gam + (int64_t)DK * 4;
+        bytes = (bytes + 255) / 256 * 256;
+    }
+};
+
+__device__ __forceinline__ float load_as_float(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_as_float(const __bf16* p, int64_t i) { return (float)p[i]; }
+
+// Store four fp32 values as fp32 (16 bytes) or bf16 (8 bytes, round to nearest even).
+__device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void store4(__bf16* p, const f32x4& v) {
+    bf16x4 q;
+    to_quad(v, q);
+    *reinterpret_cast<bf16x4*>(p) = q;
+}
+
+}  // namespace kda

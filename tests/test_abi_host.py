@@ -1,0 +1,122 @@
+"""Host-side checks of libkda.so that need no GPU.
+
+The library must load, export every function include/kda.h declares, and
+reject invalid arguments with the documented status before anything is
+launched (every call here is invalid, so none reaches a kernel).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_sequence_gated_amd as kda
+from linear_attention_sequence_gated_amd._lib import ChunkParams
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)      # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from linear_attention_sequence_gated_amd import build
+    if build.is_stale():
+        build.build()
+    return kda.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert declared == sorted(kda.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        s = kda.status_string(code)
+        assert s.startswith("KDA_")
+    assert "unknown" in kda.status_string(99)
+
+
+def _params(**kw):
+    p = dict(batch=1, seqlen=128, num_seqs=1, num_heads=2, head_dim_k=128, head_dim_v=128,
+             chunk_size=64, scale=1.0, qkv_dtype=1, o_dtype=1)
+    p.update(kw)
+    return ChunkParams(**p)
+
+
+def _ws(lib, p):
+    out = ctypes.c_size_t(0)
+    st = lib.kda_chunk_fwd_workspace_size(ctypes.byref(p), ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size(lib):
+    st, n1 = _ws(lib, _params())
+    assert st == OK and n1 > 0
+    st, n2 = _ws(lib, _params(seqlen=256))
+    assert st == OK and n2 > n1                      # grows with T
+    st, n3 = _ws(lib, _params(num_heads=4))
+    assert st == OK and n3 > n2 - 1                  # grows with H
+    st, n4 = _ws(lib, _params(batch=1, num_seqs=40, seqlen=128))
+    assert st == OK and n4 > n1                      # packed worst case: one partial chunk per sequence
+    assert _ws(lib, _params(head_dim_k=96))[0] == UNSUPPORTED
+    assert _ws(lib, _params(chunk_size=128))[0] == UNSUPPORTED
+    assert _ws(lib, _params(qkv_dtype=7))[0] == UNSUPPORTED
+    assert _ws(lib, _params(o_dtype=3))[0] == UNSUPPORTED
+    # fp32 operands with dk = 128 run 32-token chunks: the quote does not depend
+    # on a requested 64
+    assert _ws(lib, _params(qkv_dtype=0, chunk_size=64)) == _ws(lib, _params(qkv_dtype=0, chunk_size=32))
+    assert _ws(lib, _params(num_heads=0))[0] == INVALID
+    assert lib.kda_chunk_fwd_workspace_size(None, None) == INVALID
+
+
+def _fwd(lib, p, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s0=None, cu=None, o=FAKE, sf=None,
+         ws=None, wsb=0):
+    return lib.kda_chunk_fwd(ctypes.byref(p) if p is not None else None, q, k, v, a, b, s0, cu, o,
+                             sf, ws, ctypes.c_size_t(wsb), None)
+
+
+def test_chunk_fwd_rejects_before_launch(lib):
+    p = _params()
+    _, need = _ws(lib, p)
+    assert _fwd(lib, None) == INVALID
+    assert _fwd(lib, p, q=None, ws=FAKE, wsb=need) == INVALID
+    assert _fwd(lib, p, o=None, ws=FAKE, wsb=need) == INVALID
+    assert _fwd(lib, p, q=MISALIGNED, ws=FAKE, wsb=need) == INVALID
+    assert _fwd(lib, p, b=ctypes.c_void_p(0x10002), ws=FAKE, wsb=need) == INVALID
+    assert _fwd(lib, p, ws=None, wsb=0) == WORKSPACE
+    assert _fwd(lib, p, ws=FAKE, wsb=1) == WORKSPACE
+    assert _fwd(lib, p, ws=ctypes.c_void_p(0x10010), wsb=need) == WORKSPACE   # not 256-aligned
+    assert _fwd(lib, _params(head_dim_v=48), ws=FAKE, wsb=need) == UNSUPPORTED
+    assert _fwd(lib, _params(num_seqs=2), ws=FAKE, wsb=need) == INVALID      # N != B without cu
+    assert _fwd(lib, _params(batch=2, num_seqs=2), cu=FAKE, ws=FAKE, wsb=10 * need) == INVALID
+    assert _fwd(lib, _params(scale=float("nan")), ws=FAKE, wsb=need) == INVALID
+    # states that overlap without being the same buffer
+    assert _fwd(lib, p, s0=ctypes.c_void_p(0x100000), sf=ctypes.c_void_p(0x100010), ws=FAKE,
+                wsb=need) == INVALID
+
+
+def test_decode_step_rejects_before_launch(lib):
+    def call(n=4, h=2, dk=128, dv=128, scale=1.0, dt=1, odt=1, ptrs=None):
+        ptrs = ptrs or [FAKE] * 8
+        return lib.kda_decode_step(n, h, dk, dv, scale, dt, odt, *ptrs, None)
+    assert call(n=0) == INVALID
+    assert call(h=0) == INVALID
+    assert call(dk=256) == UNSUPPORTED
+    assert call(dv=24) == UNSUPPORTED
+    assert call(dt=5) == UNSUPPORTED
+    assert call(odt=-1) == UNSUPPORTED
+    assert call(scale=float("nan")) == INVALID
+    assert call(ptrs=[FAKE] * 5 + [None] + [FAKE] * 2) == INVALID       # state
+    assert call(ptrs=[FAKE] * 5 + [MISALIGNED] + [FAKE] * 2) == INVALID  # state alignment

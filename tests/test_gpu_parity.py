@@ -1,0 +1,315 @@
+"""Parity of the HIP path (through the C ABI of libkda.so) against the fp64 oracle.
+
+Error measure: max |gpu - oracle| / rms(oracle) over a whole tensor, for the
+outputs o and the final states separately.  Bounds: 1e-4 for fp32 inputs and
+2e-2 for bf16 inputs.  The bound is taken on o emitted in fp32: rounding a
+perfectly computed o to bf16 alone already costs about 2.5e-2 in this
+measure (tests/test_output_rounding.py), so the bf16 output is checked
+separately: it must equal the fp32 output of the same launch configuration
+rounded to nearest even, bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_sequence_gated_amd as kda
+import workloads
+from oracle import kda_oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def rel_err(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), "non-finite GPU output"
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    diff = float(np.max(np.abs(gpu - ref))) if gpu.size else 0.0
+    return diff / rms if rms > 0 else diff
+
+
+def to_dev(inp):
+    return {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def gpu_prefill(inp, chunk, scale=1.0, o_dtype=torch.float32, raw=False, **kw):
+    d = to_dev(inp)
+    o, S = kda.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"],
+                         chunk_size=chunk, scale=scale, o_dtype=o_dtype, **kw)
+    torch.cuda.synchronize()
+    if raw:
+        return o.cpu(), S.cpu()
+    return o.float().cpu().numpy(), S.cpu().numpy()
+
+
+def check_bf16_output(inp, chunk, scale=1.0):
+    """bf16 o == RNE(fp32 o) of the same computation, bit for bit."""
+    o32, _ = gpu_prefill(inp, chunk, scale, o_dtype=torch.float32, raw=True)
+    o16, _ = gpu_prefill(inp, chunk, scale, o_dtype=torch.bfloat16, raw=True)
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o16.view(torch.int16), o32.to(torch.bfloat16).view(torch.int16))
+
+
+def oracle_prefill(inp, scale=1.0, heads=None):
+    cu = inp["cu_seqlens"]
+    return kda_oracle.forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0=inp["S0"],
+                              cu_seqlens=None if cu is None else cu.to(torch.int64), scale=scale,
+                              heads=heads)
+
+
+def check(inp, chunk, tol, scale=1.0, label=""):
+    say(f"[case] {label} chunk={chunk} q={tuple(inp['q'].shape)} {inp['q'].dtype}")
+    og, Sg = gpu_prefill(inp, chunk, scale)
+    oo, So = oracle_prefill(inp, scale)
+    eo, es = rel_err(og, oo), rel_err(Sg, So)
+    say(f"    err o={eo:.3e} S={es:.3e} (tol {tol})")
+    assert eo < tol and es < tol, (eo, es)
+    return eo, es
+
+
+# --- the five workloads ------------------------------------------------------
+
+def test_config0_tiny_fp32():
+    w = workloads.CONFIGS[0]
+    check(workloads.config_inputs(0), w.chunk, TOL[w.dtype], label="config0")
+
+
+def test_config1_batched_bf16():
+    w = workloads.CONFIGS[1]
+    inp = workloads.config_inputs(1)
+    check(inp, w.chunk, TOL[w.dtype], label="config1")
+    check_bf16_output(inp, w.chunk)
+
+
+@pytest.mark.timeout(900)
+def test_config2_long_context_sampled_heads():
+    """Full-size launch (B1 H32 T65536); the oracle recomputes heads 0, 17 and 31."""
+    w = workloads.CONFIGS[2]
+    say("[case] config2 generating inputs")
+    inp = workloads.config_inputs(2)
+    say("[case] config2 GPU prefill")
+    og, Sg = gpu_prefill(inp, w.chunk)
+    for h in (0, 17, 31):
+        say(f"[case] config2 oracle head {h}")
+        oo, So = oracle_prefill(inp, heads=(h, h + 1))
+        eo, es = rel_err(og[:, :, h:h + 1], oo), rel_err(Sg[:, h:h + 1], So)
+        say(f"    head {h}: err o={eo:.3e} S={es:.3e}")
+        assert eo < TOL[w.dtype] and es < TOL[w.dtype], (h, eo, es)
+
+
+@pytest.mark.timeout(1200)
+def test_config4_packed_varlen_resume_sampled_heads():
+    """64 packed sequences (lengths U[1, 32768]), S0 != 0; the oracle recomputes heads 3 and 12."""
+    w = workloads.CONFIGS[4]
+    say("[case] config4 generating inputs")
+    inp = workloads.config_inputs(4)
+    say(f"[case] config4 GPU prefill, T={inp['q'].shape[1]}")
+    og, Sg = gpu_prefill(inp, w.chunk)
+    for h in (3, 12):
+        say(f"[case] config4 oracle head {h}")
+        oo, So = oracle_prefill(inp, heads=(h, h + 1))
+        eo, es = rel_err(og[:, :, h:h + 1], oo), rel_err(Sg[:, h:h + 1], So)
+        say(f"    head {h}: err o={eo:.3e} S={es:.3e}")
+        assert eo < TOL[w.dtype] and es < TOL[w.dtype], (h, eo, es)
+
+
+def _decode_run(inp, steps, scale=1.0, o_dtype=torch.float32):
+    d = to_dev(inp)
+    state = d["S0"].clone()
+    outs = []
+    for t in range(steps):
+        outs.append(kda.decode_step(d["q"][t], d["k"][t], d["v"][t], d["alpha"][t], d["beta"][t], state,
+                                    scale=scale, o_dtype=o_dtype))
+    torch.cuda.synchronize()
+    return torch.stack(outs).float().cpu().numpy(), state.cpu().numpy()
+
+
+@pytest.mark.timeout(600)
+def test_config3_decode_128_steps_sampled_sequences():
+    """256 sequences x H32, 128 in-place steps; the oracle recomputes sequences 0, 101 and 255."""
+    w = workloads.CONFIGS[3]
+    say("[case] config3 generating inputs")
+    inp = workloads.decode_inputs(3)
+    say("[case] config3 GPU decode x128")
+    og, Sg = _decode_run(inp, w.decode_steps)
+    for n in (0, 101, 255):
+        sub = {k: (v[:, n:n + 1] if k != "S0" else v[n:n + 1]) for k, v in inp.items()}
+        oo, So = kda_oracle.decode(sub["S0"], sub["q"], sub["k"], sub["v"], sub["alpha"], sub["beta"])
+        eo, es = rel_err(og[:, n:n + 1], oo), rel_err(Sg[n:n + 1], So)
+        say(f"    seq {n}: err o={eo:.3e} S={es:.3e}")
+        assert eo < TOL[w.dtype] and es < TOL[w.dtype], (n, eo, es)
+
+
+# --- shapes, ragged tails, packing --------------------------------------------
+
+SHAPES = [
+    # B, T, H, dk, dv, C, dtype, S0
+    (2, 100, 3, 64, 32, 32, torch.bfloat16, True),
+    (1, 77, 2, 128, 128, 64, torch.float32, True),
+    (3, 33, 1, 16, 128, 16, torch.bfloat16, False),
+    (1, 200, 2, 32, 64, 64, torch.float32, False),
+    (1, 1, 1, 128, 16, 64, torch.bfloat16, True),
+    (2, 130, 2, 128, 64, 16, torch.float32, True),
+    (1, 257, 2, 128, 128, 32, torch.bfloat16, True),
+]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,C,dtype,s0", SHAPES)
+def test_shapes(B, T, H, dk, dv, C, dtype, s0):
+    inp = workloads.make_inputs(B, T, H, dk, dv, dtype, alpha_mu=3.0, s0_std=0.02 if s0 else 0.0,
+                                seed=1000 + T + dk)
+    check(inp, C, TOL[dtype], scale=0.75, label=f"shape B{B} T{T} H{H} dk{dk} dv{dv}")
+    check_bf16_output(inp, C, scale=0.75)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_packed_ragged_with_empty_sequences(dtype):
+    lens = [0, 1, 63, 64, 65, 200, 0, 129, 7]
+    inp = workloads.make_inputs(1, 0, 2, 128, 128, dtype, s0_std=0.02, seed=77, lengths=lens)
+    check(inp, 64, TOL[dtype], label=f"packed {lens}")
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+def test_chunk_size_invariance(C):
+    inp = workloads.make_inputs(2, 190, 2, 128, 128, torch.bfloat16, s0_std=0.02, seed=5)
+    check(inp, C, TOL[torch.bfloat16], label="chunk invariance")
+
+
+# --- degenerate gates ---------------------------------------------------------
+
+def _gated(dtype, alpha_fn, beta_fn, T=150, seed=9):
+    inp = workloads.make_inputs(1, T, 2, 128, 64, dtype, s0_std=0.02, seed=seed)
+    inp["alpha"] = alpha_fn(inp["alpha"]).float().contiguous()
+    inp["beta"] = beta_fn(inp["beta"]).float().contiguous()
+    return inp
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_zero_decay_forgets_everything(dtype):
+    inp = _gated(dtype, torch.zeros_like, lambda b: b)   # every chunk takes the exact pairwise path
+    check(inp, 64, TOL[dtype], label="alpha=0")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_fast_decay_exact_path(dtype):
+    g = torch.Generator().manual_seed(3)
+    inp = _gated(dtype, lambda a: torch.rand(a.shape, generator=g) * 0.2 + 0.05, lambda b: b)
+    check(inp, 64, TOL[dtype], label="alpha in [0.05, 0.25]")
+
+
+def test_mixed_zero_and_tiny_decay():
+    g = torch.Generator().manual_seed(4)
+
+    def alpha_fn(a):
+        a = a.clone()
+        m = torch.rand(a.shape, generator=g)
+        a[m < 0.01] = 0.0
+        a[(m >= 0.01) & (m < 0.02)] = 1e-30
+        return a
+    check(_gated(torch.float32, alpha_fn, lambda b: b), 64, TOL[torch.float32], label="sparse zeros")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_zero_beta_is_pure_decay(dtype):
+    check(_gated(dtype, lambda a: a, torch.zeros_like), 64, TOL[dtype], label="beta=0")
+
+
+def test_identity_gate_keeps_state():
+    inp = _gated(torch.float32, torch.ones_like, torch.zeros_like)
+    og, Sg = gpu_prefill(inp, 64)
+    np.testing.assert_allclose(Sg, inp["S0"].numpy(), rtol=0, atol=1e-6)
+    ref = np.einsum("bthc,bhcj->bthj", inp["q"].double().numpy(), inp["S0"].double().numpy())
+    assert rel_err(og, ref) < 1e-4
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_exact_recall_standard_basis_keys(dtype):
+    """q = k = e_{i_t}, beta = 1: o_t = v_t for any decay (exact in bf16 storage)."""
+    T, H, d = 160, 2, 128
+    g = torch.Generator().manual_seed(11)
+    idx = torch.randint(0, d, (1, T, H), generator=g)
+    k = torch.nn.functional.one_hot(idx, d).to(dtype)
+    inp = workloads.make_inputs(1, T, H, d, d, dtype, s0_std=0.02, seed=12)
+    inp.update(q=k.clone(), k=k, beta=torch.ones(1, T, H))
+    og, _ = gpu_prefill(inp, 64)
+    err = rel_err(og, inp["v"].double().numpy())
+    say(f"    recall err {err:.3e}")
+    assert err < TOL[dtype]
+
+
+# --- state plumbing -------------------------------------------------------------
+
+def test_resume_from_final_state_equals_one_pass():
+    inp = workloads.make_inputs(1, 300, 2, 128, 128, torch.bfloat16, s0_std=0.02, seed=21)
+    o_full, S_full = gpu_prefill(inp, 64)
+    cut = 131  # mid-chunk
+    first = {k: (v[:, :cut].contiguous() if k in ("q", "k", "v", "alpha", "beta") else v)
+             for k, v in inp.items()}
+    o1, S1 = gpu_prefill(first, 64)
+    second = {k: (v[:, cut:].contiguous() if k in ("q", "k", "v", "alpha", "beta") else v)
+              for k, v in inp.items()}
+    second["S0"] = torch.from_numpy(S1)
+    o2, S2 = gpu_prefill(second, 64)
+    assert rel_err(np.concatenate([o1, o2], axis=1), o_full) < 2e-2
+    assert rel_err(S2, S_full) < 2e-2
+
+
+def test_in_place_state_alias():
+    inp = workloads.make_inputs(1, 129, 2, 64, 64, torch.float32, s0_std=0.02, seed=22)
+    d = to_dev(inp)
+    state = d["S0"].clone()
+    o, S = kda.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], state, None, chunk_size=32,
+                         final_state=state)
+    torch.cuda.synchronize()
+    assert S.data_ptr() == state.data_ptr()
+    oo, So = oracle_prefill(inp)
+    assert rel_err(state.cpu().numpy(), So) < 1e-4
+    assert rel_err(o.cpu().numpy(), oo) < 1e-4
+
+
+def test_empty_sequence_axis_copies_state():
+    inp = workloads.make_inputs(2, 0, 2, 32, 32, torch.float32, s0_std=0.02, seed=23)
+    og, Sg = gpu_prefill(inp, 32)
+    np.testing.assert_array_equal(Sg, inp["S0"].numpy())
+    assert og.size == 0
+
+
+# --- decode --------------------------------------------------------------------
+
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, torch.bfloat16), (64, 32, torch.float32),
+                                         (16, 128, torch.float32), (128, 16, torch.bfloat16)])
+def test_decode_small(dk, dv, dtype):
+    steps, N, H = 9, 3, 2
+    inp = workloads.make_inputs(steps, N, H, dk, dv, dtype, seed=31 + dk)
+    g = torch.Generator().manual_seed(32)
+    inp["S0"] = torch.randn(N, H, dk, dv, generator=g) * 0.02
+    say(f"[case] decode dk{dk} dv{dv} {dtype}")
+    og, Sg = _decode_run(inp, steps, scale=1.3)
+    oo, So = kda_oracle.decode(inp["S0"], inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                               scale=1.3)
+    eo, es = rel_err(og, oo), rel_err(Sg, So)
+    say(f"    err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL[dtype] and es < TOL[dtype]
+    ob, _ = _decode_run(inp, steps, scale=1.3, o_dtype=torch.bfloat16)
+    assert np.array_equal(ob, torch.from_numpy(og).to(torch.bfloat16).float().numpy())
+
+
+def test_decode_steps_equal_prefill():
+    """T decode steps and one prefill over the same T tokens agree (GPU against GPU)."""
+    steps, N, H, d = 70, 2, 2, 128
+    inp = workloads.make_inputs(steps, N, H, d, d, torch.float32, seed=41)
+    g = torch.Generator().manual_seed(42)
+    inp["S0"] = torch.randn(N, H, d, d, generator=g) * 0.02
+    od, Sd = _decode_run(inp, steps)
+    pre = {k: (v.transpose(0, 1).contiguous() if k in ("q", "k", "v", "alpha", "beta") else v)
+           for k, v in inp.items()}
+    op, Sp = gpu_prefill(pre, 64)
+    assert rel_err(od, op.transpose(1, 0, 2, 3)) < 1e-4
+    assert rel_err(Sd, Sp) < 1e-4

@@ -15,8 +15,10 @@ KDA inset of Visual 1 on the "Kimi K3 Architecture Teardown" page):
   (sequence, head) where a prefix-cache resume is modelled.
 
 Every draw is made in fp32 on a CPU ``torch.Generator`` seeded with
-``20261200 + config index``; the draw order is lengths (packed workload only),
-q, k, v, alpha, beta, S0.  q, k and v are cast once to their storage dtype
+``20261200 + config index``, in the order q, k, v, alpha, beta, S0.  The packed
+workload first draws its lengths from that seed and its tensors from the seed
+plus 1000; the decode workload draws its initial states from the seed plus
+500.  q, k and v are cast once to their storage dtype
 (round to nearest even); alpha, beta and S0 stay fp32.  Large tensors are drawn
 in fixed blocks of tokens so that host memory stays bounded; the result is a
 deterministic function of the seed and the shape.
@@ -69,10 +71,14 @@ CONFIGS = {
 }
 
 
+def _rows_view(x: torch.Tensor, rows: int) -> torch.Tensor:
+    return x.view(rows, x.numel() // rows if rows else 0)
+
+
 def _randn(gen: torch.Generator, shape, rows: int) -> torch.Tensor:
     """N(0,1) fp32 of ``shape`` whose first axis has ``rows`` entries, drawn block by block."""
     out = torch.empty(shape, dtype=torch.float32)
-    flat = out.view(rows, -1)
+    flat = _rows_view(out, rows)
     for r0 in range(0, rows, _BLOCK_TOKENS):
         r1 = min(rows, r0 + _BLOCK_TOKENS)
         flat[r0:r1] = torch.randn((r1 - r0, flat.shape[1]), generator=gen, dtype=torch.float32)
@@ -80,6 +86,8 @@ def _randn(gen: torch.Generator, shape, rows: int) -> torch.Tensor:
 
 
 def _l2norm_(x: torch.Tensor, rows: int) -> None:
+    if rows == 0:
+        return
     flat = x.view(rows, -1, x.shape[-1])
     for r0 in range(0, rows, _BLOCK_TOKENS):
         blk = flat[r0:r0 + _BLOCK_TOKENS]
@@ -90,7 +98,7 @@ def _cast(x: torch.Tensor, dtype: torch.dtype, rows: int) -> torch.Tensor:
     if dtype == torch.float32:
         return x
     out = torch.empty(x.shape, dtype=dtype)
-    fo, fx = out.view(rows, -1), x.view(rows, -1)
+    fo, fx = _rows_view(out, rows), _rows_view(x, rows)
     for r0 in range(0, rows, _BLOCK_TOKENS):
         fo[r0:r0 + _BLOCK_TOKENS] = fx[r0:r0 + _BLOCK_TOKENS].to(dtype)
     return out
@@ -133,12 +141,12 @@ def make_inputs(batch: int, seqlen: int, heads: int, dk: int, dv: int, dtype: to
     _l2norm_(k, rows)
     k = _cast(k, dtype, rows)
     v = _randn(gen, (batch, seqlen, heads, dv), rows)
-    fv = v.view(rows, -1)
+    fv = _rows_view(v, rows)
     for r0 in range(0, rows, _BLOCK_TOKENS):
         fv[r0:r0 + _BLOCK_TOKENS] = torch.nn.functional.silu(fv[r0:r0 + _BLOCK_TOKENS])
     v = _cast(v, dtype, rows)
     alpha = _randn(gen, (batch, seqlen, heads, dk), rows)
-    fa = alpha.view(rows, -1)
+    fa = _rows_view(alpha, rows)
     for r0 in range(0, rows, _BLOCK_TOKENS):
         fa[r0:r0 + _BLOCK_TOKENS] = torch.sigmoid(fa[r0:r0 + _BLOCK_TOKENS] + alpha_mu)
     beta = torch.sigmoid(_randn(gen, (batch, seqlen, heads), rows))
