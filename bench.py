@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step is one kda_chunk_fwd over the long-context prefill workload
+(B1 H32 T65536, dk = dv = 128, chunk 64, bf16 q/k/v, fp32 alpha/beta/state,
+o in bf16): its two halves are launched as kda_chunk_fwd_intra and
+kda_chunk_fwd_inter so that HIP events on the launch stream time each kernel.
+`value` is prefill tokens/s.  The decode workload (256 sequences x H32, 128
+in-place steps) is measured in the same run and reported under "decode" as
+state GB/s.  Inputs are seeded synthetic data already resident in HBM when a
+timed region starts.
+
+The line also carries the roofline of the dominant kernel (algorithmic bytes
+or flops per launch / measured average launch time, against MI355X peaks),
+the same for every kernel, and the fp64 CPU oracle timed on a bounded sample
+of the workload on this host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s + decode state GB/s (dk=dv=128), % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
+PREFILL_CFG = 2
+DECODE_CFG = 3
+
+
+def algorithmic(dk, dv, chunk, qkv_bytes=2, o_bytes=2):
+    """Per-unit algorithmic costs of the path (what the method itself must move or compute)."""
+    in_bytes = 2 * dk * qkv_bytes + dv * qkv_bytes + dk * 4 + 4   # q, k, v, alpha, beta
+    return {
+        # intra-chunk kernel: reads every input once
+        "intra_bytes_per_token_head": in_bytes,
+        # inter-chunk kernel: W S, Qtilde S, Kbar^T U (2 dk dv flops each) and the causal P U
+        "inter_flops_per_token_head": 6 * dk * dv + dv * (chunk + 1),
+        "prefill_bytes_per_token_head": in_bytes + dv * o_bytes,
+        "state_bytes_per_seq_head": dk * dv * 4,
+        # decode: state read + written once, plus the token's q, k, v, alpha, beta and o
+        "decode_bytes_per_head_step": 2 * dk * dv * 4 + in_bytes + dv * o_bytes,
+    }
+
+
+def roof(bound, amount, seconds, unit, kernel, traffic=None):
+    peak = HBM_PEAK_GBS if unit == "GB/s" else MFMA_F16_PEAK_TFLOPS
+    scale = 1e9 if unit == "GB/s" else 1e12
+    achieved = amount / seconds / scale
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel}
+
+
+def cpu_baseline(inp, heads, target_s=12.0):
+    """Oracle tokens/s on a leading slice of the prefill workload, all heads."""
+    from oracle import kda_oracle
+
+    def run(tokens):
+        sl = {k: inp[k][:, :tokens] for k in ("q", "k", "v", "alpha", "beta")}
+        t0 = time.perf_counter()
+        kda_oracle.forward(sl["q"], sl["k"], sl["v"], sl["alpha"], sl["beta"])
+        return time.perf_counter() - t0
+
+    probe = 256
+    dt = run(probe)
+    T = inp["q"].shape[1]
+    tokens = int(min(T, max(probe, probe * target_s / max(dt, 1e-6))))
+    tokens = max(64, tokens // 64 * 64)
+    dt = run(tokens)
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": kda_oracle.threads(),
+            "kind": "oracle",
+            "sample": f"first {tokens} tokens of the prefill workload, all {heads} heads "
+                      f"({tokens * heads} token-heads), fp64 token-by-token, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter calibration runs)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one MI355X only (--gpus {args.gpus}, WORLD_SIZE {world}): the KDA "
+              "hot path here is a single-GPU build; see DESIGN.md for how it would shard.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import linear_attention_sequence_gated_amd as kda
+    import workloads
+    from linear_attention_sequence_gated_amd import build as kbuild
+
+    if not os.path.exists(kbuild.LIB):
+        kbuild.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---- prefill -------------------------------------------------------------
+    w = workloads.CONFIGS[PREFILL_CFG]
+    log(f"generating {w.name} inputs")
+    host = workloads.config_inputs(PREFILL_CFG)
+    d = {k: (v.to(dev) if v is not None else None) for k, v in host.items()}
+    pre = kda.Prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"],
+                      chunk_size=w.chunk, o_dtype=torch.bfloat16)
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        pre.intra()
+        pre.inter()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        pre.intra()
+        ev[i][1].record(stream)
+        pre.inter()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    intra_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    inter_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    step_ms = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
+    tokens = w.batch * w.seqlen
+    th = tokens * w.heads
+    alg = algorithmic(w.dk, w.dv, w.chunk)
+    intra_roof = roof("hbm", th * alg["intra_bytes_per_token_head"], intra_ms / 1e3, "GB/s",
+                      "kda_intra_kernel")
+    inter_roof = roof("mfma", th * alg["inter_flops_per_token_head"], inter_ms / 1e3, "TFLOP/s",
+                      "kda_inter_kernel")
+    step_bytes = th * alg["prefill_bytes_per_token_head"] + w.batch * w.heads * alg["state_bytes_per_seq_head"]
+    step_roof = roof("hbm", step_bytes, step_ms / 1e3, "GB/s", "kda_chunk_fwd (whole step)")
+    del pre, d
+    torch.cuda.empty_cache()
+
+    # ---- decode --------------------------------------------------------------
+    wd = workloads.CONFIGS[DECODE_CFG]
+    log(f"generating {wd.name} inputs")
+    dh = workloads.decode_inputs(DECODE_CFG, steps=args.decode_steps)
+    dd = {k: v.to(dev) for k, v in dh.items()}
+    state = dd["S0"].clone()
+    o_dec = torch.empty(dd["v"].shape[1:], dtype=torch.bfloat16, device=dev)
+
+    def dstep(t):
+        kda.decode_step(dd["q"][t], dd["k"][t], dd["v"][t], dd["alpha"][t], dd["beta"][t], state,
+                        o=o_dec, o_dtype=torch.bfloat16)
+
+    for t in range(min(3, args.decode_steps)):
+        dstep(t)
+    state.copy_(dd["S0"])  # the timed run starts from the pristine state
+    torch.cuda.synchronize()
+    dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.decode_steps + 1)]
+    log(f"timing {args.decode_steps} decode steps")
+    dev_ev[0].record(stream)
+    for t in range(args.decode_steps):
+        dstep(t)
+        dev_ev[t + 1].record(stream)
+    torch.cuda.synchronize()
+    dec_ms = dev_ev[0].elapsed_time(dev_ev[-1]) / args.decode_steps
+    units = wd.decode_seqs * wd.heads
+    dec_bytes = units * alg["decode_bytes_per_head_step"]
+    state_bytes = units * 2 * wd.dk * wd.dv * 4
+    dec_roof = roof("hbm", dec_bytes, dec_ms / 1e3, "GB/s", "kda_decode_kernel")
+    decode = {
+        "workload": f"decode {wd.decode_seqs} seqs x H{wd.heads} dk=dv={wd.dk}, "
+                    f"{args.decode_steps} in-place steps (bf16 q/k/v/o, fp32 alpha/beta/state)",
+        "value": round(state_bytes / (dec_ms / 1e3) / 1e9, 1), "unit": "GB/s (state read + write)",
+        "ms_per_step": round(dec_ms, 4),
+        "tokens_per_s": round(wd.decode_seqs / (dec_ms / 1e3), 1),
+        "roofline": dec_roof,
+    }
+    del dd, state
+    torch.cuda.empty_cache()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- CPU baseline (oracle) ------------------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        cpu = cpu_baseline(host, w.heads)
+
+    kernels = {"kda_intra_kernel": dict(intra_roof, ms_per_launch=round(intra_ms, 4)),
+               "kda_inter_kernel": dict(inter_roof, ms_per_launch=round(inter_ms, 4)),
+               "kda_decode_kernel": dict(dec_roof, ms_per_launch=round(dec_ms, 4))}
+    dominant = intra_roof if intra_ms >= inter_ms else inter_roof
+    out = {
+        "metric": METRIC,
+        "value": round(tokens / (step_ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"long-context prefill B{w.batch} H{w.heads} T{w.seqlen} dk=dv={w.dk} "
+                               f"chunk {w.chunk} (bf16 q/k/v/o, fp32 alpha/beta/state; fp16 matrix-core "
+                               "operands, fp32 accumulation)",
+                   "batch": w.batch, "seq_len": w.seqlen, "heads": w.heads, "dk": w.dk, "dv": w.dv,
+                   "chunk": w.chunk},
+        "roofline": dominant,
+        "step_roofline": step_roof,
+        "kernels": kernels,
+        "decode": decode,
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

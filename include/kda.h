@@ -118,6 +118,29 @@ kda_status_t kda_chunk_fwd(const kda_chunk_params_t* params,
                            void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* The two halves of kda_chunk_fwd, for callers that schedule them separately
+ * (for example to time them, or to overlap the intra-chunk half of one call
+ * with other work).  Same arguments and validation as kda_chunk_fwd.
+ * kda_chunk_fwd_intra reads q, k, v, alpha, beta (and cu_seqlens) and fills
+ * the workspace with each chunk's intra-chunk factors; kda_chunk_fwd_inter
+ * then reads only the workspace, initial_state and cu_seqlens and writes o and
+ * final_state.  Calling _intra then _inter on one stream with the same
+ * arguments and an untouched workspace is exactly kda_chunk_fwd. */
+kda_status_t kda_chunk_fwd_intra(const kda_chunk_params_t* params,
+                                 const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* beta,
+                                 const float* initial_state, const int32_t* cu_seqlens,
+                                 void* o, float* final_state,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+kda_status_t kda_chunk_fwd_inter(const kda_chunk_params_t* params,
+                                 const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* beta,
+                                 const float* initial_state, const int32_t* cu_seqlens,
+                                 void* o, float* final_state,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* One decode step: every (sequence, head) consumes a single token and its
  * state is updated in place.
  *   q, k   [N, H, dk]  D        v  [N, H, dv]  D      o  [N, H, dv]  o_dtype

@@ -22,7 +22,8 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "
            4: "KDA_ERR_HIP"}
 
 # Every symbol include/kda.h declares.
-EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step")
+EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
+            "kda_chunk_fwd_inter", "kda_decode_step")
 
 
 class KdaError(RuntimeError):
@@ -60,9 +61,10 @@ def load() -> ctypes.CDLL:
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_int
     lib.kda_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(ChunkParams), ctypes.POINTER(sz)]
-    lib.kda_chunk_fwd.restype = ctypes.c_int
-    lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(ChunkParams), vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                  vp, sz, vp]
+    for name in ("kda_chunk_fwd", "kda_chunk_fwd_intra", "kda_chunk_fwd_inter"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.POINTER(ChunkParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     _lib = lib
@@ -119,6 +121,59 @@ def workspace_size(q: torch.Tensor, v: torch.Tensor, cu_seqlens=None, chunk_size
     return out.value
 
 
+class Prefill:
+    """A kda_chunk_fwd call with its arguments marshalled once.
+
+    ``run()`` issues kda_chunk_fwd; ``intra()`` / ``inter()`` issue its two
+    halves.  The tensors are kept alive by this object.
+    """
+
+    def __init__(self, q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_size: int = 64,
+                 scale: float = 1.0, output_final_state: bool = True, o=None, final_state=None,
+                 workspace=None, stream=None, o_dtype: Optional[torch.dtype] = None):
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        _need(k.shape == q.shape and alpha.shape == q.shape, "q, k and alpha must share [B,T,H,dk]")
+        _need(v.shape == (B, T, H, dv) and beta.shape == (B, T, H), "v/beta shapes")
+        _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
+        _need(alpha.dtype == torch.float32 and beta.dtype == torch.float32, "alpha, beta must be fp32")
+        for t in (q, k, v, alpha, beta):
+            _need(t.is_cuda and t.is_contiguous(), "inputs must be contiguous device tensors")
+        n = B if cu_seqlens is None else cu_seqlens.numel() - 1
+        if cu_seqlens is not None:
+            _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda, "cu_seqlens: int32 device")
+        if initial_state is not None:
+            _need(initial_state.shape == (n, H, dk, dv) and initial_state.dtype == torch.float32
+                  and initial_state.is_contiguous(), "initial_state must be fp32 [N,H,dk,dv]")
+        o_dtype = q.dtype if o_dtype is None else o_dtype
+        if o is None:
+            o = torch.empty(v.shape, dtype=o_dtype, device=v.device)
+        _need(o.shape == v.shape and o.dtype == o_dtype and o.is_contiguous(), "o shape/dtype")
+        if final_state is None and output_final_state:
+            final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
+        self.params = chunk_params(q, v, cu_seqlens, chunk_size, scale, o_dtype)
+        need = workspace_size(q, v, cu_seqlens, chunk_size, scale)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        self.o, self.final_state, self.workspace = o, final_state, workspace
+        self._keep = (q, k, v, alpha, beta, initial_state, cu_seqlens)
+        self._args = (ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                      _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(final_state), _ptr(workspace),
+                      ctypes.c_size_t(workspace.numel()), _stream(stream))
+        self._lib = load()
+
+    def run(self):
+        _check("kda_chunk_fwd", self._lib.kda_chunk_fwd(*self._args))
+        return self.o, self.final_state
+
+    def intra(self):
+        _check("kda_chunk_fwd_intra", self._lib.kda_chunk_fwd_intra(*self._args))
+
+    def inter(self):
+        _check("kda_chunk_fwd_inter", self._lib.kda_chunk_fwd_inter(*self._args))
+        return self.o, self.final_state
+
+
 def chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_size: int = 64,
               scale: float = 1.0, output_final_state: bool = True, o=None, final_state=None,
               workspace=None, stream=None, o_dtype: Optional[torch.dtype] = None):
@@ -129,35 +184,8 @@ def chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_s
     None (device tensors).  ``final_state`` may be ``initial_state`` (in-place resume).
     ``o_dtype`` (default: the dtype of q) is bf16 or fp32.
     """
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    _need(k.shape == q.shape and alpha.shape == q.shape, "q, k and alpha must share [B,T,H,dk]")
-    _need(v.shape == (B, T, H, dv) and beta.shape == (B, T, H), "v/beta shapes")
-    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
-    _need(alpha.dtype == torch.float32 and beta.dtype == torch.float32, "alpha, beta must be fp32")
-    for t in (q, k, v, alpha, beta):
-        _need(t.is_cuda and t.is_contiguous(), "inputs must be contiguous device tensors")
-    n = B if cu_seqlens is None else cu_seqlens.numel() - 1
-    if cu_seqlens is not None:
-        _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda, "cu_seqlens: int32 device")
-    if initial_state is not None:
-        _need(initial_state.shape == (n, H, dk, dv) and initial_state.dtype == torch.float32
-              and initial_state.is_contiguous(), "initial_state must be fp32 [N,H,dk,dv]")
-    o_dtype = q.dtype if o_dtype is None else o_dtype
-    if o is None:
-        o = torch.empty(v.shape, dtype=o_dtype, device=v.device)
-    _need(o.shape == v.shape and o.dtype == o_dtype and o.is_contiguous(), "o shape/dtype")
-    if final_state is None and output_final_state:
-        final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
-    p = chunk_params(q, v, cu_seqlens, chunk_size, scale, o_dtype)
-    need = workspace_size(q, v, cu_seqlens, chunk_size, scale)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    st = load().kda_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                              _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(final_state),
-                              _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
-    _check("kda_chunk_fwd", st)
-    return o, final_state
+    return Prefill(q, k, v, alpha, beta, initial_state, cu_seqlens, chunk_size, scale,
+                   output_final_state, o, final_state, workspace, stream, o_dtype).run()
 
 
 def decode_step(q, k, v, alpha, beta, state, scale: float = 1.0, o=None, stream=None,

@@ -84,10 +84,14 @@ kda_status_t kda_chunk_fwd_workspace_size(const kda_chunk_params_t* p, size_t* b
     return KDA_OK;
 }
 
-kda_status_t kda_chunk_fwd(const kda_chunk_params_t* p, const void* q, const void* k, const void* v,
-                           const float* alpha, const float* beta, const float* initial_state,
-                           const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+namespace {
+
+enum Phase { kBoth = 3, kIntra = 1, kInter = 2 };
+
+kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta, const float* initial_state,
+                            const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
+                            size_t workspace_bytes, void* stream, int phases) {
     kda_status_t st = check_params(p);
     if (st != KDA_OK) return st;
     const bool packed = cu_seqlens != nullptr;
@@ -139,14 +143,48 @@ kda_status_t kda_chunk_fwd(const kda_chunk_params_t* p, const void* q, const voi
     a.chunks_per_seq = (int32_t)((p->seqlen + C - 1) / C);
     a.scale = p->scale;
     a.o_f32 = p->o_dtype == KDA_DTYPE_F32;
+    const bool bf16 = p->qkv_dtype == KDA_DTYPE_BF16;
 
     hipError_t e = hipSuccess;
-    if (packed) {
-        e = kda::launch_chunk_offsets(cu_seqlens, p->num_seqs, C, reinterpret_cast<int32_t*>(ws), s);
+    if (phases & kIntra) {
+        if (packed) {
+            e = kda::launch_chunk_offsets(cu_seqlens, p->num_seqs, C, reinterpret_cast<int32_t*>(ws), s);
+            if (e != hipSuccess) return KDA_ERR_HIP;
+        }
+        e = kda::launch_intra(a, p->head_dim_k, C, bf16, (int)pl.max_chunks, s);
         if (e != hipSuccess) return KDA_ERR_HIP;
     }
-    e = kda::launch_prefill(a, p->head_dim_k, C, p->qkv_dtype == KDA_DTYPE_BF16, (int)pl.max_chunks, s);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    if (phases & kInter) {
+        e = kda::launch_inter(a, p->head_dim_k, C, bf16, s);
+        if (e != hipSuccess) return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
+}  // namespace
+
+kda_status_t kda_chunk_fwd(const kda_chunk_params_t* p, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const float* initial_state,
+                           const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return chunk_fwd_impl(p, q, k, v, alpha, beta, initial_state, cu_seqlens, o, final_state, workspace,
+                          workspace_bytes, stream, kBoth);
+}
+
+kda_status_t kda_chunk_fwd_intra(const kda_chunk_params_t* p, const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* beta, const float* initial_state,
+                                 const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    return chunk_fwd_impl(p, q, k, v, alpha, beta, initial_state, cu_seqlens, o, final_state, workspace,
+                          workspace_bytes, stream, kIntra);
+}
+
+kda_status_t kda_chunk_fwd_inter(const kda_chunk_params_t* p, const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* beta, const float* initial_state,
+                                 const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    return chunk_fwd_impl(p, q, k, v, alpha, beta, initial_state, cu_seqlens, o, final_state, workspace,
+                          workspace_bytes, stream, kInter);
 }
 
 kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t dk, int32_t dv, float scale,

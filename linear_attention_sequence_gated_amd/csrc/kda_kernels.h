@@ -43,7 +43,8 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t
 // C is the requested chunk size; the chunk the kernels use is
 // effective_chunk(DK, C, bf16) (fp32 operands with dk = 128 use at most 32).
 int effective_chunk(int DK, int C, bool bf16);
-hipError_t launch_prefill(const PrefillArgs& a, int DK, int C, bool bf16, int max_chunks, hipStream_t s);
+hipError_t launch_intra(const PrefillArgs& a, int DK, int C, bool bf16, int max_chunks, hipStream_t s);
+hipError_t launch_inter(const PrefillArgs& a, int DK, int C, bool bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int DK, int DV, bool bf16, hipStream_t s);
 int64_t chunk_block_bytes(int DK, int C, int DV, bool bf16);
 

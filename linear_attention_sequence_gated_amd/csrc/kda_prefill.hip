@@ -635,40 +635,40 @@ __global__ __launch_bounds__(64) void kda_inter_kernel(const PrefillArgs a) {
 // Host-side launchers (called from the C ABI after validation).
 // ---------------------------------------------------------------------------
 template <int DK, int C, typename In>
-static hipError_t launch_prefill_t(const PrefillArgs& a, int max_chunks, hipStream_t stream) {
+static hipError_t launch_phase_t(const PrefillArgs& a, int max_chunks, bool intra, hipStream_t stream) {
     if constexpr (!Intra<DK, C, typename OperandOf<In>::type>::kFits) {
         return hipErrorInvalidValue;  // effective_chunk() never selects this
     } else {
-        if (max_chunks > 0 && a.H > 0) {
-            hipLaunchKernelGGL((kda_intra_kernel<DK, C, In>), dim3(max_chunks, a.H), dim3(256), 0, stream, a);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
+        if (intra) {
+            if (max_chunks > 0) {
+                hipLaunchKernelGGL((kda_intra_kernel<DK, C, In>), dim3(max_chunks, a.H), dim3(256), 0, stream, a);
+            }
+        } else {
+            const int units = a.N * a.H;
+            const int blocks = ((units + 7) / 8) * 8 * (a.DV / 16);
+            hipLaunchKernelGGL((kda_inter_kernel<DK, C, In>), dim3(blocks), dim3(64), 0, stream, a);
         }
-        const int units = a.N * a.H;
-        const int ns = a.DV / 16;
-        const int blocks = ((units + 7) / 8) * 8 * ns;
-        hipLaunchKernelGGL((kda_inter_kernel<DK, C, In>), dim3(blocks), dim3(64), 0, stream, a);
         return hipGetLastError();
     }
 }
 
 template <int DK, typename In>
-static hipError_t launch_prefill_c(const PrefillArgs& a, int C, int max_chunks, hipStream_t s) {
+static hipError_t launch_phase_c(const PrefillArgs& a, int C, int max_chunks, bool intra, hipStream_t s) {
     switch (C) {
-        case 16: return launch_prefill_t<DK, 16, In>(a, max_chunks, s);
-        case 32: return launch_prefill_t<DK, 32, In>(a, max_chunks, s);
-        case 64: return launch_prefill_t<DK, 64, In>(a, max_chunks, s);
+        case 16: return launch_phase_t<DK, 16, In>(a, max_chunks, intra, s);
+        case 32: return launch_phase_t<DK, 32, In>(a, max_chunks, intra, s);
+        case 64: return launch_phase_t<DK, 64, In>(a, max_chunks, intra, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <typename In>
-static hipError_t launch_prefill_k(const PrefillArgs& a, int DK, int C, int max_chunks, hipStream_t s) {
+static hipError_t launch_phase_k(const PrefillArgs& a, int DK, int C, int max_chunks, bool intra, hipStream_t s) {
     switch (DK) {
-        case 16: return launch_prefill_c<16, In>(a, C, max_chunks, s);
-        case 32: return launch_prefill_c<32, In>(a, C, max_chunks, s);
-        case 64: return launch_prefill_c<64, In>(a, C, max_chunks, s);
-        case 128: return launch_prefill_c<128, In>(a, C, max_chunks, s);
+        case 16: return launch_phase_c<16, In>(a, C, max_chunks, intra, s);
+        case 32: return launch_phase_c<32, In>(a, C, max_chunks, intra, s);
+        case 64: return launch_phase_c<64, In>(a, C, max_chunks, intra, s);
+        case 128: return launch_phase_c<128, In>(a, C, max_chunks, intra, s);
     }
     return hipErrorInvalidValue;
 }
@@ -693,9 +693,13 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t
     return hipGetLastError();
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, int DK, int C, bool bf16, int max_chunks, hipStream_t s) {
-    return bf16 ? launch_prefill_k<__bf16>(a, DK, C, max_chunks, s)
-                : launch_prefill_k<float>(a, DK, C, max_chunks, s);
+hipError_t launch_intra(const PrefillArgs& a, int DK, int C, bool bf16, int max_chunks, hipStream_t s) {
+    return bf16 ? launch_phase_k<__bf16>(a, DK, C, max_chunks, true, s)
+                : launch_phase_k<float>(a, DK, C, max_chunks, true, s);
+}
+
+hipError_t launch_inter(const PrefillArgs& a, int DK, int C, bool bf16, hipStream_t s) {
+    return bf16 ? launch_phase_k<__bf16>(a, DK, C, 0, false, s) : launch_phase_k<float>(a, DK, C, 0, false, s);
 }
 
 int64_t chunk_block_bytes(int DK, int C, int DV, bool bf16) {

@@ -42,6 +42,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 enum { KDA_ORACLE_F32 = 0, KDA_ORACLE_BF16 = 1, KDA_ORACLE_F64 = 2 };
 
@@ -139,4 +142,14 @@ int kda_oracle_forward(int64_t num_seqs, const int64_t* cu_seqlens,
         free(r);
     }
     return failed ? -2 : 0;
+}
+
+/* Number of threads the parallel loop above runs with. */
+int kda_oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

@@ -30,8 +30,15 @@ def _load():
                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        lib.kda_oracle_threads.restype = ctypes.c_int
+        lib.kda_oracle_threads.argtypes = []
         _lib = lib
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle runs with."""
+    return int(_load().kda_oracle_threads())
 
 
 def _as_cpu(x):

@@ -313,3 +313,19 @@ def test_decode_steps_equal_prefill():
     op, Sp = gpu_prefill(pre, 64)
     assert rel_err(od, op.transpose(1, 0, 2, 3)) < 1e-4
     assert rel_err(Sd, Sp) < 1e-4
+
+
+def test_split_phases_equal_fused_call():
+    """kda_chunk_fwd_intra then kda_chunk_fwd_inter is exactly kda_chunk_fwd."""
+    inp = workloads.make_inputs(1, 300, 2, 128, 128, torch.bfloat16, s0_std=0.02, seed=51,
+                                lengths=None)
+    d = to_dev(inp)
+    pre = kda.Prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], None, chunk_size=64,
+                      o_dtype=torch.float32)
+    o1, S1 = pre.run()
+    o1, S1 = o1.clone(), S1.clone()
+    pre.o.zero_()
+    pre.intra()
+    o2, S2 = pre.inter()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
