@@ -187,7 +187,6 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
     T* Qf = reinterpret_cast<T*>(blk + cb.q);
     T* Kbf = reinterpret_cast<T*>(blk + cb.kb);
     T* Pf = reinterpret_cast<T*>(blk + cb.p);
-    T* Uf = reinterpret_cast<T*>(blk + cb.u);
     float* gam = reinterpret_cast<float*>(blk + cb.gam);
 
     if (tid == 0) *srange = 0u;
@@ -205,20 +204,25 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int r = 4 * sgi + u;
-            const bool in = p1 && r < valid;
             const int64_t base = ((pos.tok0 + r) * H + h) * DK + 8 * cg;
+            float al[8];
+            if (p1 && r < valid) {
+                load8(kg + base, kr[u]);
+                load8(qg + base, qr[u]);
+                load8(a.alpha + base, al);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { kr[u][e] = 0.f; qr[u][e] = 0.f; al[e] = 1.f; }
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                kr[u][e] = in ? load_as_float(kg, base + e) : 0.f;
-                qr[u][e] = in ? load_as_float(qg, base + e) : 0.f;
-                const float al = in ? a.alpha[base + e] : 1.f;
-                run[e] += fmaxf(__builtin_amdgcn_logf(al), kLog2Floor);
+                run[e] += fmaxf(__builtin_amdgcn_logf(al[e]), kLog2Floor);
                 gv[u][e] = run[e];
             }
         }
         if (p1) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) seg[sgi * DK + 8 * cg + e] = run[e];
+            *reinterpret_cast<f32x4*>(seg + sgi * DK + 8 * cg) = f32x4{run[0], run[1], run[2], run[3]};
+            *reinterpret_cast<f32x4*>(seg + sgi * DK + 8 * cg + 4) = f32x4{run[4], run[5], run[6], run[7]};
         }
     }
     // v of this thread's tokens, kept in registers until the value tile is built
@@ -229,10 +233,12 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int r = 4 * sgv + u;
-        const bool in = pv && r < valid;
-        const int64_t base = ((pos.tok0 + r) * H + h) * DV + 8 * cgv;
+        if (pv && r < valid) {
+            load8(vg + ((pos.tok0 + r) * H + h) * DV + 8 * cgv, vr[u]);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vr[u][e] = in ? load_as_float(vg, base + e) : 0.f;
+            for (int e = 0; e < 8; ++e) vr[u][e] = 0.f;
+        }
     }
     __syncthreads();
     float tot[8];
@@ -241,11 +247,13 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) { off[e] = 0.f; tot[e] = 0.f; }
         for (int s = 0; s < I::NSEG; ++s) {
+            const f32x4 t0 = *reinterpret_cast<const f32x4*>(seg + s * DK + 8 * cg);
+            const f32x4 t1 = *reinterpret_cast<const f32x4*>(seg + s * DK + 8 * cg + 4);
+            const float t[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float t = seg[s * DK + 8 * cg + e];
-                if (s < sgi) off[e] += t;
-                tot[e] += t;
+                if (s < sgi) off[e] += t[e];
+                tot[e] += t[e];
             }
         }
 #pragma unroll
@@ -280,67 +288,81 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
     __syncthreads();
     const bool fast = __uint_as_float(*srange) <= kFastRange;
     if (p1) {
-        float kbar[4][8];
+        const bool last = Rb == NB - 1;
+        float G0[8], hR[8], Gn[8], link[8], gb[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int c = 8 * cg + e;
-            const float G0 = Gs[Rb * DK + c];
-            const float hR = 0.5f * (G0 - Ge[Rb * DK + c]);
-            const bool last = Rb == NB - 1;
-            const float Gn = last ? 0.f : Gs[(Rb + 1) * DK + c];
+            G0[e] = Gs[Rb * DK + c];
+            hR[e] = 0.5f * (G0[e] - Ge[Rb * DK + c]);
+            Gn[e] = last ? 0.f : Gs[(Rb + 1) * DK + c];
             // 2^{g_C - G_{R+1}} links the off-diagonal column factor to Kbar
-            const float link = last ? 1.f : __builtin_amdgcn_exp2f(fminf(tot[e] - Gn, 0.f));
-            const float gb = __builtin_amdgcn_exp2f(fminf(G0 - hR, 0.f));
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int r = 4 * sgi + u;
-                const float gr = gv[u][e];
-                float gam_r, kb_f;
-                if (fast) {
-                    const float fa = __builtin_amdgcn_exp2f(gr - G0 + hR);   // in 2^[-h, h]
-                    const float fb = __builtin_amdgcn_rcpf(fa);
-                    Ak[r * LD_ROW + c] = (T)(kr[u][e] * fa);
-                    Aq[r * LD_ROW + c] = (T)(qr[u][e] * fa);
-                    Bd[r * LD_ROW + c] = (T)(kr[u][e] * fb);
-                    gam_r = fa * gb;                                        // 2^{g_r}
-                    if (!last) {
-                        const float fo = __builtin_amdgcn_exp2f(fminf(Gn - gr, 0.f));
-                        Bo[r * LD_ROW + c] = (T)(kr[u][e] * fo);
-                        kb_f = fo * link;                                    // 2^{g_C - g_r}
-                    } else {
-                        kb_f = __builtin_amdgcn_exp2f(fminf(tot[e] - gr, 0.f));
-                    }
-                } else {
-                    gam_r = __builtin_amdgcn_exp2f(gr);
-                    kb_f = __builtin_amdgcn_exp2f(fminf(tot[e] - gr, 0.f));
-                }
-                KtT[c * LD_CT + r] = (T)(kr[u][e] * gam_r);   // Ktilde, transposed
-                qr[u][e] *= gam_r;                            // Qtilde
-                kbar[u][e] = kr[u][e] * kb_f;                 // Kbar
-            }
+            link[e] = last ? 1.f : __builtin_amdgcn_exp2f(fminf(tot[e] - Gn[e], 0.f));
+            gb[e] = __builtin_amdgcn_exp2f(fminf(G0[e] - hR[e], 0.f));
         }
+        float kbar[4][8], ktil[4][8];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int r = 4 * sgi + u;
+            float ak[8], aq[8], bd[8], bo[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float gr = gv[u][e];
+                float gam_r, kb_f;
+                if (fast) {
+                    const float fa = __builtin_amdgcn_exp2f(gr - G0[e] + hR[e]);   // in 2^[-h, h]
+                    const float fb = __builtin_amdgcn_rcpf(fa);
+                    ak[e] = kr[u][e] * fa;
+                    aq[e] = qr[u][e] * fa;
+                    bd[e] = kr[u][e] * fb;
+                    gam_r = fa * gb[e];                                       // 2^{g_r}
+                    if (!last) {
+                        const float fo = __builtin_amdgcn_exp2f(fminf(Gn[e] - gr, 0.f));
+                        bo[e] = kr[u][e] * fo;
+                        kb_f = fo * link[e];                                  // 2^{g_C - g_r}
+                    } else {
+                        bo[e] = 0.f;
+                        kb_f = __builtin_amdgcn_exp2f(fminf(tot[e] - gr, 0.f));
+                    }
+                } else {
+                    ak[e] = aq[e] = bd[e] = bo[e] = 0.f;
+                    gam_r = __builtin_amdgcn_exp2f(gr);
+                    kb_f = __builtin_amdgcn_exp2f(fminf(tot[e] - gr, 0.f));
+                }
+                ktil[u][e] = kr[u][e] * gam_r;   // Ktilde
+                qr[u][e] *= gam_r;               // Qtilde
+                kbar[u][e] = kr[u][e] * kb_f;    // Kbar
+            }
+            if (fast) {
+                store8(Ak + r * LD_ROW + 8 * cg, ak);
+                store8(Aq + r * LD_ROW + 8 * cg, aq);
+                store8(Bd + r * LD_ROW + 8 * cg, bd);
+                if (!last) store8(Bo + r * LD_ROW + 8 * cg, bo);
+            }
 #pragma unroll
             for (int hq = 0; hq < 2; ++hq) {  // Qtilde quads: token r, channel groups 2cg, 2cg+1
                 const int a4 = 2 * cg + hq, ut = a4 >> 2, gq = a4 & 3;
                 const f32x4 v4{qr[u][4 * hq], qr[u][4 * hq + 1], qr[u][4 * hq + 2], qr[u][4 * hq + 3]};
-                *reinterpret_cast<Q*>(Qf + Frag<T>::off(r >> 4, ut, 16 * gq + (r & 15), DK)) = make_quad<T>(v4);
+                store_q<T>(Qf + Frag<T>::off(r >> 4, ut, 16 * gq + (r & 15), DK), v4);
             }
         }
-        {   // Kbar^T quads: channel c, tokens 4*sgi .. 4*sgi+3
+        {   // Ktilde^T into LDS and Kbar^T quads to the workspace: channel c, tokens 4*sgi .. +3
             const int ut = sgi >> 2, gq = sgi & 3;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int c = 8 * cg + e;
-                const f32x4 v4{kbar[0][e], kbar[1][e], kbar[2][e], kbar[3][e]};
-                *reinterpret_cast<Q*>(Kbf + Frag<T>::off(c >> 4, ut, 16 * gq + (c & 15), C)) = make_quad<T>(v4);
+                store_q<T>(KtT + c * LD_CT + 4 * sgi, f32x4{ktil[0][e], ktil[1][e], ktil[2][e], ktil[3][e]});
+                store_q<T>(Kbf + Frag<T>::off(c >> 4, ut, 16 * gq + (c & 15), C),
+                           f32x4{kbar[0][e], kbar[1][e], kbar[2][e], kbar[3][e]});
             }
         }
         if (sgi == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) gam[8 * cg + e] = __builtin_amdgcn_exp2f(tot[e]);
+            *reinterpret_cast<f32x4*>(gam + 8 * cg) =
+                f32x4{__builtin_amdgcn_exp2f(tot[0]), __builtin_amdgcn_exp2f(tot[1]), __builtin_amdgcn_exp2f(tot[2]),
+                      __builtin_amdgcn_exp2f(tot[3])};
+            *reinterpret_cast<f32x4*>(gam + 8 * cg + 4) =
+                f32x4{__builtin_amdgcn_exp2f(tot[4]), __builtin_amdgcn_exp2f(tot[5]), __builtin_amdgcn_exp2f(tot[6]),
+                      __builtin_amdgcn_exp2f(tot[7])};
         }
     }
     __syncthreads();
@@ -487,8 +509,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
     if (pv) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) VT[(8 * cgv + e) * LD_CT + 4 * sgv + u] = (T)vr[u][e];
+            store_q<T>(VT + (8 * cgv + e) * LD_CT + 4 * sgv, f32x4{vr[0][e], vr[1][e], vr[2][e], vr[3][e]});
     }
     for (int e = tid; e < NB * NB * 64; e += I::kThreads) {
         const int ct = e / (NB * 64), ut = (e / 64) % NB, ln = e & 63;
@@ -520,29 +541,86 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
             bq[u] = *reinterpret_cast<const Q*>(VT + (16 * s + cl) * LD_CT + 16 * u + 4 * g);
         }
         const f32x4 res = mma_quads_upto(aq, bq, tb, zero4());
-        *reinterpret_cast<Q*>(Uf + ((int64_t)(s * 64 + lane) * NB + tb) * 4) = make_quad<T>(res);
+        T* Us = reinterpret_cast<T*>(blk + cb.u_slice(s));
+        *reinterpret_cast<Q*>(Us + (lane * NB + tb) * 4) = make_quad<T>(res);
     }
 }
 
 // ---------------------------------------------------------------------------
-// K2: inter-chunk pass.  One wave per (sequence, head, 16 value columns).
+// K2: inter-chunk pass.  One workgroup per (sequence, head, group of up to 4
+// value slices of 16 columns):
+//   waves 0 .. ncw-1  compute: each holds its dk x 16 slice of S in MFMA
+//                     accumulator registers (fp32) and walks the chunks;
+//   wave ncw          I/O: copies the next chunk's block from the workspace
+//                     into the other half of a double-buffered LDS ring with
+//                     direct-to-LDS loads, so compute waves only read LDS and
+//                     only write global memory (they never wait on a load).
+// One s_barrier per chunk hands the ring over.  The slice groups of one
+// (sequence, head) are placed on one XCD (blocks are dealt round-robin over
+// the 8 XCDs) so the block is fetched from HBM once per XCD.
 // ---------------------------------------------------------------------------
+// All N quads of row tile rt of a fragment matrix (K = 16 N), read as whole
+// 16-byte vectors per lane.
+template <int N>
+__device__ __forceinline__ void load_frag(f16x4 (&q)[N], const char* base, int rt, int lane) {
+    const _Float16* p = reinterpret_cast<const _Float16*>(base) + Frag<_Float16>::off(rt, 0, lane, 16 * N);
+    constexpr int NG = (N + 1) / 2;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        const _Float16* pg = p + gi * 64 * 8;
+        if (2 * gi + 1 < N) {
+            const f16x8 v = *reinterpret_cast<const f16x8*>(pg);
+            q[2 * gi] = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+            q[2 * gi + 1] = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+        } else {
+            q[2 * gi] = *reinterpret_cast<const f16x4*>(pg);
+        }
+    }
+}
+template <int N>
+__device__ __forceinline__ void load_frag(f32x4 (&q)[N], const char* base, int rt, int lane) {
+    const float* p = reinterpret_cast<const float*>(base) + Frag<float>::off(rt, 0, lane, 16 * N);
+#pragma unroll
+    for (int u = 0; u < N; ++u) q[u] = *reinterpret_cast<const f32x4*>(p + u * 64 * 4);
+}
+
+template <int DK, int C, typename T> struct Inter {
+    static constexpr int64_t kShared = (2 * Frag<T>::elems(C, DK) + Frag<T>::elems(DK, C) + Frag<T>::elems(C, C)) *
+                                           (int64_t)sizeof(T) + round_kib(DK * 4);
+    static constexpr int64_t kGroupMax = round_kib((int64_t)kMaxComputeWaves * C * 16 * sizeof(T));
+    static constexpr int64_t kBuf = kShared + kGroupMax;
+    static constexpr bool kFits = 2 * kBuf <= 163840;
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// Copy `bytes` (a multiple of 1 KiB) from global to LDS, 16 bytes per lane per instruction.
+__device__ __forceinline__ void dma_to_lds(const char* src, char* dst, int64_t bytes, int lane) {
+    for (int64_t off = 0; off < bytes; off += 1024)
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + off + lane * 16), (lds_void_t*)(dst + off), 16, 0, 0);
+}
+
 template <int DK, int C, typename In>
-__global__ __launch_bounds__(64) void kda_inter_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(64 * (kMaxComputeWaves + 1)) void kda_inter_kernel(const PrefillArgs a) {
     using T = typename OperandOf<In>::type;
     using Q = quad_t<T>;
+    using X = Inter<DK, C, T>;
+    static_assert(X::kFits, "LDS ring of the inter-chunk kernel exceeds one workgroup");
     constexpr int NB = C / 16, NQK = DK / 16;
-    const int lane = threadIdx.x, g = lane >> 4, cl = lane & 15;
-    const int NS = a.DV / 16;
-    // blocks are dealt round-robin over the 8 XCDs: keep the slices of one
-    // (sequence, head) on one XCD so they share its L2
-    const int b = blockIdx.x, xcd = b & 7, jx = b >> 3;
-    const int s = jx % NS;
-    const int unit = (jx / NS) * 8 + xcd;
-    if (unit >= a.N * a.H) return;
-    const int n = unit / a.H, h = unit % a.H;
+    __shared__ __attribute__((aligned(1024))) char ring[2 * X::kBuf];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, cl = lane & 15;
     const int H = a.H, DV = a.DV;
-    const int col = 16 * s + cl;
+    const ChunkBlock<T> cb(DK, C, DV);
+    const int ncw = cb.ncw, ngroups = DV / 16 / ncw;
+    // blocks are dealt round-robin over the 8 XCDs: keep the slice groups of
+    // one (sequence, head) on one XCD so they share its L2
+    const int b = blockIdx.x, xcd = b & 7, jx = b >> 3;
+    const int grp = jx % ngroups;
+    const int unit = (jx / ngroups) * 8 + xcd;
+    if (unit >= a.N * a.H) return;  // whole workgroup
+    const int n = unit / H, h = unit % H;
 
     int c_begin, c_end;
     int64_t tok_begin, seq_len;
@@ -558,6 +636,26 @@ __global__ __launch_bounds__(64) void kda_inter_kernel(const PrefillArgs a) {
         seq_len = a.T;
     }
 
+    if (wave == ncw) {
+        // ---- I/O wave ----------------------------------------------------------
+        auto fetch = [&](int x, int slot) {
+            const char* src = a.ws_chunks + ((int64_t)x * H + h) * cb.bytes;
+            char* dst = ring + slot * X::kBuf;
+            dma_to_lds(src, dst, cb.shared, lane);
+            dma_to_lds(src + cb.u + grp * cb.group, dst + X::kShared, cb.group, lane);
+        };
+        if (c_begin < c_end) fetch(c_begin, 0);
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        for (int x = c_begin; x < c_end; ++x) {
+            if (x + 1 < c_end) fetch(x + 1, (x + 1 - c_begin) & 1);
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+        return;
+    }
+
+    // ---- compute waves -----------------------------------------------------------
+    const int s = grp * ncw + wave;   // value slice
+    const int col = 16 * s + cl;
     // S slice in accumulator layout: acc[t][j] = S[16t + 4g + j][col]
     f32x4 acc[NQK];
     const int64_t sbase = (int64_t)unit * DK * DV;
@@ -566,19 +664,20 @@ __global__ __launch_bounds__(64) void kda_inter_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             acc[t][j] = a.s0 ? a.s0[sbase + (int64_t)(16 * t + 4 * g + j) * DV + col] : 0.f;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    const ChunkBlock<T> cb(DK, C, DV);
+
     for (int x = c_begin; x < c_end; ++x) {
         const int jc = x - c_begin;
         const int64_t tok0 = tok_begin + (int64_t)jc * C;
         const int valid = (int)min((int64_t)C, seq_len - (int64_t)jc * C);
-        const char* blk = a.ws_chunks + ((int64_t)x * H + h) * cb.bytes;
-        const T* Wf = reinterpret_cast<const T*>(blk + cb.w);
-        const T* Qf = reinterpret_cast<const T*>(blk + cb.q);
-        const T* Kbf = reinterpret_cast<const T*>(blk + cb.kb);
-        const T* Pf = reinterpret_cast<const T*>(blk + cb.p);
-        const T* Uf = reinterpret_cast<const T*>(blk + cb.u);
-        const float* gam = reinterpret_cast<const float*>(blk + cb.gam);
+        const char* buf = ring + (jc & 1) * X::kBuf;
+        const char* Wl = buf + cb.w;
+        const char* Ql = buf + cb.q;
+        const char* Kl = buf + cb.kb;
+        const char* Pl = buf + cb.p;
+        const float* gl = reinterpret_cast<const float*>(buf + cb.gam);
+        const T* Ul = reinterpret_cast<const T*>(buf + X::kShared + wave * cb.slice);
 
         Q sb[NQK];
 #pragma unroll
@@ -589,20 +688,25 @@ __global__ __launch_bounds__(64) void kda_inter_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
             Q wq[NQK];
-#pragma unroll
-            for (int u = 0; u < NQK; ++u) wq[u] = *reinterpret_cast<const Q*>(Wf + Frag<T>::off(tb, u, lane, DK));
+            load_frag(wq, Wl, tb, lane);
             const f32x4 xw = mma_quads(wq, sb, zero4());
-            const f32x4 ut = from_quad(*reinterpret_cast<const Q*>(Uf + ((int64_t)(s * 64 + lane) * NB + tb) * 4));
+            const f32x4 ut = from_quad(*reinterpret_cast<const Q*>(Ul + (lane * NB + tb) * 4));
             ub[tb] = make_quad<T>(ut - xw);
         }
-        // O^T = S^T Qtilde^T + U^T P^T   (lane: columns 4g + j, token 16tb + cl)
+        // S <- diag(gamma_C) S + Kbar^T U
+#pragma unroll
+        for (int t = 0; t < NQK; ++t) {
+            const f32x4 gv = *reinterpret_cast<const f32x4*>(gl + 16 * t + 4 * g);
+            Q kq[NB];
+            load_frag(kq, Kl, t, lane);
+            acc[t] = mma_quads(kq, ub, acc[t] * gv);
+        }
+        // O^T = S^T Qtilde^T + U^T P^T   (lane: columns 4g + j, token 16tb + cl); S^T from sb (pre-update)
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
             Q qq[NQK], pq[NB];
-#pragma unroll
-            for (int u = 0; u < NQK; ++u) qq[u] = *reinterpret_cast<const Q*>(Qf + Frag<T>::off(tb, u, lane, DK));
-#pragma unroll
-            for (int u = 0; u < NB; ++u) pq[u] = *reinterpret_cast<const Q*>(Pf + Frag<T>::off(tb, u, lane, C));
+            load_frag(qq, Ql, tb, lane);
+            load_frag(pq, Pl, tb, lane);
             f32x4 ot = mma_quads(sb, qq, zero4());
             ot = mma_quads_upto(ub, pq, tb, ot);
             const int r = 16 * tb + cl;
@@ -613,15 +717,7 @@ __global__ __launch_bounds__(64) void kda_inter_kernel(const PrefillArgs a) {
                 else store4(reinterpret_cast<__bf16*>(a.o) + oi, sc);
             }
         }
-        // S <- diag(gamma_C) S + Kbar^T U
-#pragma unroll
-        for (int t = 0; t < NQK; ++t) {
-            const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * t + 4 * g);
-            Q kq[NB];
-#pragma unroll
-            for (int u = 0; u < NB; ++u) kq[u] = *reinterpret_cast<const Q*>(Kbf + Frag<T>::off(t, u, lane, C));
-            acc[t] = mma_quads(kq, ub, acc[t] * gv);
-        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     if (a.s_final) {
 #pragma unroll
@@ -636,7 +732,8 @@ __global__ __launch_bounds__(64) void kda_inter_kernel(const PrefillArgs a) {
 // ---------------------------------------------------------------------------
 template <int DK, int C, typename In>
 static hipError_t launch_phase_t(const PrefillArgs& a, int max_chunks, bool intra, hipStream_t stream) {
-    if constexpr (!Intra<DK, C, typename OperandOf<In>::type>::kFits) {
+    if constexpr (!Intra<DK, C, typename OperandOf<In>::type>::kFits ||
+                  !Inter<DK, C, typename OperandOf<In>::type>::kFits) {
         return hipErrorInvalidValue;  // effective_chunk() never selects this
     } else {
         if (intra) {
@@ -645,8 +742,9 @@ static hipError_t launch_phase_t(const PrefillArgs& a, int max_chunks, bool intr
             }
         } else {
             const int units = a.N * a.H;
-            const int blocks = ((units + 7) / 8) * 8 * (a.DV / 16);
-            hipLaunchKernelGGL((kda_inter_kernel<DK, C, In>), dim3(blocks), dim3(64), 0, stream, a);
+            const int ncw = slice_waves(a.DV);
+            const int blocks = ((units + 7) / 8) * 8 * (a.DV / 16 / ncw);
+            hipLaunchKernelGGL((kda_inter_kernel<DK, C, In>), dim3(blocks), dim3(64 * (ncw + 1)), 0, stream, a);
         }
         return hipGetLastError();
     }
@@ -674,7 +772,7 @@ static hipError_t launch_phase_k(const PrefillArgs& a, int DK, int C, int max_ch
 }
 
 template <typename T> static bool fits(int DK, int C) {
-#define KDA_FITS_CASE(D, CC) if (DK == D && C == CC) return Intra<D, CC, T>::kFits;
+#define KDA_FITS_CASE(D, CC) if (DK == D && C == CC) return Intra<D, CC, T>::kFits && Inter<D, CC, T>::kFits;
     KDA_FITS_CASE(16, 16) KDA_FITS_CASE(16, 32) KDA_FITS_CASE(16, 64)
     KDA_FITS_CASE(32, 16) KDA_FITS_CASE(32, 32) KDA_FITS_CASE(32, 64)
     KDA_FITS_CASE(64, 16) KDA_FITS_CASE(64, 32) KDA_FITS_CASE(64, 64)

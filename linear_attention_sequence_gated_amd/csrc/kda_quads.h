@@ -122,24 +122,61 @@ template <typename T> struct Frag {
 };
 
 // Per-(chunk, head) block that the intra-chunk kernel writes and the
-// inter-chunk kernel reads.  All offsets in bytes, all multiples of 16.
+// inter-chunk kernel reads.  Offsets in bytes; every region is a multiple of
+// 1 KiB so that one wave moves it with whole 64-lane x 16-byte transfers.
+//   [W | Qtilde | Kbar^T | P | gamma_C (padded)]  shared by all value slices
+//   [Utilde of slice group 0 | group 1 | ...]      ncw slices of 16 columns each
+constexpr int kMaxComputeWaves = 4;
+__host__ __device__ constexpr int64_t round_kib(int64_t x) { return (x + 1023) / 1024 * 1024; }
+__host__ __device__ constexpr int slice_waves(int DV) { return DV / 16 < kMaxComputeWaves ? DV / 16 : kMaxComputeWaves; }
+
 template <typename T> struct ChunkBlock {
-    int64_t w, q, kb, p, u, gam, bytes;
+    int64_t w, q, kb, p, gam, shared, u, slice, group, bytes;
+    int ncw;
     __host__ __device__ ChunkBlock(int DK, int C, int DV) {
         const int64_t s = sizeof(T);
         w = 0;                                   // W = T Ktilde      : C x DK frag
         q = w + Frag<T>::elems(C, DK) * s;       // Qtilde            : C x DK frag
         kb = q + Frag<T>::elems(C, DK) * s;      // Kbar^T            : DK x C frag
         p = kb + Frag<T>::elems(DK, C) * s;      // P (as P^T B-frag) : C x C frag
-        u = p + Frag<T>::elems(C, C) * s;        // Utilde = T V      : [DV/16][64][C/16][4]
-        gam = u + (int64_t)DV * C * s;           // gamma_C           : DK fp32
-        bytes = gam + (int64_t)DK * 4;
-        bytes = (bytes + 255) / 256 * 256;
+        gam = p + Frag<T>::elems(C, C) * s;      // gamma_C           : DK fp32
+        shared = gam + round_kib((int64_t)DK * 4);
+        ncw = slice_waves(DV);
+        slice = (int64_t)C * 16 * s;             // Utilde slice      : [64 lanes][C/16][4]
+        group = round_kib(ncw * slice);
+        u = shared;
+        bytes = shared + (int64_t)(DV / 16 / ncw) * group;
     }
+    __host__ __device__ int64_t u_slice(int sl) const { return u + (sl / ncw) * group + (sl % ncw) * slice; }
 };
 
 __device__ __forceinline__ float load_as_float(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float load_as_float(const __bf16* p, int64_t i) { return (float)p[i]; }
+
+// Eight consecutive elements (16-byte aligned) as fp32, in as few vector loads as possible.
+__device__ __forceinline__ void load8(const float* p, float (&o)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o[i] = a[i]; o[4 + i] = b[i]; }
+}
+__device__ __forceinline__ void load8(const __bf16* p, float (&o)[8]) {
+    typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (float)a[i];
+}
+// Eight consecutive values to LDS in the operand type (16- or 32-byte vector stores).
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+__device__ __forceinline__ void store8(_Float16* p, const float (&v)[8]) {
+    *reinterpret_cast<f16x8*>(p) = f16x8{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3],
+                                         (_Float16)v[4], (_Float16)v[5], (_Float16)v[6], (_Float16)v[7]};
+}
+template <typename T> __device__ __forceinline__ void store_q(T* p, const f32x4& v) {
+    *reinterpret_cast<quad_t<T>*>(p) = make_quad<T>(v);
+}
 
 // Store four fp32 values as fp32 (16 bytes) or bf16 (8 bytes, round to nearest even).
 __device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
