@@ -51,7 +51,7 @@ def load() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    path = _build.LIB
+    path = os.environ.get("KDA_LIBRARY", _build.LIB)   # another build of the same ABI
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
                           "(python -m linear_attention_sequence_gated_amd.build)")

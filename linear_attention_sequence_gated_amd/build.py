@@ -19,8 +19,8 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wall", "-Wno-unused-result"]
 
 
-def _compile(src: str, obj: str, verbose: bool) -> None:
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, obj: str, verbose: bool, extra=()) -> None:
+    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -31,19 +31,22 @@ def _compile(src: str, obj: str, verbose: bool) -> None:
         print(out, flush=True)
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
-    objs = [os.path.join(OUT_DIR, s + ".o") for s in SOURCES]
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile and link libkda.so to `out`; `defines` are extra -D flags (tuning builds)."""
+    out_dir = os.path.dirname(out)
+    os.makedirs(out_dir, exist_ok=True)
+    extra = [f"-D{d}" for d in defines]
+    objs = [os.path.join(out_dir, os.path.basename(out) + "." + s + ".o") for s in SOURCES]
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(SOURCES, objs)))
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
+        list(ex.map(lambda so: _compile(so[0], so[1], verbose, extra), zip(SOURCES, objs)))
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out + ".tmp", *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(out + ".tmp", out)
     for o in objs:
         os.remove(o)
-    return LIB
+    return out
 
 
 def is_stale() -> bool:

@@ -106,12 +106,14 @@ __device__ __forceinline__ bool locate_chunk(const PrefillArgs& a, int C, int x,
 // operand format.  The chunk is cut into 16-token blocks; with G_R the decay
 // exponent at the first token of block R and h_R half of the block's own
 // decay range (per channel), the products k_r k_i 2^{g_r - g_i} are split as
-//   row side   (r in block R)  k_r 2^{g_r - G_R + h_R}             in 2^[-h_R, h_R]
-//   diagonal   (i in block R)  k_i 2^{G_R - h_R - g_i}             in 2^[-h_R, h_R]
-//   off-diag.  (i in block I<R) k_i 2^{G_{I+1} - g_i} * 2^{G_R - G_{I+1} - h_R}   <= 1
+//   row side   (r in block R)   k_r 2^{g_r - G_R + h_R}                 in 2^[-h_R, h_R]
+//   column side (i in block I)  k_i 2^{G_I - h_I - g_i}                 in 2^[-h_I, h_I]
+//                               times 2^{G_R - G_I + h_I - h_R} <= 1 when I < R
 // which keeps every factor within 2^[-6, 6] while each block decays by less
-// than 2^-12 in every channel.  Chunks beyond that take the exact pairwise
-// path (decay products in linear space, fp32).
+// than 2^-12 in every channel.  Inside such blocks no alpha is floored, so the
+// factors are running products of alpha scaled by a few per-channel powers of
+// two.  Chunks beyond that take the exact pairwise path (decay products in
+// linear space, fp32).
 // ---------------------------------------------------------------------------
 template <int DK, int C, typename T> struct Intra {
     static constexpr int kThreads = 256;
@@ -124,26 +126,29 @@ template <int DK, int C, typename T> struct Intra {
     static constexpr int LD_CT = C + 8;    // [*][C] tiles (elements)
     static constexpr int LD_F = C + 4;     // fp32 [C][C] matrices
     static constexpr int kDvMax = 128;
-    // region 1: {Ak, Aq, Bd, Bo} -> {P, M, X} -> {P, VT}
-    static constexpr size_t kTiles = (size_t)(4 * C - 16) * LD_ROW * sizeof(T);
-    static constexpr size_t kMPX = 3ull * C * LD_F * sizeof(float);
-    static constexpr size_t kPVT = 1ull * C * LD_F * sizeof(float) + (size_t)kDvMax * LD_CT * sizeof(T);
+    static constexpr size_t a16(size_t x) { return (x + 15) / 16 * 16; }
     static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
-    static constexpr size_t kR1 = (cmax(cmax(kTiles, kMPX), kPVT) + 15) / 16 * 16;
-    static constexpr size_t kKtT = (size_t)DK * LD_CT * sizeof(T);
-    // region 3: {segment sums} -> {Y} -> {Tm}
+    // region 1, in turn: segment sums -> {Ak, Aq, Bd} -> {P, MX, Y, Tm} -> {P, VT, Tm}
+    static constexpr size_t kSeg = (size_t)NSEG * DK * 4;
+    static constexpr size_t kTile = (size_t)C * LD_ROW * sizeof(T);
+    static constexpr size_t kMat = (size_t)C * LD_F * 4;
+    static constexpr size_t oP = 0, oMX = kMat, oY = 2 * kMat;
+    static constexpr size_t oTb = a16(oY + (size_t)(NB > 1 ? NB - 1 : 1) * 256 * 4);
     static constexpr size_t kTb = (size_t)C * LD_CT * sizeof(T);
-    static constexpr size_t kSeg = (size_t)NSEG * DK * sizeof(float);
-    static constexpr size_t kY = (size_t)(NB > 1 ? NB - 1 : 1) * 256 * sizeof(float);
-    static constexpr size_t kR3 = (cmax(cmax(kTb, kSeg), kY) + 15) / 16 * 16;
-    // small: beta, block exponents G/E, pair factors, range flag
+    static constexpr size_t kVT = (size_t)kDvMax * LD_CT * sizeof(T);
+    static constexpr size_t oVT = (oTb - kMat >= kVT) ? kMat : a16(oTb + kTb);
+    static constexpr size_t kR1 = a16(cmax(cmax(kSeg, 3 * kTile), cmax(oTb + kTb, oVT + kVT)));
+    static constexpr size_t kKtT = (size_t)DK * LD_CT * sizeof(T);
+    // small: beta, block exponents at first / last token, pair factors, range flag
     static constexpr size_t kSmall = (size_t)C * 4 + 2ull * NB * DK * 4 + (size_t)(NOFF > 0 ? NOFF : 1) * DK * 4 + 16;
-    static constexpr size_t kLds = kR1 + kKtT + kR3 + kSmall;
+    static constexpr size_t kLds = kR1 + kKtT + kSmall;
     static constexpr bool kFits = kLds <= 163840;
+    static constexpr int kMinBlocks = kLds <= 81920 ? 2 : 1;
 };
 
 template <int DK, int C, typename In>
-__global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(256, (Intra<DK, C, typename OperandOf<In>::type>::kMinBlocks))
+void kda_intra_kernel(const PrefillArgs a) {
     using T = typename OperandOf<In>::type;
     using I = Intra<DK, C, T>;
     static_assert(I::kFits, "LDS budget of one gfx950 workgroup exceeded");
@@ -151,23 +156,20 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
     using Q = quad_t<T>;
     constexpr int NB = I::NB, NQK = I::NQK, LD_ROW = I::LD_ROW, LD_CT = I::LD_CT, LD_F = I::LD_F;
     __shared__ __attribute__((aligned(16))) char smem[I::kLds];
-    T* Ak = reinterpret_cast<T*>(smem);         // [C][LD_ROW]   row side, k
-    T* Aq = Ak + C * LD_ROW;                    // [C][LD_ROW]   row side, q
-    T* Bd = Aq + C * LD_ROW;                    // [C][LD_ROW]   diagonal-block column side
-    T* Bo = Bd + C * LD_ROW;                    // [C-16][LD_ROW] off-diagonal column side
-    float* Pm = reinterpret_cast<float*>(smem);
-    float* Mm = Pm + C * LD_F;
-    float* Xm = Mm + C * LD_F;
-    T* VT = reinterpret_cast<T*>(smem + (size_t)C * LD_F * sizeof(float));
-    T* KtT = reinterpret_cast<T*>(smem + I::kR1);
-    char* r3 = smem + I::kR1 + I::kKtT;
-    float* seg = reinterpret_cast<float*>(r3);
-    float* Ys = reinterpret_cast<float*>(r3);
-    T* Tb = reinterpret_cast<T*>(r3);
-    float* sbeta = reinterpret_cast<float*>(r3 + I::kR3);
+    float* seg = reinterpret_cast<float*>(smem);             // [NSEG][DK]
+    T* Ak = reinterpret_cast<T*>(smem);                       // [C][LD_ROW]  row side, k
+    T* Aq = Ak + C * LD_ROW;                                  // [C][LD_ROW]  row side, q
+    T* Bd = Aq + C * LD_ROW;                                  // [C][LD_ROW]  column side
+    float* Pm = reinterpret_cast<float*>(smem + I::oP);      // [C][LD_F]  P (lower)
+    float* MX = reinterpret_cast<float*>(smem + I::oMX);     // [C][LD_F]  M strictly lower, X^T strictly upper
+    float* Ys = reinterpret_cast<float*>(smem + I::oY);      // [NB-1][16][16] scratch
+    T* Tb = reinterpret_cast<T*>(smem + I::oTb);             // [C][LD_CT] Tm = X diag(beta)
+    T* VT = reinterpret_cast<T*>(smem + I::oVT);             // [DV][LD_CT] V^T
+    T* KtT = reinterpret_cast<T*>(smem + I::kR1);            // [DK][LD_CT] Ktilde^T
+    float* sbeta = reinterpret_cast<float*>(smem + I::kR1 + I::kKtT);
     float* Gs = sbeta + C;                      // [NB][DK] exponent at each block's first token
     float* Ge = Gs + NB * DK;                   // [NB][DK] exponent at each block's last token
-    float* sIR = Ge + NB * DK;                  // [NOFF][DK] pair factors 2^{G_R - G_{I+1} - h_R}
+    float* sIR = Ge + NB * DK;                  // [NOFF][DK] pair factors 2^{G_R - G_I + h_I - h_R}
     unsigned* srange = reinterpret_cast<unsigned*>(sIR + (I::NOFF > 0 ? I::NOFF : 1) * DK);
 
     const int tid = threadIdx.x;
@@ -189,63 +191,60 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
     T* Pf = reinterpret_cast<T*>(blk + cb.p);
     float* gam = reinterpret_cast<float*>(blk + cb.gam);
 
-    if (tid == 0) *srange = 0u;
-    if (tid < C) sbeta[tid] = tid < valid ? a.beta[(pos.tok0 + tid) * H + h] : 0.f;
-
-    // ---- phase 1: decay exponents and operand factors ------------------------
-    // thread -> 4 consecutive tokens (segment sgi, block R = sgi/4) x 8 channels
+    // ---- phase 1: every global load first ------------------------------------
+    // thread -> 4 consecutive tokens (segment sgi, block Rb = sgi/4) x 8 channels
     const bool p1 = tid < I::NSEG * I::NCG;
-    const int sgi = tid / I::NCG, cg = tid % I::NCG, Rb = sgi >> 2;
-    float kr[4][8], qr[4][8], gv[4][8];
-    {
-        float run[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) run[e] = 0.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int r = 4 * sgi + u;
-            const int64_t base = ((pos.tok0 + r) * H + h) * DK + 8 * cg;
-            float al[8];
-            if (p1 && r < valid) {
-                load8(kg + base, kr[u]);
-                load8(qg + base, qr[u]);
-                load8(a.alpha + base, al);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { kr[u][e] = 0.f; qr[u][e] = 0.f; al[e] = 1.f; }
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                run[e] += fmaxf(__builtin_amdgcn_logf(al[e]), kLog2Floor);
-                gv[u][e] = run[e];
-            }
-        }
-        if (p1) {
-            *reinterpret_cast<f32x4*>(seg + sgi * DK + 8 * cg) = f32x4{run[0], run[1], run[2], run[3]};
-            *reinterpret_cast<f32x4*>(seg + sgi * DK + 8 * cg + 4) = f32x4{run[4], run[5], run[6], run[7]};
-        }
-    }
-    // v of this thread's tokens, kept in registers until the value tile is built
+    const int sgi = tid / I::NCG, cg = tid % I::NCG, Rb = sgi >> 2, sp = sgi & 3;
     const int NCGV = DV / 8;
     const bool pv = tid < I::NSEG * NCGV;
     const int sgv = tid / NCGV, cgv = tid % NCGV;
-    float vr[4][8];
+    float kr[4][8], qr[4][8], al[4][8], vr[4][8];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int r = 4 * sgv + u;
-        if (pv && r < valid) {
-            load8(vg + ((pos.tok0 + r) * H + h) * DV + 8 * cgv, vr[u]);
+        const int r = 4 * sgi + u;
+        if (p1 && r < valid) {
+            const int64_t base = ((pos.tok0 + r) * H + h) * DK + 8 * cg;
+            load8(kg + base, kr[u]);
+            load8(qg + base, qr[u]);
+            load8(a.alpha + base, al[u]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { kr[u][e] = 0.f; qr[u][e] = 0.f; al[u][e] = 1.f; }
+        }
+        const int rv = 4 * sgv + u;
+        if (pv && rv < valid) {
+            load8(vg + ((pos.tok0 + rv) * H + h) * DV + 8 * cgv, vr[u]);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) vr[u][e] = 0.f;
         }
     }
-    __syncthreads();
-    float tot[8];
-    if (p1) {
-        float off[8];
+    if (tid < C) sbeta[tid] = tid < valid ? a.beta[(pos.tok0 + tid) * H + h] : 0.f;
+    if (tid == 0) *srange = 0u;
+
+    // segment sums of log2 alpha (floored), then the exclusive prefix per segment
+    float lg[4][8];  // inclusive running sum inside the segment
+    {
+        float run[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { off[e] = 0.f; tot[e] = 0.f; }
+        for (int e = 0; e < 8; ++e) run[e] = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                run[e] += fmaxf(__builtin_amdgcn_logf(al[u][e]), kLog2Floor);
+                lg[u][e] = run[e];
+            }
+        if (p1) {
+            *reinterpret_cast<f32x4*>(seg + sgi * DK + 8 * cg) = f32x4{run[0], run[1], run[2], run[3]};
+            *reinterpret_cast<f32x4*>(seg + sgi * DK + 8 * cg + 4) = f32x4{run[4], run[5], run[6], run[7]};
+        }
+    }
+    __syncthreads();
+    float off[8], tot[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { off[e] = 0.f; tot[e] = 0.f; }
+    if (p1) {
         for (int s = 0; s < I::NSEG; ++s) {
             const f32x4 t0 = *reinterpret_cast<const f32x4*>(seg + s * DK + 8 * cg);
             const f32x4 t1 = *reinterpret_cast<const f32x4*>(seg + s * DK + 8 * cg + 4);
@@ -256,22 +255,18 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
                 tot[e] += t[e];
             }
         }
+        if (sp == 0) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) gv[u][e] += off[e];   // inclusive exponent g_r
-        if ((sgi & 3) == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) Gs[Rb * DK + 8 * cg + e] = gv[0][e];
+            for (int e = 0; e < 8; ++e) Gs[Rb * DK + 8 * cg + e] = off[e] + lg[0][e];
         }
-        if ((sgi & 3) == 3) {
+        if (sp == 3) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Ge[Rb * DK + 8 * cg + e] = gv[3][e];
+            for (int e = 0; e < 8; ++e) Ge[Rb * DK + 8 * cg + e] = off[e] + lg[3][e];
         }
     }
     __syncthreads();
     // block ranges decide the path; pair factors for the off-diagonal tiles
-    if (p1 && (sgi & 3) == 0) {
+    if (p1 && sp == 0) {
         float mx = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) mx = fmaxf(mx, Gs[Rb * DK + 8 * cg + e] - Ge[Rb * DK + 8 * cg + e]);
@@ -283,79 +278,88 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
         while (R * (R + 1) / 2 <= p) ++R;          // off-diagonal pair p = R(R-1)/2 + Ib
         const int Ib = p - R * (R - 1) / 2;
         const float hR = 0.5f * (Gs[R * DK + c] - Ge[R * DK + c]);
-        sIR[e] = __builtin_amdgcn_exp2f(fminf(Gs[R * DK + c] - Gs[(Ib + 1) * DK + c] - hR, 0.f));
+        const float hI = 0.5f * (Gs[Ib * DK + c] - Ge[Ib * DK + c]);
+        sIR[e] = __builtin_amdgcn_exp2f(fminf(Gs[R * DK + c] - Gs[Ib * DK + c] + hI - hR, 0.f));
     }
     __syncthreads();
     const bool fast = __uint_as_float(*srange) <= kFastRange;
+
+    // ---- phase 1 (cont.): operand factors, tiles and the workspace quads ----
     if (p1) {
-        const bool last = Rb == NB - 1;
-        float G0[8], hR[8], Gn[8], link[8], gb[8];
+        float sh[8], gb[8], pre[8], tail[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int c = 8 * cg + e;
-            G0[e] = Gs[Rb * DK + c];
-            hR[e] = 0.5f * (G0[e] - Ge[Rb * DK + c]);
-            Gn[e] = last ? 0.f : Gs[(Rb + 1) * DK + c];
-            // 2^{g_C - G_{R+1}} links the off-diagonal column factor to Kbar
-            link[e] = last ? 1.f : __builtin_amdgcn_exp2f(fminf(tot[e] - Gn[e], 0.f));
-            gb[e] = __builtin_amdgcn_exp2f(fminf(G0[e] - hR[e], 0.f));
+            const float G0 = Gs[Rb * DK + c];
+            const float hR = 0.5f * (G0 - Ge[Rb * DK + c]);
+            sh[e] = __builtin_amdgcn_exp2f(fminf(hR, 30.f));          // 2^{h_R}
+            gb[e] = __builtin_amdgcn_exp2f(G0);                        // 2^{G_R}
+            pre[e] = sp == 0 ? 1.f : __builtin_amdgcn_exp2f(off[e] - G0);  // decay from the block's first token
+            tail[e] = __builtin_amdgcn_exp2f(fminf(tot[e] - (off[e] + lg[3][e]), 0.f));  // to the chunk's end
         }
-        float kbar[4][8], ktil[4][8];
+        // backward pass: Kbar = k 2^{g_C - g_r} (suffix products), straight to the workspace
+        {
+            const int ut = sgi >> 2, gq = sgi & 3;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = 8 * cg + e;
+                float kb4[4];
+                if (fast) {
+                    float sf = tail[e];
+#pragma unroll
+                    for (int u = 3; u >= 0; --u) {
+                        kb4[u] = kr[u][e] * sf;
+                        sf *= al[u][e];
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        kb4[u] = kr[u][e] * __builtin_amdgcn_exp2f(fminf(tot[e] - (off[e] + lg[u][e]), 0.f));
+                }
+                store_q<T>(Kbf + Frag<T>::off(c >> 4, ut, 16 * gq + (c & 15), C), f32x4{kb4[0], kb4[1], kb4[2], kb4[3]});
+            }
+        }
+        // forward pass: prefix products give the row / column factors and 2^{g_r}
+        float ktil[4][8];
+        float pr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pr[e] = pre[e];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int r = 4 * sgi + u;
-            float ak[8], aq[8], bd[8], bo[8];
+            float ak[8], aq[8], bd[8], qt[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float gr = gv[u][e];
-                float gam_r, kb_f;
+                float gm;
                 if (fast) {
-                    const float fa = __builtin_amdgcn_exp2f(gr - G0[e] + hR[e]);   // in 2^[-h, h]
+                    if (!(sp == 0 && u == 0)) pr[e] *= al[u][e];   // 2^{g_r - G_R}
+                    const float fa = pr[e] * sh[e];                // in 2^[-h, h]
                     const float fb = __builtin_amdgcn_rcpf(fa);
                     ak[e] = kr[u][e] * fa;
                     aq[e] = qr[u][e] * fa;
                     bd[e] = kr[u][e] * fb;
-                    gam_r = fa * gb[e];                                       // 2^{g_r}
-                    if (!last) {
-                        const float fo = __builtin_amdgcn_exp2f(fminf(Gn[e] - gr, 0.f));
-                        bo[e] = kr[u][e] * fo;
-                        kb_f = fo * link[e];                                  // 2^{g_C - g_r}
-                    } else {
-                        bo[e] = 0.f;
-                        kb_f = __builtin_amdgcn_exp2f(fminf(tot[e] - gr, 0.f));
-                    }
+                    gm = pr[e] * gb[e];                            // 2^{g_r}
                 } else {
-                    ak[e] = aq[e] = bd[e] = bo[e] = 0.f;
-                    gam_r = __builtin_amdgcn_exp2f(gr);
-                    kb_f = __builtin_amdgcn_exp2f(fminf(tot[e] - gr, 0.f));
+                    gm = __builtin_amdgcn_exp2f(off[e] + lg[u][e]);
                 }
-                ktil[u][e] = kr[u][e] * gam_r;   // Ktilde
-                qr[u][e] *= gam_r;               // Qtilde
-                kbar[u][e] = kr[u][e] * kb_f;    // Kbar
+                ktil[u][e] = kr[u][e] * gm;
+                qt[e] = qr[u][e] * gm;
             }
             if (fast) {
                 store8(Ak + r * LD_ROW + 8 * cg, ak);
                 store8(Aq + r * LD_ROW + 8 * cg, aq);
                 store8(Bd + r * LD_ROW + 8 * cg, bd);
-                if (!last) store8(Bo + r * LD_ROW + 8 * cg, bo);
             }
 #pragma unroll
             for (int hq = 0; hq < 2; ++hq) {  // Qtilde quads: token r, channel groups 2cg, 2cg+1
                 const int a4 = 2 * cg + hq, ut = a4 >> 2, gq = a4 & 3;
-                const f32x4 v4{qr[u][4 * hq], qr[u][4 * hq + 1], qr[u][4 * hq + 2], qr[u][4 * hq + 3]};
-                store_q<T>(Qf + Frag<T>::off(r >> 4, ut, 16 * gq + (r & 15), DK), v4);
+                store_q<T>(Qf + Frag<T>::off(r >> 4, ut, 16 * gq + (r & 15), DK),
+                           f32x4{qt[4 * hq], qt[4 * hq + 1], qt[4 * hq + 2], qt[4 * hq + 3]});
             }
         }
-        {   // Ktilde^T into LDS and Kbar^T quads to the workspace: channel c, tokens 4*sgi .. +3
-            const int ut = sgi >> 2, gq = sgi & 3;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int c = 8 * cg + e;
-                store_q<T>(KtT + c * LD_CT + 4 * sgi, f32x4{ktil[0][e], ktil[1][e], ktil[2][e], ktil[3][e]});
-                store_q<T>(Kbf + Frag<T>::off(c >> 4, ut, 16 * gq + (c & 15), C),
-                           f32x4{kbar[0][e], kbar[1][e], kbar[2][e], kbar[3][e]});
-            }
-        }
+        for (int e = 0; e < 8; ++e)   // Ktilde^T: channel c, tokens 4*sgi .. +3
+            store_q<T>(KtT + (8 * cg + e) * LD_CT + 4 * sgi, f32x4{ktil[0][e], ktil[1][e], ktil[2][e], ktil[3][e]});
         if (sgi == 0) {
             *reinterpret_cast<f32x4*>(gam + 8 * cg) =
                 f32x4{__builtin_amdgcn_exp2f(tot[0]), __builtin_amdgcn_exp2f(tot[1]), __builtin_amdgcn_exp2f(tot[2]),
@@ -391,12 +395,12 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
                     for (int u = 0; u < NQK; ++u)
                         aq[u] = *reinterpret_cast<const Q*>(Bd + (16 * Ib + cl) * LD_ROW + 16 * u + 4 * g);
                 } else {
-                    const float* sp = sIR + (R * (R - 1) / 2 + Ib) * DK;
+                    const float* sp4 = sIR + (R * (R - 1) / 2 + Ib) * DK;
 #pragma unroll
                     for (int u = 0; u < NQK; ++u) {
-                        const f32x4 bo = from_quad(*reinterpret_cast<const Q*>(Bo + (16 * Ib + cl) * LD_ROW + 16 * u + 4 * g));
-                        const f32x4 sf = *reinterpret_cast<const f32x4*>(sp + 16 * u + 4 * g);
-                        aq[u] = make_quad<T>(bo * sf);
+                        const f32x4 b4 = from_quad(*reinterpret_cast<const Q*>(Bd + (16 * Ib + cl) * LD_ROW + 16 * u + 4 * g));
+                        const f32x4 sf = *reinterpret_cast<const f32x4*>(sp4 + 16 * u + 4 * g);
+                        aq[u] = make_quad<T>(b4 * sf);
                     }
                 }
 #pragma unroll
@@ -408,7 +412,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
                 pres[pi] = mma_quads(aq, bq, zero4());
             }
         }
-        __syncthreads();  // the operand tiles are dead from here on; P/M/X reuse them
+        __syncthreads();  // the operand tiles are dead from here on
 #pragma unroll
         for (int pi = 0; pi < MAXP; ++pi) {
             const int p = wave + 4 * pi;
@@ -416,46 +420,48 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
                 // lane holds M'^T[i = 16Ib + 4g + j][r = 16R + cl] for j = 0..3
                 const int r = 16 * pR[pi] + cl, i0 = 16 * pI[pi] + 4 * g;
                 const float br = sbeta[r];
-                f32x4 mv, pvv;
+                if (pI[pi] < pR[pi]) {
+                    *reinterpret_cast<f32x4*>(MX + r * LD_F + i0) = br * mres[pi];
+                    *reinterpret_cast<f32x4*>(Pm + r * LD_F + i0) = pres[pi];
+                } else {   // diagonal tile: keep the strictly lower (M) / lower (P) part
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    mv[j] = (i0 + j < r) ? br * mres[pi][j] : 0.f;
-                    pvv[j] = (i0 + j <= r) ? pres[pi][j] : 0.f;
+                    for (int j = 0; j < 4; ++j) {
+                        if (i0 + j < r) MX[r * LD_F + i0 + j] = br * mres[pi][j];
+                        Pm[r * LD_F + i0 + j] = (i0 + j <= r) ? pres[pi][j] : 0.f;
+                    }
                 }
-                *reinterpret_cast<f32x4*>(Mm + r * LD_F + i0) = mv;
-                *reinterpret_cast<f32x4*>(Pm + r * LD_F + i0) = pvv;
             }
         }
     } else {
         // exact pairwise path: decay products taken in linear space
-        for (int e = tid; e < 2 * C * LD_F; e += I::kThreads) Pm[e] = 0.f;  // P and M
+        for (int e = tid; e < 2 * C * LD_F; e += I::kThreads) Pm[e] = 0.f;  // P and MX
         __syncthreads();
         constexpr int PARTS = I::kThreads / C;
         constexpr int CPP = DK / PARTS;
         const int i = tid % C, part = tid / C, c0 = part * CPP;
         if (i < valid) {
-            float ki[CPP], pr[CPP];
+            float ki[CPP], prd[CPP];
             const int64_t bi = ((pos.tok0 + i) * H + h) * DK + c0;
 #pragma unroll
-            for (int c = 0; c < CPP; ++c) { ki[c] = load_as_float(kg, bi + c); pr[c] = 1.f; }
+            for (int c = 0; c < CPP; ++c) { ki[c] = load_as_float(kg, bi + c); prd[c] = 1.f; }
             for (int r = i; r < valid; ++r) {
                 const int64_t br = ((pos.tok0 + r) * H + h) * DK + c0;
                 float m = 0.f, pp = 0.f;
 #pragma unroll
                 for (int c = 0; c < CPP; ++c) {
-                    if (r > i) pr[c] *= a.alpha[br + c];
-                    const float w = ki[c] * pr[c];
+                    if (r > i) prd[c] *= a.alpha[br + c];
+                    const float w = ki[c] * prd[c];
                     m += load_as_float(kg, br + c) * w;
                     pp += load_as_float(qg, br + c) * w;
                 }
-                if (r > i) atomicAdd(&Mm[r * LD_F + i], sbeta[r] * m);
+                if (r > i) atomicAdd(&MX[r * LD_F + i], sbeta[r] * m);
                 atomicAdd(&Pm[r * LD_F + i], pp);
             }
         }
     }
     __syncthreads();
 
-    // ---- phase 3: X = (I + M)^{-1}, blocked over 16-token blocks -------------
+    // ---- phase 3: X = (I + M)^{-1}; X^T kept in the strictly upper part of MX
     if (tid < C) {  // diagonal blocks by forward substitution, one column each
         const int R = tid >> 4, ci = tid & 15, b0 = 16 * R;
         float xv[16];
@@ -463,15 +469,20 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
         for (int r = 0; r < 16; ++r) xv[r] = (r == ci) ? 1.f : 0.f;
 #pragma unroll
         for (int r = 1; r < 16; ++r) {
-            if (r > ci) {
-                float s = 0.f;
+            const float* mrow = MX + (b0 + r) * LD_F + b0;
+            float s = 0.f;
 #pragma unroll
-                for (int j = 0; j < r; ++j) s += Mm[(b0 + r) * LD_F + b0 + j] * xv[j];
-                xv[r] = -s;
+            for (int j4 = 0; j4 < r; j4 += 4) {
+                const f32x4 m4 = *reinterpret_cast<const f32x4*>(mrow + j4);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    if (j4 + jj < r) s += m4[jj] * xv[j4 + jj];
             }
+            if (r > ci) xv[r] = -s;
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Xm[(b0 + r) * LD_F + b0 + ci] = xv[r];
+        for (int r = 1; r < 16; ++r)
+            if (r > ci) MX[(b0 + ci) * LD_F + b0 + r] = xv[r];   // X[b0+r][b0+ci], transposed
     }
     __syncthreads();
 #pragma unroll
@@ -480,28 +491,43 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
         const int nel = (NB - d) * 256;
         for (int e = tid; e < nel; e += I::kThreads) {
             const int Ib = e >> 8, R = Ib + d, rr = (e >> 4) & 15, ii = e & 15;
+            const int col = 16 * Ib + ii;           // column of X, row of X^T
+            const float* mrow = MX + (16 * R + rr) * LD_F;
+            const float* xrow = MX + col * LD_F;    // X^T row: X[.][col]
             float y = 0.f;
-            for (int J = Ib; J < R; ++J)
+            for (int J = Ib; J < R; ++J) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    y += Mm[(16 * R + rr) * LD_F + 16 * J + j] * Xm[(16 * J + j) * LD_F + 16 * Ib + ii];
-            Ys[e] = y;
+                for (int j4 = 0; j4 < 16; j4 += 4) {
+                    const f32x4 m4 = *reinterpret_cast<const f32x4*>(mrow + 16 * J + j4);
+                    const f32x4 x4 = *reinterpret_cast<const f32x4*>(xrow + 16 * J + j4);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int jrow = 16 * J + j4 + jj;   // row of X
+                        // X[jrow][col]: 1 on the diagonal, 0 above it, stored (transposed) below
+                        const float xv = jrow == col ? 1.f : (jrow > col ? x4[jj] : 0.f);
+                        y += m4[jj] * xv;
+                    }
+                }
+            }
+            Ys[(Ib << 8) + (ii << 4) + rr] = y;     // Y^T of block (R, Ib)
         }
         __syncthreads();
         for (int e = tid; e < nel; e += I::kThreads) {
             const int Ib = e >> 8, R = Ib + d, rr = (e >> 4) & 15, ii = e & 15;
-            float xs = 0.f;
+            const float* yrow = Ys + (Ib << 8) + (ii << 4);   // Y[.][ii]
+            float xs = yrow[rr];                               // X_RR[rr][rr] = 1
 #pragma unroll
             for (int j = 0; j < 16; ++j)
-                xs += Xm[(16 * R + rr) * LD_F + 16 * R + j] * Ys[(Ib << 8) + (j << 4) + ii];
-            Xm[(16 * R + rr) * LD_F + 16 * Ib + ii] = -xs;
+                if (j < rr) xs += MX[(16 * R + j) * LD_F + 16 * R + rr] * yrow[j];   // X_RR[rr][j]
+            MX[(16 * Ib + ii) * LD_F + 16 * R + rr] = -xs;     // X[16R+rr][16Ib+ii], transposed
         }
         __syncthreads();
     }
     // Tm = X diag(beta), lower triangle, in the operand type
     for (int e = tid; e < C * C; e += I::kThreads) {
         const int r = e / C, i = e % C;
-        Tb[r * LD_CT + i] = (T)(i <= r ? Xm[r * LD_F + i] * sbeta[i] : 0.f);
+        const float xv = i == r ? 1.f : (i < r ? MX[i * LD_F + r] : 0.f);
+        Tb[r * LD_CT + i] = (T)(xv * sbeta[i]);
     }
     __syncthreads();
 
@@ -554,7 +580,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const PrefillArgs a) {
 //   wave ncw          I/O: copies the next chunk's block from the workspace
 //                     into the other half of a double-buffered LDS ring with
 //                     direct-to-LDS loads, so compute waves only read LDS and
-//                     only write global memory (they never wait on a load).
+//                     only write global memory (they never wait on a load);
 // One s_barrier per chunk hands the ring over.  The slice groups of one
 // (sequence, head) are placed on one XCD (blocks are dealt round-robin over
 // the 8 XCDs) so the block is fetched from HBM once per XCD.
