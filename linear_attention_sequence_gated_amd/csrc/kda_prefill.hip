@@ -128,16 +128,18 @@ template <int DK, int C, typename T> struct Intra {
     static constexpr int kDvMax = 128;
     static constexpr size_t a16(size_t x) { return (x + 15) / 16 * 16; }
     static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
-    // region 1, in turn: segment sums -> {Ak, Aq, Bd} -> {P, MX, Y, Tm} -> {P, VT, Tm}
+    // region 1, in turn: segment sums -> {Ak, Aq, Bd} -> {P, MX, Tm, XD} -> {P, VT, Tm}
     static constexpr size_t kSeg = (size_t)NSEG * DK * 4;
     static constexpr size_t kTile = (size_t)C * LD_ROW * sizeof(T);
     static constexpr size_t kMat = (size_t)C * LD_F * 4;
-    static constexpr size_t oP = 0, oMX = kMat, oY = 2 * kMat;
-    static constexpr size_t oTb = a16(oY + (size_t)(NB > 1 ? NB - 1 : 1) * 256 * 4);
+    static constexpr size_t oP = 0, oMX = kMat, oY = 2 * kMat;   // oY: end of P and MX
     static constexpr size_t kTb = (size_t)C * LD_CT * sizeof(T);
     static constexpr size_t kVT = (size_t)kDvMax * LD_CT * sizeof(T);
-    static constexpr size_t oVT = (oTb - kMat >= kVT) ? kMat : a16(oTb + kTb);
-    static constexpr size_t kR1 = a16(cmax(cmax(kSeg, 3 * kTile), cmax(oTb + kTb, oVT + kVT)));
+    static constexpr size_t oVT = kMat;                       // over MX once X is consumed
+    static constexpr size_t oTb = a16(cmax(oY, oVT + kVT));
+    static constexpr size_t oXD = a16(oTb + kTb);            // [NB][16][16] fp32 diagonal blocks of X
+    static constexpr size_t kXD = (size_t)NB * 256 * 4;
+    static constexpr size_t kR1 = a16(cmax(cmax(kSeg, 3 * kTile), cmax(oXD + kXD, oVT + kVT)));
     static constexpr size_t kKtT = (size_t)DK * LD_CT * sizeof(T);
     // small: beta, block exponents at first / last token, pair factors, range flag
     static constexpr size_t kSmall = (size_t)C * 4 + 2ull * NB * DK * 4 + (size_t)(NOFF > 0 ? NOFF : 1) * DK * 4 + 16;
@@ -162,7 +164,7 @@ void kda_intra_kernel(const PrefillArgs a) {
     T* Bd = Aq + C * LD_ROW;                                  // [C][LD_ROW]  column side
     float* Pm = reinterpret_cast<float*>(smem + I::oP);      // [C][LD_F]  P (lower)
     float* MX = reinterpret_cast<float*>(smem + I::oMX);     // [C][LD_F]  M strictly lower, X^T strictly upper
-    float* Ys = reinterpret_cast<float*>(smem + I::oY);      // [NB-1][16][16] scratch
+    float* XD = reinterpret_cast<float*>(smem + I::oXD);     // [NB][16][16] X_RR, row-major
     T* Tb = reinterpret_cast<T*>(smem + I::oTb);             // [C][LD_CT] Tm = X diag(beta)
     T* VT = reinterpret_cast<T*>(smem + I::oVT);             // [DV][LD_CT] V^T
     T* KtT = reinterpret_cast<T*>(smem + I::kR1);            // [DK][LD_CT] Ktilde^T
@@ -173,7 +175,8 @@ void kda_intra_kernel(const PrefillArgs a) {
     unsigned* srange = reinterpret_cast<unsigned*>(sIR + (I::NOFF > 0 ? I::NOFF : 1) * DK);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, cl = lane & 15;
+    const int lane = tid & 63, g = lane >> 4, cl = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int x = blockIdx.x, h = blockIdx.y;
     ChunkPos pos;
     if (!locate_chunk(a, C, x, pos)) return;  // uniform over the workgroup
@@ -481,45 +484,41 @@ void kda_intra_kernel(const PrefillArgs a) {
             if (r > ci) xv[r] = -s;
         }
 #pragma unroll
-        for (int r = 1; r < 16; ++r)
-            if (r > ci) MX[(b0 + ci) * LD_F + b0 + r] = xv[r];   // X[b0+r][b0+ci], transposed
+        for (int r = 0; r < 16; ++r) {
+            XD[R * 256 + r * 16 + ci] = xv[r];                        // X_RR[r][ci], row-major
+            if (r > ci) MX[(b0 + ci) * LD_F + b0 + r] = xv[r];       // X[b0+r][b0+ci], transposed
+        }
     }
     __syncthreads();
-#pragma unroll
+    // Off-diagonal blocks, one block pair (R, Ib = R - d) per wave, on fp32 MFMA:
+    //   Y = sum_{J=Ib}^{R-1} M_RJ X_JIb ;  X_RIb^T = -(Y^T X_RR^T)
+    // Y's accumulator is already Y^T in operand layout (lane: row ii = cl,
+    // quad over j = 4g..4g+3), so it feeds the second product directly.
     for (int d = 1; d < NB; ++d) {
-        // Y_RI = sum_{J=I}^{R-1} M_RJ X_JI, then X_RI = -X_RR Y_RI, for R - I = d
-        const int nel = (NB - d) * 256;
-        for (int e = tid; e < nel; e += I::kThreads) {
-            const int Ib = e >> 8, R = Ib + d, rr = (e >> 4) & 15, ii = e & 15;
-            const int col = 16 * Ib + ii;           // column of X, row of X^T
-            const float* mrow = MX + (16 * R + rr) * LD_F;
-            const float* xrow = MX + col * LD_F;    // X^T row: X[.][col]
-            float y = 0.f;
+        if (wave < NB - d) {
+            const int Ib = wave, R = Ib + d;
+            const int rowX = 16 * Ib + cl;                   // row of X^T = column of X
+            f32x4 y = zero4();
             for (int J = Ib; J < R; ++J) {
-#pragma unroll
-                for (int j4 = 0; j4 < 16; j4 += 4) {
-                    const f32x4 m4 = *reinterpret_cast<const f32x4*>(mrow + 16 * J + j4);
-                    const f32x4 x4 = *reinterpret_cast<const f32x4*>(xrow + 16 * J + j4);
+                const f32x4 m4 = *reinterpret_cast<const f32x4*>(MX + (16 * R + cl) * LD_F + 16 * J + 4 * g);
+                f32x4 x4 = *reinterpret_cast<const f32x4*>(MX + rowX * LD_F + 16 * J + 4 * g);
+                if (J == Ib) {   // diagonal block: X[j][ii] is 1 at j == ii, 0 above it
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
-                        const int jrow = 16 * J + j4 + jj;   // row of X
-                        // X[jrow][col]: 1 on the diagonal, 0 above it, stored (transposed) below
-                        const float xv = jrow == col ? 1.f : (jrow > col ? x4[jj] : 0.f);
-                        y += m4[jj] * xv;
+                        const int j = 4 * g + jj;
+                        x4[jj] = j == cl ? 1.f : (j > cl ? x4[jj] : 0.f);
                     }
                 }
+                // A = M_RJ (lane row cl), B = X_JIb (lane column cl): both quads over j
+                y = mma_step(m4, x4, y);
             }
-            Ys[(Ib << 8) + (ii << 4) + rr] = y;     // Y^T of block (R, Ib)
-        }
-        __syncthreads();
-        for (int e = tid; e < nel; e += I::kThreads) {
-            const int Ib = e >> 8, R = Ib + d, rr = (e >> 4) & 15, ii = e & 15;
-            const float* yrow = Ys + (Ib << 8) + (ii << 4);   // Y[.][ii]
-            float xs = yrow[rr];                               // X_RR[rr][rr] = 1
+            // Z^T = Y^T X_RR^T: A = Y^T (lane row ii = cl; the C layout of y), B = X_RR^T (lane column rr = cl)
+            const f32x4 yt = f32x4{y[0], y[1], y[2], y[3]};
+            const f32x4 xr = *reinterpret_cast<const f32x4*>(XD + R * 256 + cl * 16 + 4 * g);  // X_RR[rr=cl][4g..]
+            const f32x4 z = mma_step(yt, xr, zero4());
+            // lane holds Z^T[ii = 4g + j][rr = cl]; X_RIb^T[ii][rr] = -Z^T[ii][rr]
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                if (j < rr) xs += MX[(16 * R + j) * LD_F + 16 * R + rr] * yrow[j];   // X_RR[rr][j]
-            MX[(16 * Ib + ii) * LD_F + 16 * R + rr] = -xs;     // X[16R+rr][16Ib+ii], transposed
+            for (int jj = 0; jj < 4; ++jj) MX[(16 * Ib + 4 * g + jj) * LD_F + 16 * R + cl] = -z[jj];
         }
         __syncthreads();
     }
@@ -577,10 +576,11 @@ void kda_intra_kernel(const PrefillArgs a) {
 // value slices of 16 columns):
 //   waves 0 .. ncw-1  compute: each holds its dk x 16 slice of S in MFMA
 //                     accumulator registers (fp32) and walks the chunks;
-//   wave ncw          I/O: copies the next chunk's block from the workspace
-//                     into the other half of a double-buffered LDS ring with
-//                     direct-to-LDS loads, so compute waves only read LDS and
-//                     only write global memory (they never wait on a load);
+//   waves ncw ..      I/O (kIoWaves of them): copy the next chunk's block from
+//                     the workspace into the other half of a double-buffered
+//                     LDS ring with direct-to-LDS loads, so compute waves only
+//                     read LDS and only write global memory (they never wait
+//                     on a load);
 // One s_barrier per chunk hands the ring over.  The slice groups of one
 // (sequence, head) are placed on one XCD (blocks are dealt round-robin over
 // the 8 XCDs) so the block is fetched from HBM once per XCD.
@@ -621,14 +621,32 @@ template <int DK, int C, typename T> struct Inter {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-// Copy `bytes` (a multiple of 1 KiB) from global to LDS, 16 bytes per lane per instruction.
-__device__ __forceinline__ void dma_to_lds(const char* src, char* dst, int64_t bytes, int lane) {
-    for (int64_t off = 0; off < bytes; off += 1024)
+#ifndef KDA_IO_WAVES
+#define KDA_IO_WAVES 4
+#endif
+// Waves per workgroup that copy chunk blocks into LDS (they split the 1 KiB units).
+constexpr int kIoWaves = KDA_IO_WAVES;
+// Value slices (16 columns each) per compute wave: the A fragments loaded from
+// LDS feed kSlicesPerWave MFMA column tiles.  A slice group of up to four
+// slices is then served by compute_waves(DV) waves.
+#ifndef KDA_SLICES_PER_WAVE
+#define KDA_SLICES_PER_WAVE 2
+#endif
+constexpr int kSlicesPerWave = KDA_SLICES_PER_WAVE;
+__host__ __device__ constexpr int compute_waves(int DV) {
+    return (slice_waves(DV) + kSlicesPerWave - 1) / kSlicesPerWave;
+}
+
+// Copy the 1 KiB units first, first + step, ... of `bytes` (a multiple of
+// 1 KiB) from global to LDS, 16 bytes per lane per instruction.
+__device__ __forceinline__ void dma_to_lds(const char* src, char* dst, int64_t bytes, int lane, int first, int step) {
+    for (int64_t off = (int64_t)first * 1024; off < bytes; off += (int64_t)step * 1024)
         __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + off + lane * 16), (lds_void_t*)(dst + off), 16, 0, 0);
 }
 
 template <int DK, int C, typename In>
-__global__ __launch_bounds__(64 * (kMaxComputeWaves + 1)) void kda_inter_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(64 * ((kMaxComputeWaves + kSlicesPerWave - 1) / kSlicesPerWave + kIoWaves))
+void kda_inter_kernel(const PrefillArgs a) {
     using T = typename OperandOf<In>::type;
     using Q = quad_t<T>;
     using X = Inter<DK, C, T>;
@@ -636,10 +654,11 @@ __global__ __launch_bounds__(64 * (kMaxComputeWaves + 1)) void kda_inter_kernel(
     constexpr int NB = C / 16, NQK = DK / 16;
     __shared__ __attribute__((aligned(1024))) char ring[2 * X::kBuf];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, cl = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, cl = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets go to M0
     const int H = a.H, DV = a.DV;
     const ChunkBlock<T> cb(DK, C, DV);
-    const int ncw = cb.ncw, ngroups = DV / 16 / ncw;
+    const int ncw = compute_waves(DV), ngroups = DV / 16 / cb.ncw;
     // blocks are dealt round-robin over the 8 XCDs: keep the slice groups of
     // one (sequence, head) on one XCD so they share its L2
     const int b = blockIdx.x, xcd = b & 7, jx = b >> 3;
@@ -662,13 +681,14 @@ __global__ __launch_bounds__(64 * (kMaxComputeWaves + 1)) void kda_inter_kernel(
         seq_len = a.T;
     }
 
-    if (wave == ncw) {
-        // ---- I/O wave ----------------------------------------------------------
+    if (wave >= ncw) {
+        // ---- I/O waves -----------------------------------------------------------
+        const int io = wave - ncw;
         auto fetch = [&](int x, int slot) {
             const char* src = a.ws_chunks + ((int64_t)x * H + h) * cb.bytes;
             char* dst = ring + slot * X::kBuf;
-            dma_to_lds(src, dst, cb.shared, lane);
-            dma_to_lds(src + cb.u + grp * cb.group, dst + X::kShared, cb.group, lane);
+            dma_to_lds(src, dst, cb.shared, lane, io, kIoWaves);
+            dma_to_lds(src + cb.u + grp * cb.group, dst + X::kShared, cb.group, lane, io, kIoWaves);
         };
         if (c_begin < c_end) fetch(c_begin, 0);
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
@@ -679,19 +699,22 @@ __global__ __launch_bounds__(64 * (kMaxComputeWaves + 1)) void kda_inter_kernel(
         return;
     }
 
-    // ---- compute waves -----------------------------------------------------------
-    const int s = grp * ncw + wave;   // value slice
-    const int col = 16 * s + cl;
-    // S slice in accumulator layout: acc[t][j] = S[16t + 4g + j][col]
-    f32x4 acc[NQK];
+    // ---- compute waves: NTW value slices (16 columns each) per wave ---------------
+    const int s0 = grp * cb.ncw + wave * kSlicesPerWave;   // first value slice of this wave
+    // slices this wave owns (a group may hold fewer than kSlicesPerWave * waves);
+    // the accumulators of a missing slice are computed on stale LDS and never stored
+    const int nsl = min(kSlicesPerWave, cb.ncw - wave * kSlicesPerWave);
+    // S slices in accumulator layout: acc[n][t][j] = S[16t + 4g + j][16 (s0 + n) + cl]
+    f32x4 acc[kSlicesPerWave][NQK];
     const int64_t sbase = (int64_t)unit * DK * DV;
 #pragma unroll
-    for (int t = 0; t < NQK; ++t)
+    for (int n = 0; n < kSlicesPerWave; ++n)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[t][j] = a.s0 ? a.s0[sbase + (int64_t)(16 * t + 4 * g + j) * DV + col] : 0.f;
+        for (int t = 0; t < NQK; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[n][t][j] = (a.s0 && n < nsl) ? a.s0[sbase + (int64_t)(16 * t + 4 * g + j) * DV + 16 * (s0 + n) + cl] : 0.f;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
 
     for (int x = c_begin; x < c_end; ++x) {
         const int jc = x - c_begin;
@@ -703,21 +726,26 @@ __global__ __launch_bounds__(64 * (kMaxComputeWaves + 1)) void kda_inter_kernel(
         const char* Kl = buf + cb.kb;
         const char* Pl = buf + cb.p;
         const float* gl = reinterpret_cast<const float*>(buf + cb.gam);
-        const T* Ul = reinterpret_cast<const T*>(buf + X::kShared + wave * cb.slice);
+        const T* Ul = reinterpret_cast<const T*>(buf + X::kShared + (s0 - grp * cb.ncw) * cb.slice);
 
-        Q sb[NQK];
+        Q sb[kSlicesPerWave][NQK];
 #pragma unroll
-        for (int t = 0; t < NQK; ++t) sb[t] = make_quad<T>(acc[t]);
+        for (int n = 0; n < kSlicesPerWave; ++n)
+#pragma unroll
+            for (int t = 0; t < NQK; ++t) sb[n][t] = make_quad<T>(acc[n][t]);
 
-        // U = Utilde - W S   (lane: tokens 16tb + 4g + j, column col)
-        Q ub[NB];
+        // U = Utilde - W S   (lane: tokens 16tb + 4g + j, column of slice n)
+        Q ub[kSlicesPerWave][NB];
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
             Q wq[NQK];
             load_frag(wq, Wl, tb, lane);
-            const f32x4 xw = mma_quads(wq, sb, zero4());
-            const f32x4 ut = from_quad(*reinterpret_cast<const Q*>(Ul + (lane * NB + tb) * 4));
-            ub[tb] = make_quad<T>(ut - xw);
+#pragma unroll
+            for (int n = 0; n < kSlicesPerWave; ++n) {
+                const f32x4 xw = mma_quads(wq, sb[n], zero4());
+                const f32x4 ut = from_quad(*reinterpret_cast<const Q*>(Ul + n * (cb.slice / sizeof(T)) + (lane * NB + tb) * 4));
+                ub[n][tb] = make_quad<T>(ut - xw);
+            }
         }
         // S <- diag(gamma_C) S + Kbar^T U
 #pragma unroll
@@ -725,7 +753,8 @@ __global__ __launch_bounds__(64 * (kMaxComputeWaves + 1)) void kda_inter_kernel(
             const f32x4 gv = *reinterpret_cast<const f32x4*>(gl + 16 * t + 4 * g);
             Q kq[NB];
             load_frag(kq, Kl, t, lane);
-            acc[t] = mma_quads(kq, ub, acc[t] * gv);
+#pragma unroll
+            for (int n = 0; n < kSlicesPerWave; ++n) acc[n][t] = mma_quads(kq, ub[n], acc[n][t] * gv);
         }
         // O^T = S^T Qtilde^T + U^T P^T   (lane: columns 4g + j, token 16tb + cl); S^T from sb (pre-update)
 #pragma unroll
@@ -733,23 +762,31 @@ __global__ __launch_bounds__(64 * (kMaxComputeWaves + 1)) void kda_inter_kernel(
             Q qq[NQK], pq[NB];
             load_frag(qq, Ql, tb, lane);
             load_frag(pq, Pl, tb, lane);
-            f32x4 ot = mma_quads(sb, qq, zero4());
-            ot = mma_quads_upto(ub, pq, tb, ot);
             const int r = 16 * tb + cl;
-            if (r < valid) {
-                const f32x4 sc = ot * a.scale;
-                const int64_t oi = ((tok0 + r) * H + h) * DV + 16 * s + 4 * g;
-                if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + oi, sc);
-                else store4(reinterpret_cast<__bf16*>(a.o) + oi, sc);
+#pragma unroll
+            for (int n = 0; n < kSlicesPerWave; ++n) {
+                // two chains summed on the VALU: with dk or C of 16 one of them is a
+                // single K=16 step, which must not accumulate onto a K=32 result
+                const f32x4 ot = mma_quads(sb[n], qq, zero4()) + mma_quads_upto(ub[n], pq, tb, zero4());
+                if (r < valid && n < nsl) {
+                    const f32x4 sc = ot * a.scale;
+                    const int64_t oi = ((tok0 + r) * H + h) * DV + 16 * (s0 + n) + 4 * g;
+                    if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + oi, sc);
+                    else store4(reinterpret_cast<__bf16*>(a.o) + oi, sc);
+                }
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     if (a.s_final) {
 #pragma unroll
-        for (int t = 0; t < NQK; ++t)
+        for (int n = 0; n < kSlicesPerWave; ++n)
+            if (n < nsl)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) a.s_final[sbase + (int64_t)(16 * t + 4 * g + j) * DV + col] = acc[t][j];
+            for (int t = 0; t < NQK; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    a.s_final[sbase + (int64_t)(16 * t + 4 * g + j) * DV + 16 * (s0 + n) + cl] = acc[n][t][j];
     }
 }
 
@@ -768,9 +805,9 @@ static hipError_t launch_phase_t(const PrefillArgs& a, int max_chunks, bool intr
             }
         } else {
             const int units = a.N * a.H;
-            const int ncw = slice_waves(a.DV);
-            const int blocks = ((units + 7) / 8) * 8 * (a.DV / 16 / ncw);
-            hipLaunchKernelGGL((kda_inter_kernel<DK, C, In>), dim3(blocks), dim3(64 * (ncw + 1)), 0, stream, a);
+            const int blocks = ((units + 7) / 8) * 8 * (a.DV / 16 / slice_waves(a.DV));
+            hipLaunchKernelGGL((kda_inter_kernel<DK, C, In>), dim3(blocks), dim3(64 * (compute_waves(a.DV) + kIoWaves)),
+                               0, stream, a);
         }
         return hipGetLastError();
     }

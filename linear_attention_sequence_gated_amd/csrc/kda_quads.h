@@ -84,12 +84,22 @@ __device__ __forceinline__ f32x4 mma_step2(const f32x4& a0, const f32x4& a1, con
     return mma_step(a1, b1, mma_step(a0, b0, c));
 }
 
+// A K=16 fp16 step never takes its accumulator from a K=32 step: when the two
+// opcodes (of different pass counts) issue back to back as one accumulation
+// chain, gfx950 returned stale rows in the short step's result.  An odd
+// trailing quad therefore accumulates from zero and is added on the VALU.
+template <typename Q>
+__device__ __forceinline__ f32x4 mma_tail(const Q& a, const Q& b, f32x4 c) {
+    if constexpr (sizeof(Q) == sizeof(f16x4)) return c + mma_step(a, b, zero4());
+    else return mma_step(a, b, c);
+}
+
 // c += sum over quads u in [0, N) of A_u * B_u, with N a compile-time count.
 template <int N, typename Q>
 __device__ __forceinline__ f32x4 mma_quads(const Q (&a)[N], const Q (&b)[N], f32x4 c) {
 #pragma unroll
     for (int u = 0; u + 1 < N; u += 2) c = mma_step2(a[u], a[u + 1], b[u], b[u + 1], c);
-    if constexpr (N % 2 == 1) c = mma_step(a[N - 1], b[N - 1], c);
+    if constexpr (N % 2 == 1) c = mma_tail(a[N - 1], b[N - 1], c);
     return c;
 }
 
@@ -101,7 +111,7 @@ __device__ __forceinline__ f32x4 mma_quads_upto(const Q (&a)[N], const Q (&b)[N]
     for (int u = 0; u + 1 < N; u += 2)
         if (u <= last) c = mma_step2(a[u], a[u + 1], b[u], b[u + 1], c);
     if constexpr (N % 2 == 1) {
-        if (N - 1 <= last) c = mma_step(a[N - 1], b[N - 1], c);
+        if (N - 1 <= last) c = mma_tail(a[N - 1], b[N - 1], c);
     }
     return c;
 }

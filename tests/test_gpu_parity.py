@@ -158,6 +158,12 @@ SHAPES = [
     (1, 1, 1, 128, 16, 64, torch.bfloat16, True),
     (2, 130, 2, 128, 64, 16, torch.float32, True),
     (1, 257, 2, 128, 128, 32, torch.bfloat16, True),
+    # fp16 matrix-core tiles whose dk or C is 16 end in a single K=16 step next
+    # to K=32 steps; dv >= 32 gives each compute wave two value slices
+    (2, 70, 2, 32, 128, 16, torch.bfloat16, True),
+    (1, 80, 2, 64, 128, 16, torch.bfloat16, True),
+    (1, 90, 2, 16, 64, 32, torch.bfloat16, True),
+    (1, 150, 1, 16, 32, 64, torch.bfloat16, False),
 ]
 
 
