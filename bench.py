@@ -39,13 +39,49 @@ def algorithmic(dk, dv, chunk, qkv_bytes=2, o_bytes=2):
     return {
         # intra-chunk kernel: reads every input once
         "intra_bytes_per_token_head": in_bytes,
-        # inter-chunk kernel: W S, Qtilde S, Kbar^T U (2 dk dv flops each) and the causal P U
-        "inter_flops_per_token_head": 6 * dk * dv + dv * (chunk + 1),
+        # inter-chunk kernel: W S, Qtilde S, Kbar^T U (2 dk dv flops each) and the causal
+        # P U (triangle counted at half: C dv)
+        "inter_flops_per_token_head": 6 * dk * dv + chunk * dv,
         "prefill_bytes_per_token_head": in_bytes + dv * o_bytes,
         "state_bytes_per_seq_head": dk * dv * 4,
         # decode: state read + written once, plus the token's q, k, v, alpha, beta and o
         "decode_bytes_per_head_step": 2 * dk * dv * 4 + in_bytes + dv * o_bytes,
     }
+
+
+# HBM bytes per launch of each kernel on the workloads above, from two rocprofv3
+# counter passes over this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+# each scaled by what the same counter reads for a calibration dispatch that
+# reads and writes 1 GiB (--copy-calibration): FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.
+# A figure is reported only while the kernel sources hash to the value it was
+# measured on; after any change it is null until the counters are taken again.
+KERNEL_SOURCES = {
+    "prefill": ["kda_prefill.hip", "kda_quads.h", "kda_kernels.h"],
+    "decode": ["kda_decode.hip", "kda_quads.h", "kda_kernels.h"],
+}
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+TRAFFIC = {  # kernel: (sources, sha256[:16] of the sources, FETCH_SIZE KiB, WRITE_SIZE KiB)
+    "kda_intra_kernel": ("prefill", "09fffe1b917f05db", 1442030.0, 2416762.0),
+    "kda_inter_kernel": ("prefill", "09fffe1b917f05db", 1196106.0, 526336.0),
+    "kda_decode_kernel": ("decode", "1ee5a50a45e7a2e3", 267561.0, 526336.0),
+}
+
+
+def source_sha(which):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[which]:
+        with open(os.path.join(ROOT, "linear_attention_sequence_gated_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic(kernel):
+    """Measured HBM bytes per launch, or None if the kernel changed since."""
+    which, sha, fetch_kib, write_kib = TRAFFIC[kernel]
+    if source_sha(which) != sha:
+        return None
+    return int((fetch_kib * FETCH_SCALE + write_kib * WRITE_SCALE) * 1024)
 
 
 def roof(bound, amount, seconds, unit, kernel, traffic=None):
@@ -143,11 +179,13 @@ def main():
     th = tokens * w.heads
     alg = algorithmic(w.dk, w.dv, w.chunk)
     intra_roof = roof("hbm", th * alg["intra_bytes_per_token_head"], intra_ms / 1e3, "GB/s",
-                      "kda_intra_kernel")
+                      "kda_intra_kernel", traffic("kda_intra_kernel"))
     inter_roof = roof("mfma", th * alg["inter_flops_per_token_head"], inter_ms / 1e3, "TFLOP/s",
-                      "kda_inter_kernel")
+                      "kda_inter_kernel", traffic("kda_inter_kernel"))
     step_bytes = th * alg["prefill_bytes_per_token_head"] + w.batch * w.heads * alg["state_bytes_per_seq_head"]
-    step_roof = roof("hbm", step_bytes, step_ms / 1e3, "GB/s", "kda_chunk_fwd (whole step)")
+    t_in, t_out = traffic("kda_intra_kernel"), traffic("kda_inter_kernel")
+    step_roof = roof("hbm", step_bytes, step_ms / 1e3, "GB/s", "kda_chunk_fwd (whole step)",
+                     t_in + t_out if t_in is not None and t_out is not None else None)
     del pre, d
     torch.cuda.empty_cache()
 
@@ -178,7 +216,8 @@ def main():
     units = wd.decode_seqs * wd.heads
     dec_bytes = units * alg["decode_bytes_per_head_step"]
     state_bytes = units * 2 * wd.dk * wd.dv * 4
-    dec_roof = roof("hbm", dec_bytes, dec_ms / 1e3, "GB/s", "kda_decode_kernel")
+    dec_roof = roof("hbm", dec_bytes, dec_ms / 1e3, "GB/s", "kda_decode_kernel",
+                    traffic("kda_decode_kernel"))
     decode = {
         "workload": f"decode {wd.decode_seqs} seqs x H{wd.heads} dk=dv={wd.dk}, "
                     f"{args.decode_steps} in-place steps (bf16 q/k/v/o, fp32 alpha/beta/state)",
@@ -190,12 +229,24 @@ def main():
     del dd, state
     torch.cuda.empty_cache()
 
+    calib = None
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # one elementwise kernel that reads 1 GiB and writes 1 GiB: the reference
+        # dispatch for scaling FETCH_SIZE / WRITE_SIZE, and the practical
+        # read+write bandwidth of this GPU
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(4):
-            dst.copy_(src)
+        torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
+        ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ce[0].record(stream)
+        for _ in range(4):
+            torch.mul(src, 2.0, out=dst)
+        ce[1].record(stream)
+        torch.cuda.synchronize()
+        cms = ce[0].elapsed_time(ce[1]) / 4
+        calib = {"kernel": "torch.mul fp32, 1 GiB in + 1 GiB out", "ms": round(cms, 4),
+                 "GB/s": round(2 * (1 << 30) / (cms / 1e3) / 1e9, 1)}
         del src, dst
 
     # ---- CPU baseline (oracle) ------------------------------------------------
@@ -231,6 +282,7 @@ def main():
         "kernels": kernels,
         "decode": decode,
         "cpu_baseline": cpu,
+        "copy_calibration": calib,
         "wall_s_timed_region": round(wall, 4),
     }
     print(json.dumps(out), flush=True)

@@ -613,7 +613,7 @@ __device__ __forceinline__ void load_frag(f32x4 (&q)[N], const char* base, int r
 template <int DK, int C, typename T> struct Inter {
     static constexpr int64_t kShared = (2 * Frag<T>::elems(C, DK) + Frag<T>::elems(DK, C) + Frag<T>::elems(C, C)) *
                                            (int64_t)sizeof(T) + round_kib(DK * 4);
-    static constexpr int64_t kGroupMax = round_kib((int64_t)kMaxComputeWaves * C * 16 * sizeof(T));
+    static constexpr int64_t kGroupMax = round_kib((int64_t)kGroupSlices * C * 16 * sizeof(T));
     static constexpr int64_t kBuf = kShared + kGroupMax;
     static constexpr bool kFits = 2 * kBuf <= 163840;
 };
@@ -630,11 +630,11 @@ constexpr int kIoWaves = KDA_IO_WAVES;
 // LDS feed kSlicesPerWave MFMA column tiles.  A slice group of up to four
 // slices is then served by compute_waves(DV) waves.
 #ifndef KDA_SLICES_PER_WAVE
-#define KDA_SLICES_PER_WAVE 2
+#define KDA_SLICES_PER_WAVE 1
 #endif
 constexpr int kSlicesPerWave = KDA_SLICES_PER_WAVE;
 __host__ __device__ constexpr int compute_waves(int DV) {
-    return (slice_waves(DV) + kSlicesPerWave - 1) / kSlicesPerWave;
+    return (group_slices(DV) + kSlicesPerWave - 1) / kSlicesPerWave;
 }
 
 // Copy the 1 KiB units first, first + step, ... of `bytes` (a multiple of
@@ -645,7 +645,7 @@ __device__ __forceinline__ void dma_to_lds(const char* src, char* dst, int64_t b
 }
 
 template <int DK, int C, typename In>
-__global__ __launch_bounds__(64 * ((kMaxComputeWaves + kSlicesPerWave - 1) / kSlicesPerWave + kIoWaves))
+__global__ __launch_bounds__(64 * ((kGroupSlices + kSlicesPerWave - 1) / kSlicesPerWave + kIoWaves))
 void kda_inter_kernel(const PrefillArgs a) {
     using T = typename OperandOf<In>::type;
     using Q = quad_t<T>;
@@ -658,7 +658,7 @@ void kda_inter_kernel(const PrefillArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets go to M0
     const int H = a.H, DV = a.DV;
     const ChunkBlock<T> cb(DK, C, DV);
-    const int ncw = compute_waves(DV), ngroups = DV / 16 / cb.ncw;
+    const int ncw = compute_waves(DV), ngroups = DV / 16 / cb.gsl;
     // blocks are dealt round-robin over the 8 XCDs: keep the slice groups of
     // one (sequence, head) on one XCD so they share its L2
     const int b = blockIdx.x, xcd = b & 7, jx = b >> 3;
@@ -700,10 +700,10 @@ void kda_inter_kernel(const PrefillArgs a) {
     }
 
     // ---- compute waves: NTW value slices (16 columns each) per wave ---------------
-    const int s0 = grp * cb.ncw + wave * kSlicesPerWave;   // first value slice of this wave
+    const int s0 = grp * cb.gsl + wave * kSlicesPerWave;   // first value slice of this wave
     // slices this wave owns (a group may hold fewer than kSlicesPerWave * waves);
     // the accumulators of a missing slice are computed on stale LDS and never stored
-    const int nsl = min(kSlicesPerWave, cb.ncw - wave * kSlicesPerWave);
+    const int nsl = min(kSlicesPerWave, cb.gsl - wave * kSlicesPerWave);
     // S slices in accumulator layout: acc[n][t][j] = S[16t + 4g + j][16 (s0 + n) + cl]
     f32x4 acc[kSlicesPerWave][NQK];
     const int64_t sbase = (int64_t)unit * DK * DV;
@@ -726,7 +726,7 @@ void kda_inter_kernel(const PrefillArgs a) {
         const char* Kl = buf + cb.kb;
         const char* Pl = buf + cb.p;
         const float* gl = reinterpret_cast<const float*>(buf + cb.gam);
-        const T* Ul = reinterpret_cast<const T*>(buf + X::kShared + (s0 - grp * cb.ncw) * cb.slice);
+        const T* Ul = reinterpret_cast<const T*>(buf + X::kShared + (s0 - grp * cb.gsl) * cb.slice);
 
         Q sb[kSlicesPerWave][NQK];
 #pragma unroll
@@ -805,7 +805,7 @@ static hipError_t launch_phase_t(const PrefillArgs& a, int max_chunks, bool intr
             }
         } else {
             const int units = a.N * a.H;
-            const int blocks = ((units + 7) / 8) * 8 * (a.DV / 16 / slice_waves(a.DV));
+            const int blocks = ((units + 7) / 8) * 8 * (a.DV / 16 / group_slices(a.DV));
             hipLaunchKernelGGL((kda_inter_kernel<DK, C, In>), dim3(blocks), dim3(64 * (compute_waves(a.DV) + kIoWaves)),
                                0, stream, a);
         }

@@ -135,14 +135,24 @@ template <typename T> struct Frag {
 // inter-chunk kernel reads.  Offsets in bytes; every region is a multiple of
 // 1 KiB so that one wave moves it with whole 64-lane x 16-byte transfers.
 //   [W | Qtilde | Kbar^T | P | gamma_C (padded)]  shared by all value slices
-//   [Utilde of slice group 0 | group 1 | ...]      ncw slices of 16 columns each
-constexpr int kMaxComputeWaves = 4;
+//   [Utilde of slice group 0 | group 1 | ...]      gsl slices of 16 columns each
+// A slice group is what one inter-chunk workgroup owns: it copies the shared
+// region and its group's Utilde slices into LDS for every chunk.  The chunk
+// chain of a (sequence, head) is serial, so one slice per workgroup spreads a
+// few long sequences over every CU (32 heads x 8 slices fill 256 CUs); the
+// price is that each slice's workgroup reads the shared region from L2 itself.
+#ifndef KDA_GROUP_SLICES
+#define KDA_GROUP_SLICES 1
+#endif
+constexpr int kGroupSlices = KDA_GROUP_SLICES;
+static_assert(kGroupSlices == 1 || kGroupSlices == 2 || kGroupSlices == 4 || kGroupSlices == 8,
+              "slice groups must divide every supported dv / 16");
 __host__ __device__ constexpr int64_t round_kib(int64_t x) { return (x + 1023) / 1024 * 1024; }
-__host__ __device__ constexpr int slice_waves(int DV) { return DV / 16 < kMaxComputeWaves ? DV / 16 : kMaxComputeWaves; }
+__host__ __device__ constexpr int group_slices(int DV) { return DV / 16 < kGroupSlices ? DV / 16 : kGroupSlices; }
 
 template <typename T> struct ChunkBlock {
     int64_t w, q, kb, p, gam, shared, u, slice, group, bytes;
-    int ncw;
+    int gsl;
     __host__ __device__ ChunkBlock(int DK, int C, int DV) {
         const int64_t s = sizeof(T);
         w = 0;                                   // W = T Ktilde      : C x DK frag
@@ -151,13 +161,13 @@ template <typename T> struct ChunkBlock {
         p = kb + Frag<T>::elems(DK, C) * s;      // P (as P^T B-frag) : C x C frag
         gam = p + Frag<T>::elems(C, C) * s;      // gamma_C           : DK fp32
         shared = gam + round_kib((int64_t)DK * 4);
-        ncw = slice_waves(DV);
+        gsl = group_slices(DV);
         slice = (int64_t)C * 16 * s;             // Utilde slice      : [64 lanes][C/16][4]
-        group = round_kib(ncw * slice);
+        group = round_kib(gsl * slice);
         u = shared;
-        bytes = shared + (int64_t)(DV / 16 / ncw) * group;
+        bytes = shared + (int64_t)(DV / 16 / gsl) * group;
     }
-    __host__ __device__ int64_t u_slice(int sl) const { return u + (sl / ncw) * group + (sl % ncw) * slice; }
+    __host__ __device__ int64_t u_slice(int sl) const { return u + (sl / gsl) * group + (sl % gsl) * slice; }
 };
 
 __device__ __forceinline__ float load_as_float(const float* p, int64_t i) { return p[i]; }
