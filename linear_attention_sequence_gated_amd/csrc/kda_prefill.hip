@@ -37,6 +37,9 @@ constexpr float kLog2Floor = -40.f;
 // Largest decay (log2 units) a 16-token block may show in any channel for the
 // factored Gram path; see the intra-chunk kernel.
 constexpr float kFastRange = 12.f;
+#ifndef KDA_LATE_V
+#define KDA_LATE_V 1
+#endif
 
 // ---------------------------------------------------------------------------
 // K0: exclusive prefix of ceil(len_n / C) over the packed sequences.
@@ -214,14 +217,22 @@ void kda_intra_kernel(const PrefillArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) { kr[u][e] = 0.f; qr[u][e] = 0.f; al[u][e] = 1.f; }
         }
-        const int rv = 4 * sgv + u;
-        if (pv && rv < valid) {
-            load8(vg + ((pos.tok0 + rv) * H + h) * DV + 8 * cgv, vr[u]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vr[u][e] = 0.f;
-        }
     }
+    // v is needed only once the solve is done: its loads go out after the Gram
+    // phase (KDA_LATE_V) so that they do not queue behind the factor inputs
+    auto load_v = [&]() {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int rv = 4 * sgv + u;
+            if (pv && rv < valid) {
+                load8(vg + ((pos.tok0 + rv) * H + h) * DV + 8 * cgv, vr[u]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vr[u][e] = 0.f;
+            }
+        }
+    };
+    if (!KDA_LATE_V) load_v();
     if (tid < C) sbeta[tid] = tid < valid ? a.beta[(pos.tok0 + tid) * H + h] : 0.f;
     if (tid == 0) *srange = 0u;
 
@@ -248,6 +259,7 @@ void kda_intra_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) { off[e] = 0.f; tot[e] = 0.f; }
     if (p1) {
+#pragma unroll
         for (int s = 0; s < I::NSEG; ++s) {
             const f32x4 t0 = *reinterpret_cast<const f32x4*>(seg + s * DK + 8 * cg);
             const f32x4 t1 = *reinterpret_cast<const f32x4*>(seg + s * DK + 8 * cg + 4);
@@ -464,6 +476,8 @@ void kda_intra_kernel(const PrefillArgs a) {
     }
     __syncthreads();
 
+    if (KDA_LATE_V) load_v();
+
     // ---- phase 3: X = (I + M)^{-1}; X^T kept in the strictly upper part of MX
     if (tid < C) {  // diagonal blocks by forward substitution, one column each
         const int R = tid >> 4, ci = tid & 15, b0 = 16 * R;
@@ -522,11 +536,18 @@ void kda_intra_kernel(const PrefillArgs a) {
         }
         __syncthreads();
     }
-    // Tm = X diag(beta), lower triangle, in the operand type
-    for (int e = tid; e < C * C; e += I::kThreads) {
-        const int r = e / C, i = e % C;
-        const float xv = i == r ? 1.f : (i < r ? MX[i * LD_F + r] : 0.f);
-        Tb[r * LD_CT + i] = (T)(xv * sbeta[i]);
+    // Tm = X diag(beta), lower triangle, in the operand type; lanes run over
+    // rows r so that reading X^T (stored in MX's upper part) is conflict-free
+    for (int e = tid; e < C * C / 4; e += I::kThreads) {
+        const int r = e % C, i0 = 4 * (e / C);
+        float t4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = i0 + j;
+            const float xv = i == r ? 1.f : (i < r ? MX[i * LD_F + r] : 0.f);
+            t4[j] = xv * sbeta[i];
+        }
+        store_q<T>(Tb + r * LD_CT + i0, f32x4{t4[0], t4[1], t4[2], t4[3]});
     }
     __syncthreads();
 
