@@ -141,6 +141,55 @@ kda_status_t kda_chunk_fwd_inter(const kda_chunk_params_t* params,
                                  void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* Options of kda_chunk_fwd_ex.  A zero-filled struct is exactly kda_chunk_fwd.
+ * Fields that are set but not built in this library return
+ * KDA_ERR_UNSUPPORTED before anything is launched. */
+typedef struct {
+    /* State checkpoints at prefix boundaries.  The serving side keeps the
+     * fixed-size recurrent state at selected prefix boundaries so that a
+     * repeated prompt resumes prefill there ("Kimi K3 architecture: KDA, MLA
+     * and MoE", section "Serving K3 means managing two cache lifecycles";
+     * "Kimi K3 Architecture Teardown", section "Scale: Total vs Active
+     * Parameters and Serving Economics").  When ckpt_every > 0, checkpoint j
+     * of sequence n is the state after the first (j + 1) * ckpt_every tokens
+     * of that sequence, written to checkpoints [N, max_ckpts, H, dk, dv] fp32
+     * (16-byte aligned, not overlapping the states) for every j < max_ckpts
+     * with (j + 1) * ckpt_every <= the length of sequence n; other slots are
+     * left untouched.  ckpt_every must be a multiple of 64 and max_ckpts >= 1.
+     * Fed back as initial_state, checkpoint j resumes the sequence at token
+     * (j + 1) * ckpt_every. */
+    float* checkpoints;
+    int64_t ckpt_every;
+    int32_t max_ckpts;
+    /* Floored decay: alpha values below decay_floor are raised to it (0: no
+     * floor).  Not built yet. */
+    float decay_floor;
+    /* 0: alpha is per key channel [B, T, H, dk]; 1: one decay per token and
+     * head, alpha [B, T, H] (scalar gate).  Not built yet. */
+    int32_t alpha_mode;
+    /* 1: q and k are L2-normalised per (token, head) and alpha, beta are
+     * logits passed through a sigmoid, inside the kernels.  Not built yet. */
+    int32_t fuse_inputs;
+    /* Output gate: NULL, or gate logits [B, T, H, dv] (qkv dtype); then
+     * o = rmsnorm(o) * norm_weight * sigmoid(gate), the norm over dv with
+     * norm_eps, norm_weight [dv] fp32 or NULL for ones.  Not built yet. */
+    const void* gate;
+    const float* norm_weight;
+    float norm_eps;
+} kda_chunk_options_t;
+
+/* kda_chunk_fwd with the options above (NULL options = kda_chunk_fwd).  The
+ * workspace is the one kda_chunk_fwd_workspace_size quotes.  Errors as
+ * kda_chunk_fwd, plus KDA_ERR_INVALID_ARG for bad option values and
+ * KDA_ERR_UNSUPPORTED for options not built. */
+kda_status_t kda_chunk_fwd_ex(const kda_chunk_params_t* params, const kda_chunk_options_t* options,
+                              const void* q, const void* k, const void* v,
+                              const float* alpha, const float* beta,
+                              const float* initial_state, const int32_t* cu_seqlens,
+                              void* o, float* final_state,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* One decode step: every (sequence, head) consumes a single token and its
  * state is updated in place.
  *   q, k   [N, H, dk]  D        v  [N, H, dv]  D      o  [N, H, dv]  o_dtype

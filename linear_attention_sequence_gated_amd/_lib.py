@@ -23,7 +23,7 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "
 
 # Every symbol include/kda.h declares.
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
-            "kda_chunk_fwd_inter", "kda_decode_step")
+            "kda_chunk_fwd_inter", "kda_chunk_fwd_ex", "kda_decode_step")
 
 
 class KdaError(RuntimeError):
@@ -37,6 +37,13 @@ class ChunkParams(ctypes.Structure):
                 ("num_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32),
                 ("head_dim_v", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("qkv_dtype", ctypes.c_int32), ("o_dtype", ctypes.c_int32)]
+
+
+class ChunkOptions(ctypes.Structure):
+    """kda_chunk_options_t (include/kda.h); zero-filled = the plain operation."""
+    _fields_ = [("checkpoints", ctypes.c_void_p), ("ckpt_every", ctypes.c_int64), ("max_ckpts", ctypes.c_int32),
+                ("decay_floor", ctypes.c_float), ("alpha_mode", ctypes.c_int32), ("fuse_inputs", ctypes.c_int32),
+                ("gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float)]
 
 
 _lib = None
@@ -65,6 +72,9 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [ctypes.POINTER(ChunkParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kda_chunk_fwd_ex.restype = ctypes.c_int
+    lib.kda_chunk_fwd_ex.argtypes = [ctypes.POINTER(ChunkParams), ctypes.POINTER(ChunkOptions),
+                                     vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     _lib = lib
@@ -130,7 +140,8 @@ class Prefill:
 
     def __init__(self, q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_size: int = 64,
                  scale: float = 1.0, output_final_state: bool = True, o=None, final_state=None,
-                 workspace=None, stream=None, o_dtype: Optional[torch.dtype] = None):
+                 workspace=None, stream=None, o_dtype: Optional[torch.dtype] = None,
+                 checkpoints=None, ckpt_every: int = 0):
         B, T, H, dk = q.shape
         dv = v.shape[-1]
         _need(k.shape == q.shape and alpha.shape == q.shape, "q, k and alpha must share [B,T,H,dk]")
@@ -156,14 +167,27 @@ class Prefill:
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         self.o, self.final_state, self.workspace = o, final_state, workspace
-        self._keep = (q, k, v, alpha, beta, initial_state, cu_seqlens)
+        self.options = None
+        self.checkpoints = checkpoints
+        if ckpt_every:
+            _need(checkpoints is not None and checkpoints.dim() == 5 and checkpoints.shape[0] == n
+                  and checkpoints.shape[2:] == (H, dk, dv) and checkpoints.dtype == torch.float32
+                  and checkpoints.is_cuda and checkpoints.is_contiguous(),
+                  "checkpoints must be fp32 [N, max_ckpts, H, dk, dv]")
+            self.options = ChunkOptions(checkpoints=checkpoints.data_ptr(), ckpt_every=int(ckpt_every),
+                                        max_ckpts=checkpoints.shape[1])
+        self._keep = (q, k, v, alpha, beta, initial_state, cu_seqlens, checkpoints)
         self._args = (ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                       _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(final_state), _ptr(workspace),
                       ctypes.c_size_t(workspace.numel()), _stream(stream))
         self._lib = load()
 
     def run(self):
-        _check("kda_chunk_fwd", self._lib.kda_chunk_fwd(*self._args))
+        if self.options is not None:
+            _check("kda_chunk_fwd_ex", self._lib.kda_chunk_fwd_ex(self._args[0], ctypes.byref(self.options),
+                                                                  *self._args[1:]))
+        else:
+            _check("kda_chunk_fwd", self._lib.kda_chunk_fwd(*self._args))
         return self.o, self.final_state
 
     def intra(self):
@@ -176,16 +200,20 @@ class Prefill:
 
 def chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_size: int = 64,
               scale: float = 1.0, output_final_state: bool = True, o=None, final_state=None,
-              workspace=None, stream=None, o_dtype: Optional[torch.dtype] = None):
+              workspace=None, stream=None, o_dtype: Optional[torch.dtype] = None,
+              checkpoints=None, ckpt_every: int = 0):
     """Chunked KDA prefill through kda_chunk_fwd.  Returns (o, final_state or None).
 
     q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32, same dtype), alpha [B,T,H,dk] fp32,
     beta [B,T,H] fp32, initial_state [N,H,dk,dv] fp32 or None, cu_seqlens int32 [N+1] or
     None (device tensors).  ``final_state`` may be ``initial_state`` (in-place resume).
-    ``o_dtype`` (default: the dtype of q) is bf16 or fp32.
+    ``o_dtype`` (default: the dtype of q) is bf16 or fp32.  With ``ckpt_every`` (a
+    multiple of 64) the call goes through kda_chunk_fwd_ex and writes the state after
+    every ``ckpt_every`` tokens of each sequence into ``checkpoints`` [N,max_ckpts,H,dk,dv].
     """
     return Prefill(q, k, v, alpha, beta, initial_state, cu_seqlens, chunk_size, scale,
-                   output_final_state, o, final_state, workspace, stream, o_dtype).run()
+                   output_final_state, o, final_state, workspace, stream, o_dtype,
+                   checkpoints, ckpt_every).run()
 
 
 def decode_step(q, k, v, alpha, beta, state, scale: float = 1.0, o=None, stream=None,

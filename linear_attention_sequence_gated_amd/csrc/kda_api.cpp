@@ -88,12 +88,42 @@ namespace {
 
 enum Phase { kBoth = 3, kIntra = 1, kInter = 2 };
 
-kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const void* q, const void* k, const void* v,
-                            const float* alpha, const float* beta, const float* initial_state,
-                            const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
-                            size_t workspace_bytes, void* stream, int phases) {
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const char* x = reinterpret_cast<const char*>(a);
+    const char* y = reinterpret_cast<const char*>(b);
+    return a && b && x < y + nb && y < x + na;
+}
+
+// Options: everything zero is the plain operation; only the fields that are
+// built are accepted.
+kda_status_t check_options(const kda_chunk_params_t* p, const kda_chunk_options_t* op,
+                           const float* initial_state, const float* final_state) {
+    if (!op) return KDA_OK;
+    if (op->decay_floor != 0.f || op->alpha_mode != 0 || op->fuse_inputs != 0 || op->gate || op->norm_weight)
+        return KDA_ERR_UNSUPPORTED;
+    if (op->ckpt_every < 0) return KDA_ERR_INVALID_ARG;
+    if (op->ckpt_every > 0) {
+        if (op->ckpt_every % 64 != 0 || op->max_ckpts < 1 || !op->checkpoints || !aligned(op->checkpoints, 16))
+            return KDA_ERR_INVALID_ARG;
+        const size_t state = (size_t)p->num_heads * p->head_dim_k * p->head_dim_v * sizeof(float);
+        const size_t cb = (size_t)p->num_seqs * (size_t)op->max_ckpts * state;
+        if (cb / state / (size_t)p->num_seqs != (size_t)op->max_ckpts) return KDA_ERR_INVALID_ARG;
+        const size_t sb = (size_t)p->num_seqs * state;
+        if (overlaps(op->checkpoints, cb, initial_state, sb) || overlaps(op->checkpoints, cb, final_state, sb))
+            return KDA_ERR_INVALID_ARG;
+    }
+    return KDA_OK;
+}
+
+kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options_t* op, const void* q,
+                            const void* k, const void* v, const float* alpha, const float* beta,
+                            const float* initial_state, const int32_t* cu_seqlens, void* o, float* final_state,
+                            void* workspace, size_t workspace_bytes, void* stream, int phases) {
     kda_status_t st = check_params(p);
     if (st != KDA_OK) return st;
+    st = check_options(p, op, initial_state, final_state);
+    if (st != KDA_OK) return st;
+    const bool ckpt = op && op->ckpt_every > 0;
     const bool packed = cu_seqlens != nullptr;
     if (packed && p->batch != 1) return KDA_ERR_INVALID_ARG;
     if (!packed && p->num_seqs != p->batch) return KDA_ERR_INVALID_ARG;
@@ -110,16 +140,14 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const void* q, const vo
     if (initial_state && final_state && initial_state != final_state) {
         // partial overlap would race between slices; exact aliasing is fine
         const size_t sb = (size_t)p->num_seqs * p->num_heads * p->head_dim_k * p->head_dim_v * sizeof(float);
-        const char* a0 = reinterpret_cast<const char*>(initial_state);
-        const char* b0 = reinterpret_cast<const char*>(final_state);
-        if (a0 < b0 + sb && b0 < a0 + sb) return KDA_ERR_INVALID_ARG;
+        if (overlaps(initial_state, sb, final_state, sb)) return KDA_ERR_INVALID_ARG;
     }
     const PrefillPlan pl = plan_prefill(p, packed);
     if (pl.total > 0) {
         if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_WORKSPACE;
         if (workspace_bytes < pl.total) return KDA_ERR_WORKSPACE;
     }
-    if (!final_state && !has_tokens) return KDA_OK;  // nothing to compute or write
+    if (!final_state && !has_tokens) return KDA_OK;  // nothing to compute or write (no checkpoint is reached)
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* ws = reinterpret_cast<char*>(workspace);
@@ -143,6 +171,9 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const void* q, const vo
     a.chunks_per_seq = (int32_t)((p->seqlen + C - 1) / C);
     a.scale = p->scale;
     a.o_f32 = p->o_dtype == KDA_DTYPE_F32;
+    a.ckpt = ckpt ? op->checkpoints : nullptr;
+    a.ckpt_every = ckpt ? op->ckpt_every : 0;
+    a.max_ckpts = ckpt ? op->max_ckpts : 0;
     const bool bf16 = p->qkv_dtype == KDA_DTYPE_BF16;
 
     hipError_t e = hipSuccess;
@@ -167,7 +198,15 @@ kda_status_t kda_chunk_fwd(const kda_chunk_params_t* p, const void* q, const voi
                            const float* alpha, const float* beta, const float* initial_state,
                            const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
                            size_t workspace_bytes, void* stream) {
-    return chunk_fwd_impl(p, q, k, v, alpha, beta, initial_state, cu_seqlens, o, final_state, workspace,
+    return chunk_fwd_impl(p, nullptr, q, k, v, alpha, beta, initial_state, cu_seqlens, o, final_state, workspace,
+                          workspace_bytes, stream, kBoth);
+}
+
+kda_status_t kda_chunk_fwd_ex(const kda_chunk_params_t* p, const kda_chunk_options_t* options, const void* q,
+                              const void* k, const void* v, const float* alpha, const float* beta,
+                              const float* initial_state, const int32_t* cu_seqlens, void* o, float* final_state,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    return chunk_fwd_impl(p, options, q, k, v, alpha, beta, initial_state, cu_seqlens, o, final_state, workspace,
                           workspace_bytes, stream, kBoth);
 }
 
@@ -175,7 +214,7 @@ kda_status_t kda_chunk_fwd_intra(const kda_chunk_params_t* p, const void* q, con
                                  const float* alpha, const float* beta, const float* initial_state,
                                  const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-    return chunk_fwd_impl(p, q, k, v, alpha, beta, initial_state, cu_seqlens, o, final_state, workspace,
+    return chunk_fwd_impl(p, nullptr, q, k, v, alpha, beta, initial_state, cu_seqlens, o, final_state, workspace,
                           workspace_bytes, stream, kIntra);
 }
 
@@ -183,7 +222,7 @@ kda_status_t kda_chunk_fwd_inter(const kda_chunk_params_t* p, const void* q, con
                                  const float* alpha, const float* beta, const float* initial_state,
                                  const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-    return chunk_fwd_impl(p, q, k, v, alpha, beta, initial_state, cu_seqlens, o, final_state, workspace,
+    return chunk_fwd_impl(p, nullptr, q, k, v, alpha, beta, initial_state, cu_seqlens, o, final_state, workspace,
                           workspace_bytes, stream, kInter);
 }
 

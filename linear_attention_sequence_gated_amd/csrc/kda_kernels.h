@@ -24,6 +24,9 @@ struct PrefillArgs {
     int32_t chunks_per_seq;      // fixed length: ceil(T / C)
     float scale;
     int32_t o_f32;               // 1: o is fp32, 0: o is bf16
+    float* ckpt;                 // [N, max_ckpts, H, dk, dv] state checkpoints, or null
+    int64_t ckpt_every;          // tokens between checkpoints (a multiple of the chunk)
+    int32_t max_ckpts;
 };
 
 struct DecodeArgs {

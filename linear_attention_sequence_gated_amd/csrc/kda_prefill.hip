@@ -686,7 +686,7 @@ void kda_inter_kernel(const PrefillArgs a) {
     const int grp = jx % ngroups;
     const int unit = (jx / ngroups) * 8 + xcd;
     if (unit >= a.N * a.H) return;  // whole workgroup
-    const int n = unit / H, h = unit % H;
+    const int n = unit / H, h = unit % H, seq = n;
 
     int c_begin, c_end;
     int64_t tok_begin, seq_len;
@@ -776,6 +776,22 @@ void kda_inter_kernel(const PrefillArgs a) {
             load_frag(kq, Kl, t, lane);
 #pragma unroll
             for (int n = 0; n < kSlicesPerWave; ++n) acc[n][t] = mma_quads(kq, ub[n], acc[n][t] * gv);
+        }
+        // state checkpoint: S after the first (jc + 1) C tokens when that is a
+        // multiple of ckpt_every inside the sequence (a full chunk)
+        if (a.ckpt) {
+            const int64_t done = (int64_t)(jc + 1) * C;
+            if (done <= seq_len && done % a.ckpt_every == 0 && done / a.ckpt_every <= a.max_ckpts) {
+                float* cp = a.ckpt + (((int64_t)seq * a.max_ckpts + done / a.ckpt_every - 1) * H + h) * DK * DV;
+#pragma unroll
+                for (int sl = 0; sl < kSlicesPerWave; ++sl)
+                    if (sl < nsl)
+#pragma unroll
+                        for (int t = 0; t < NQK; ++t)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                cp[(int64_t)(16 * t + 4 * g + j) * DV + 16 * (s0 + sl) + cl] = acc[sl][t][j];
+            }
         }
         // O^T = S^T Qtilde^T + U^T P^T   (lane: columns 4g + j, token 16tb + cl); S^T from sb (pre-update)
 #pragma unroll

@@ -107,6 +107,28 @@ def test_chunk_fwd_rejects_before_launch(lib):
                 wsb=need) == INVALID
 
 
+def _fwd_ex(lib, p, opt, sf=None, ws=FAKE, wsb=1 << 40):
+    return lib.kda_chunk_fwd_ex(ctypes.byref(p), ctypes.byref(opt) if opt is not None else None, FAKE, FAKE,
+                                FAKE, FAKE, FAKE, None, None, FAKE, sf, ws, ctypes.c_size_t(wsb), None)
+
+
+def test_chunk_fwd_ex_rejects_bad_options_before_launch(lib):
+    p = _params()
+    ck = ctypes.c_void_p(0x200000)
+    Opt = kda.ChunkOptions
+    assert _fwd_ex(lib, p, Opt(checkpoints=ck.value, ckpt_every=100, max_ckpts=2)) == INVALID   # not a multiple of 64
+    assert _fwd_ex(lib, p, Opt(checkpoints=ck.value, ckpt_every=-64, max_ckpts=2)) == INVALID
+    assert _fwd_ex(lib, p, Opt(checkpoints=None, ckpt_every=64, max_ckpts=2)) == INVALID
+    assert _fwd_ex(lib, p, Opt(checkpoints=ck.value, ckpt_every=64, max_ckpts=0)) == INVALID
+    assert _fwd_ex(lib, p, Opt(checkpoints=0x200004, ckpt_every=64, max_ckpts=1)) == INVALID     # misaligned
+    # checkpoints that overlap the final state
+    assert _fwd_ex(lib, p, Opt(checkpoints=ck.value, ckpt_every=64, max_ckpts=1),
+                   sf=ctypes.c_void_p(ck.value + 256)) == INVALID
+    # options that are declared but not built
+    for kw in ({"decay_floor": 0.5}, {"alpha_mode": 1}, {"fuse_inputs": 1}, {"gate": 0x300000}):
+        assert _fwd_ex(lib, p, Opt(**kw)) == UNSUPPORTED, kw
+
+
 def test_decode_step_rejects_before_launch(lib):
     def call(n=4, h=2, dk=128, dv=128, scale=1.0, dt=1, odt=1, ptrs=None):
         ptrs = ptrs or [FAKE] * 8

@@ -335,3 +335,61 @@ def test_split_phases_equal_fused_call():
     o2, S2 = pre.inter()
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+# --- state checkpoints (kda_chunk_fwd_ex) ---------------------------------------
+
+def _ckpt_check(inp, chunk, every, mx, tol, label):
+    say(f"[case] checkpoints {label} chunk={chunk} every={every} max={mx} {inp['q'].dtype}")
+    d = to_dev(inp)
+    B, T, H, dk = inp["q"].shape
+    dv = inp["v"].shape[-1]
+    n = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
+    ck = torch.full((n, mx, H, dk, dv), float("nan"), device="cuda")
+    o, S = kda.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"],
+                         chunk_size=chunk, o_dtype=torch.float32, checkpoints=ck, ckpt_every=every)
+    torch.cuda.synchronize()
+    cu = inp["cu_seqlens"]
+    oo, So, cko = kda_oracle.forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0=inp["S0"],
+                                     cu_seqlens=None if cu is None else cu.to(torch.int64),
+                                     ckpt_every=every, max_ckpts=mx, return_ckpt=True)
+    ckg = ck.cpu().numpy()
+    written_g = ~np.isnan(ckg).all(axis=(2, 3, 4))
+    written_o = ~np.isnan(cko).all(axis=(2, 3, 4))
+    assert np.array_equal(written_g, written_o), (written_g, written_o)   # the same slots, the rest untouched
+    assert written_o.any()
+    worst = 0.0
+    for sq, j in zip(*np.nonzero(written_o)):
+        worst = max(worst, rel_err(ckg[sq, j], cko[sq, j]))
+    eo, es = rel_err(o.cpu().numpy(), oo), rel_err(S.cpu().numpy(), So)
+    say(f"    {int(written_o.sum())} checkpoints, err ckpt={worst:.3e} o={eo:.3e} S={es:.3e} (tol {tol})")
+    assert worst < tol and eo < tol and es < tol
+    return ck
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_checkpoints_packed_ragged(dtype):
+    lens = [0, 1, 63, 64, 65, 200, 128, 129, 7]
+    inp = workloads.make_inputs(1, 0, 2, 128, 128, dtype, s0_std=0.02, seed=91, lengths=lens)
+    _ckpt_check(inp, 64, 64, 3, TOL[dtype], f"packed {lens}")
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_checkpoints_fixed_length(chunk):
+    inp = workloads.make_inputs(2, 300, 3, 64, 32, torch.bfloat16, s0_std=0.02, seed=92)
+    _ckpt_check(inp, chunk, 128, 3, TOL[torch.bfloat16], "B2 T300")
+
+
+def test_resume_from_checkpoint():
+    inp = workloads.make_inputs(1, 320, 2, 128, 128, torch.bfloat16, s0_std=0.02, seed=93)
+    ck = _ckpt_check(inp, 64, 128, 2, TOL[torch.bfloat16], "resume source")
+    # prefill resumed from checkpoint 1 (token 256) on the remaining tokens
+    tail = {k: (v[:, 256:].contiguous() if k in ("q", "k", "v", "alpha", "beta") else v) for k, v in inp.items()}
+    d = to_dev(tail)
+    o2, S2 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], ck[:, 1].contiguous(), None,
+                           chunk_size=64, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oo, So = oracle_prefill(inp)
+    eo, es = rel_err(o2.cpu().numpy(), oo[:, 256:]), rel_err(S2.cpu().numpy(), So)
+    say(f"    resumed tail err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16]
