@@ -205,6 +205,49 @@ kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads,
                              const float* alpha, const float* beta,
                              float* state, void* o, void* stream);
 
+/* Options of kda_decode_step_ex.  A zero-filled struct is exactly
+ * kda_decode_step. */
+typedef struct {
+    /* Paged state pool: NULL, or [N] int32 on the device.  Then `state` is a
+     * pool [P, H, dk, dv] fp32 and sequence n reads and updates pool entry
+     * state_slots[n] in place (the unified paged pool that holds the KDA
+     * states, "Kimi K3 architecture: KDA, MLA and MoE", section "Serving K3
+     * means managing two cache lifecycles").  Slots must lie in [0, P) and be
+     * distinct within a call; they are device data and are not checked. */
+    const int32_t* state_slots;
+    /* Floored decay: alpha values below decay_floor are raised to it (0: no
+     * floor), applied after the sigmoid of fuse_inputs. */
+    float decay_floor;
+    /* 0: alpha [N, H, dk] per key channel; 1: alpha [N, H], one decay per
+     * (sequence, head) for every channel (the scalar gate of Gated DeltaNet,
+     * "Kimi K3 architecture: KDA, MLA and MoE", section "KDA is a writable
+     * state, not a smaller KV cache"). */
+    int32_t alpha_mode;
+    /* 1: the neighbours of the token mixer run inside the step ("Kimi K3
+     * Architecture Teardown", Visual 1, the KDA inset): q and k are
+     * L2-normalised as x / max(|x|, 1e-12), alpha and beta are logits passed
+     * through 1 / (1 + e^-x). */
+    int32_t fuse_inputs;
+    /* Output norm and gate of the same inset: NULL, or gate logits [N, H, dv]
+     * (qkv dtype); then o = o / sqrt(mean_j(o_j^2) + norm_eps) * norm_weight
+     * * sigmoid(gate), the mean over the dv values of the head, norm_weight
+     * [dv] fp32 or NULL for ones. */
+    const void* gate;
+    const float* norm_weight;
+    float norm_eps;
+} kda_decode_options_t;
+
+/* kda_decode_step with the options above (NULL options = kda_decode_step).
+ * Errors as kda_decode_step, plus KDA_ERR_INVALID_ARG for bad option values
+ * (a negative or NaN floor or eps, misaligned pointers). */
+kda_status_t kda_decode_step_ex(int32_t num_seqs, int32_t num_heads,
+                                int32_t head_dim_k, int32_t head_dim_v,
+                                float scale, int32_t qkv_dtype, int32_t o_dtype,
+                                const kda_decode_options_t* options,
+                                const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta,
+                                float* state, void* o, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "
 
 # Every symbol include/kda.h declares.
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
-            "kda_chunk_fwd_inter", "kda_chunk_fwd_ex", "kda_decode_step")
+            "kda_chunk_fwd_inter", "kda_chunk_fwd_ex", "kda_decode_step", "kda_decode_step_ex")
 
 
 class KdaError(RuntimeError):
@@ -44,6 +44,13 @@ class ChunkOptions(ctypes.Structure):
     _fields_ = [("checkpoints", ctypes.c_void_p), ("ckpt_every", ctypes.c_int64), ("max_ckpts", ctypes.c_int32),
                 ("decay_floor", ctypes.c_float), ("alpha_mode", ctypes.c_int32), ("fuse_inputs", ctypes.c_int32),
                 ("gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float)]
+
+
+class DecodeOptions(ctypes.Structure):
+    """kda_decode_options_t (include/kda.h); zero-filled = the plain step."""
+    _fields_ = [("state_slots", ctypes.c_void_p), ("decay_floor", ctypes.c_float), ("alpha_mode", ctypes.c_int32),
+                ("fuse_inputs", ctypes.c_int32), ("gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float)]
 
 
 _lib = None
@@ -77,6 +84,9 @@ def load() -> ctypes.CDLL:
                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kda_decode_step_ex.restype = ctypes.c_int
+    lib.kda_decode_step_ex.argtypes = [i32, i32, i32, i32, f32, i32, i32, ctypes.POINTER(DecodeOptions),
+                                       vp, vp, vp, vp, vp, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -217,27 +227,55 @@ def chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_s
 
 
 def decode_step(q, k, v, alpha, beta, state, scale: float = 1.0, o=None, stream=None,
-                o_dtype: Optional[torch.dtype] = None):
-    """One decode step through kda_decode_step; ``state`` [N,H,dk,dv] is updated in place.
+                o_dtype: Optional[torch.dtype] = None, state_slots=None, decay_floor: float = 0.0,
+                alpha_scalar: bool = False, fuse_inputs: bool = False, gate=None, norm_weight=None,
+                norm_eps: float = 0.0):
+    """One decode step through kda_decode_step (or kda_decode_step_ex with any option).
 
-    q, k, alpha [N,H,dk], v [N,H,dv], beta [N,H].  Returns o [N,H,dv] (``o_dtype``,
-    default the dtype of q).
+    q, k [N,H,dk], alpha [N,H,dk] ([N,H] with ``alpha_scalar``), v [N,H,dv], beta [N,H];
+    ``state`` [N,H,dk,dv] is updated in place, or with ``state_slots`` (int32 [N] device)
+    it is a pool [P,H,dk,dv] and sequence n updates entry state_slots[n].  Options as in
+    include/kda.h: ``decay_floor``, ``fuse_inputs`` (L2 norm of q, k; alpha, beta logits),
+    ``gate`` [N,H,dv] logits with ``norm_weight`` [dv] and ``norm_eps``.
+    Returns o [N,H,dv] (``o_dtype``, default the dtype of q).
     """
     N, H, dk = q.shape
     dv = v.shape[-1]
-    _need(k.shape == q.shape and alpha.shape == q.shape and v.shape == (N, H, dv)
-          and beta.shape == (N, H) and state.shape == (N, H, dk, dv), "decode shapes")
+    a_shape = (N, H) if alpha_scalar else (N, H, dk)
+    _need(k.shape == q.shape and alpha.shape == a_shape and v.shape == (N, H, dv)
+          and beta.shape == (N, H), "decode shapes")
+    if state_slots is None:
+        _need(state.shape == (N, H, dk, dv), "state must be [N,H,dk,dv]")
+    else:
+        _need(state.dim() == 4 and state.shape[1:] == (H, dk, dv), "state pool must be [P,H,dk,dv]")
+        _need(state_slots.shape == (N,) and state_slots.dtype == torch.int32 and state_slots.is_cuda,
+              "state_slots must be int32 [N] on the device")
     _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
     _need(alpha.dtype == torch.float32 and beta.dtype == torch.float32
           and state.dtype == torch.float32, "alpha, beta, state must be fp32")
     for t in (q, k, v, alpha, beta, state):
         _need(t.is_cuda and t.is_contiguous(), "inputs must be contiguous device tensors")
+    if gate is not None:
+        _need(gate.shape == v.shape and gate.dtype == q.dtype and gate.is_cuda and gate.is_contiguous(),
+              "gate must be [N,H,dv] in the dtype of q")
+    if norm_weight is not None:
+        _need(norm_weight.shape == (dv,) and norm_weight.dtype == torch.float32 and norm_weight.is_cuda,
+              "norm_weight must be fp32 [dv]")
     o_dtype = q.dtype if o_dtype is None else o_dtype
     if o is None:
         o = torch.empty(v.shape, dtype=o_dtype, device=v.device)
     _need(o.shape == v.shape and o.dtype == o_dtype and o.is_contiguous(), "o shape/dtype")
-    st = load().kda_decode_step(N, H, dk, dv, float(scale), _code(q.dtype), _code(o_dtype),
-                                _ptr(q), _ptr(k), _ptr(v),
-                                _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o), _stream(stream))
-    _check("kda_decode_step", st)
+    lib = load()
+    head = (N, H, dk, dv, float(scale), _code(q.dtype), _code(o_dtype))
+    tail = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o), _stream(stream))
+    if (state_slots is None and not decay_floor and not alpha_scalar and not fuse_inputs and gate is None
+            and norm_weight is None):
+        _check("kda_decode_step", lib.kda_decode_step(*head, *tail))
+    else:
+        opt = DecodeOptions(state_slots=None if state_slots is None else state_slots.data_ptr(),
+                            decay_floor=float(decay_floor), alpha_mode=int(bool(alpha_scalar)),
+                            fuse_inputs=int(bool(fuse_inputs)), gate=None if gate is None else gate.data_ptr(),
+                            norm_weight=None if norm_weight is None else norm_weight.data_ptr(),
+                            norm_eps=float(norm_eps))
+        _check("kda_decode_step_ex", lib.kda_decode_step_ex(*head, ctypes.byref(opt), *tail))
     return o

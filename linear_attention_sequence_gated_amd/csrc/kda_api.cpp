@@ -226,18 +226,32 @@ kda_status_t kda_chunk_fwd_inter(const kda_chunk_params_t* p, const void* q, con
                           workspace_bytes, stream, kInter);
 }
 
-kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t dk, int32_t dv, float scale,
-                             int32_t qkv_dtype, int32_t o_dtype, const void* q, const void* k, const void* v,
-                             const float* alpha, const float* beta, float* state, void* o, void* stream) {
+namespace {
+
+kda_status_t decode_impl(int32_t num_seqs, int32_t num_heads, int32_t dk, int32_t dv, float scale,
+                         int32_t qkv_dtype, int32_t o_dtype, const kda_decode_options_t* op, const void* q,
+                         const void* k, const void* v, const float* alpha, const float* beta, float* state,
+                         void* o, void* stream) {
     if (num_seqs < 1 || num_heads < 1) return KDA_ERR_INVALID_ARG;
     if ((int64_t)num_seqs * num_heads > ((int64_t)1 << 31) - 1) return KDA_ERR_INVALID_ARG;
     if (!dtype_ok(qkv_dtype) || !dtype_ok(o_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
     if (!(scale == scale)) return KDA_ERR_INVALID_ARG;
     if (!q || !k || !v || !alpha || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(alpha, 16) ||
-        !aligned(state, 16) || !aligned(beta, 4))
+    const bool scalar_alpha = op && op->alpha_mode == 1;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(alpha, scalar_alpha ? 4 : 16) || !aligned(state, 16) || !aligned(beta, 4))
         return KDA_ERR_INVALID_ARG;
+    if (op) {
+        if (!(op->decay_floor >= 0.f) || !(op->norm_eps >= 0.f)) return KDA_ERR_INVALID_ARG;  // also NaN
+        if (op->alpha_mode != 0 && op->alpha_mode != 1) return KDA_ERR_INVALID_ARG;
+        if (op->fuse_inputs != 0 && op->fuse_inputs != 1) return KDA_ERR_INVALID_ARG;
+        if (op->state_slots && !aligned(op->state_slots, 4)) return KDA_ERR_INVALID_ARG;
+        if (op->gate && !aligned(op->gate, qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4)) return KDA_ERR_INVALID_ARG;
+        if (op->norm_weight && !aligned(op->norm_weight, 4)) return KDA_ERR_INVALID_ARG;
+        if (op->norm_weight && !op->gate) return KDA_ERR_INVALID_ARG;
+        if (op->gate && kda::decode_columns(dv) < dv) return KDA_ERR_UNSUPPORTED;  // row split over workgroups
+    }
     kda::DecodeArgs a{};
     a.q = q;
     a.k = k;
@@ -247,10 +261,37 @@ kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t dk, in
     a.state = state;
     a.o = o;
     a.units = num_seqs * num_heads;
+    a.H = num_heads;
     a.scale = scale;
     a.o_f32 = o_dtype == KDA_DTYPE_F32;
+    if (op) {
+        a.slots = op->state_slots;
+        a.alpha_floor = op->decay_floor;
+        a.alpha_scalar = op->alpha_mode;
+        a.fuse_inputs = op->fuse_inputs;
+        a.gate = op->gate;
+        a.norm_w = op->norm_weight;
+        a.norm_eps = op->norm_eps;
+    }
     const hipError_t e = kda::launch_decode(a, dk, dv, qkv_dtype == KDA_DTYPE_BF16, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t dk, int32_t dv, float scale,
+                             int32_t qkv_dtype, int32_t o_dtype, const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, float* state, void* o, void* stream) {
+    return decode_impl(num_seqs, num_heads, dk, dv, scale, qkv_dtype, o_dtype, nullptr, q, k, v, alpha, beta, state,
+                       o, stream);
+}
+
+kda_status_t kda_decode_step_ex(int32_t num_seqs, int32_t num_heads, int32_t dk, int32_t dv, float scale,
+                                int32_t qkv_dtype, int32_t o_dtype, const kda_decode_options_t* options,
+                                const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                                float* state, void* o, void* stream) {
+    return decode_impl(num_seqs, num_heads, dk, dv, scale, qkv_dtype, o_dtype, options, q, k, v, alpha, beta, state,
+                       o, stream);
 }
 
 }  // extern "C"

@@ -51,19 +51,23 @@ template <int DK, int DV> struct DecodeShape {
     static_assert(CG <= 64 && NT % CG == 0 && RPP * PASSES == DK, "decode thread mapping");
 };
 
+__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+
 template <int DK, int DV, typename T>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void kda_decode_kernel(const DecodeArgs a) {
     using D = DecodeShape<DK, DV>;
     constexpr int CG = D::CG, RPP = D::RPP, PASSES = D::PASSES, NW = D::NW, DVW = D::DVW;
     __shared__ float sq[DK], sk[DK], sa[DK], sv[DVW];
     __shared__ f32x4 red_r[NW][CG], red_y[NW][CG];
-    __shared__ float sqk;
+    __shared__ float sqk, siq, sik;
 
     const int unit = blockIdx.x / D::CB;        // n * H + h
     const int col0 = (blockIdx.x % D::CB) * DVW;  // first value column of this workgroup
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cg = tid % CG, r0 = tid / CG;
-    float* __restrict__ S = a.state + (int64_t)unit * DK * DV + col0;
+    // state of this (sequence, head): its own, or a pool entry
+    const int64_t sidx = a.slots ? (int64_t)a.slots[unit / a.H] * a.H + unit % a.H : (int64_t)unit;
+    float* __restrict__ S = a.state + sidx * DK * DV + col0;
 
     // state rows of this thread: issue every load before anything else
     f32x4 s[PASSES];
@@ -78,17 +82,34 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void kda_decode_kernel(c
     for (int i = tid; i < DK; i += D::NT) {
         sq[i] = load_as_float(q, i);
         sk[i] = load_as_float(k, i);
-        sa[i] = a.alpha[(int64_t)unit * DK + i];
+        float al = a.alpha_scalar ? a.alpha[unit] : a.alpha[(int64_t)unit * DK + i];
+        if (a.fuse_inputs) al = sigmoid(al);
+        sa[i] = fmaxf(al, a.alpha_floor);
     }
     for (int i = tid; i < DVW; i += D::NT) sv[i] = load_as_float(v, i);
-    const float beta = a.beta[unit];
+    float beta = a.beta[unit];
+    if (a.fuse_inputs) beta = sigmoid(beta);
     __syncthreads();
-    if (wave == 0) {
-        float t = 0.f;
-        for (int i = lane; i < DK; i += 64) t += sq[i] * sk[i];
+    if (wave == 0) {  // q.k and, for fused inputs, the inverse norms of q and k
+        float t = 0.f, nq = 0.f, nk = 0.f;
+        for (int i = lane; i < DK; i += 64) {
+            t += sq[i] * sk[i];
+            nq += sq[i] * sq[i];
+            nk += sk[i] * sk[i];
+        }
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) t += __shfl_xor(t, m, 64);
-        if (lane == 0) sqk = t;
+        for (int m = 32; m >= 1; m >>= 1) {
+            t += __shfl_xor(t, m, 64);
+            nq += __shfl_xor(nq, m, 64);
+            nk += __shfl_xor(nk, m, 64);
+        }
+        if (lane == 0) {
+            const float iq = a.fuse_inputs ? 1.f / fmaxf(sqrtf(nq), 1e-12f) : 1.f;
+            const float ik = a.fuse_inputs ? 1.f / fmaxf(sqrtf(nk), 1e-12f) : 1.f;
+            sqk = t * iq * ik;
+            siq = iq;
+            sik = ik;
+        }
     }
 
     // decay, then the two column reductions r = S'^T k and y = S'^T q
@@ -119,20 +140,37 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void kda_decode_kernel(c
         r += red_r[w][cg];
         y += red_y[w][cg];
     }
+    // normalised q and k enter linearly: scale the reductions once
+    const float iq = siq, ik = sik;
+    r = r * ik;
+    y = y * iq;
     const f32x4 vv{sv[4 * cg], sv[4 * cg + 1], sv[4 * cg + 2], sv[4 * cg + 3]};
     const f32x4 e = vv - r;  // correction towards the new value
 
     // erase and write with the same beta, back to the same addresses
+    const float bk = beta * ik;
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
         const int c = r0 + p * RPP;
-        const f32x4 ns = s[p] + (beta * sk[c]) * e;
+        const f32x4 ns = s[p] + (bk * sk[c]) * e;
         if (KDA_DECODE_NT_STORE) __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(S + c * DV + 4 * cg));
         else *reinterpret_cast<f32x4*>(S + c * DV + 4 * cg) = ns;
     }
-    if (r0 == 0) {
-        const f32x4 o4 = (y + (beta * sqk) * e) * a.scale;
+    if (r0 == 0) {  // the CG threads of the first row group: lanes 0 .. CG-1 of wave 0
+        f32x4 o4 = (y + (beta * sqk) * e) * a.scale;
         const int64_t oi = (int64_t)unit * DV + col0 + 4 * cg;
+        if (a.gate) {  // norm over the row (this workgroup holds all of it), weight, sigmoid gate
+            float ss = o4[0] * o4[0] + o4[1] * o4[1] + o4[2] * o4[2] + o4[3] * o4[3];
+#pragma unroll
+            for (int m = 1; m < CG; m <<= 1) ss += __shfl_xor(ss, m, 64);
+            const float inv = rsqrtf(ss / (float)DV + a.norm_eps);
+            const T* __restrict__ gt = reinterpret_cast<const T*>(a.gate) + oi;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float w = a.norm_w ? a.norm_w[col0 + 4 * cg + j] : 1.f;
+                o4[j] = o4[j] * inv * w * sigmoid(load_as_float(gt, j));
+            }
+        }
         if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + oi, o4);
         else store4(reinterpret_cast<__bf16*>(a.o) + oi, o4);
     }
@@ -166,6 +204,8 @@ static hipError_t launch_decode_k(const DecodeArgs& a, int DK, int DV, hipStream
     }
     return hipErrorInvalidValue;
 }
+
+int decode_columns(int DV) { return DV < KDA_DECODE_COLS ? DV : KDA_DECODE_COLS; }
 
 hipError_t launch_decode(const DecodeArgs& a, int DK, int DV, bool bf16, hipStream_t s) {
     return bf16 ? launch_decode_k<__bf16>(a, DK, DV, s) : launch_decode_k<float>(a, DK, DV, s);

@@ -38,8 +38,16 @@ struct DecodeArgs {
     float* state;
     void* o;
     int32_t units;               // N * H
+    int32_t H;
     float scale;
     int32_t o_f32;               // 1: o is fp32, 0: o is bf16
+    const int32_t* slots;        // [N] pool entries of the states, or null (state n * H + h)
+    float alpha_floor;           // alpha = max(alpha, floor); 0 leaves it as is
+    int32_t alpha_scalar;        // alpha [N, H]
+    int32_t fuse_inputs;         // L2 norm of q, k; sigmoid of alpha, beta logits
+    const void* gate;            // [N, H, dv] gate logits (q dtype), or null
+    const float* norm_w;         // [dv] or null
+    float norm_eps;
 };
 
 hipError_t launch_chunk_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t* chunk_off, hipStream_t s);
@@ -49,6 +57,8 @@ int effective_chunk(int DK, int C, bool bf16);
 hipError_t launch_intra(const PrefillArgs& a, int DK, int C, bool bf16, int max_chunks, hipStream_t s);
 hipError_t launch_inter(const PrefillArgs& a, int DK, int C, bool bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int DK, int DV, bool bf16, hipStream_t s);
+// Value columns one decode workgroup owns (the output gate needs the whole row).
+int decode_columns(int DV);
 int64_t chunk_block_bytes(int DK, int C, int DV, bool bf16);
 
 }  // namespace kda

@@ -142,3 +142,20 @@ def test_decode_step_rejects_before_launch(lib):
     assert call(scale=float("nan")) == INVALID
     assert call(ptrs=[FAKE] * 5 + [None] + [FAKE] * 2) == INVALID       # state
     assert call(ptrs=[FAKE] * 5 + [MISALIGNED] + [FAKE] * 2) == INVALID  # state alignment
+
+
+def test_decode_step_ex_rejects_bad_options_before_launch(lib):
+    Opt = kda.DecodeOptions
+
+    def call(opt, alpha=FAKE):
+        return lib.kda_decode_step_ex(2, 2, 64, 64, 1.0, 1, 0, ctypes.byref(opt), FAKE, FAKE, FAKE, alpha, FAKE,
+                                      FAKE, FAKE, None)
+    assert call(Opt(decay_floor=-0.5)) == INVALID
+    assert call(Opt(decay_floor=float("nan"))) == INVALID
+    assert call(Opt(norm_eps=-1.0, gate=0x30000)) == INVALID
+    assert call(Opt(alpha_mode=2)) == INVALID
+    assert call(Opt(fuse_inputs=3)) == INVALID
+    assert call(Opt(state_slots=0x30002)) == INVALID                 # misaligned slots
+    assert call(Opt(norm_weight=0x30000)) == INVALID                 # a norm weight needs a gate
+    assert call(Opt(), alpha=MISALIGNED) == INVALID                  # per-channel alpha: 16-byte aligned
+    assert call(Opt(alpha_mode=1), alpha=ctypes.c_void_p(0x10003)) == INVALID

@@ -393,3 +393,85 @@ def test_resume_from_checkpoint():
     eo, es = rel_err(o2.cpu().numpy(), oo[:, 256:]), rel_err(S2.cpu().numpy(), So)
     say(f"    resumed tail err o={eo:.3e} S={es:.3e}")
     assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16]
+
+
+# --- decode options (kda_decode_step_ex) ----------------------------------------
+
+def _decode_opts_case(N, H, dk, dv, steps, dtype, seed, pool=None, slots=None, **opts):
+    """Run `steps` decode steps with options on the GPU and the oracle; return the errors."""
+    g = torch.Generator().manual_seed(seed)
+    fuse = opts.get("fuse_inputs", False)
+    scal = opts.get("alpha_scalar", False)
+    q = torch.randn(steps, N, H, dk, generator=g)
+    k = torch.randn(steps, N, H, dk, generator=g)
+    if not fuse:
+        q = torch.nn.functional.normalize(q, dim=-1)
+        k = torch.nn.functional.normalize(k, dim=-1)
+    v = torch.nn.functional.silu(torch.randn(steps, N, H, dv, generator=g))
+    a_shape = (steps, N, H) if scal else (steps, N, H, dk)
+    al = torch.randn(*a_shape, generator=g) + 3.0          # logits
+    bl = torch.randn(steps, N, H, generator=g)
+    alpha, beta = (al, bl) if fuse else (torch.sigmoid(al), torch.sigmoid(bl))
+    gate = torch.randn(steps, N, H, dv, generator=g).to(dtype) if opts.get("gate") else None
+    w = (torch.rand(dv, generator=g) + 0.5) if opts.get("gate") else None
+    q, k, v = q.to(dtype), k.to(dtype), v.to(dtype)
+    P = pool if pool is not None else N
+    S0 = 0.02 * torch.randn(P, H, dk, dv, generator=g)
+    floor = opts.get("decay_floor", 0.0)
+    eps = 1e-5 if gate is not None else 0.0
+    state = S0.cuda()
+    dsl = None if slots is None else torch.tensor(slots, dtype=torch.int32, device="cuda")
+    outs = []
+    for t in range(steps):
+        o = kda.decode_step(q[t].cuda(), k[t].cuda(), v[t].cuda(), alpha[t].cuda(), beta[t].cuda(), state,
+                            o_dtype=torch.float32, state_slots=dsl, decay_floor=floor, alpha_scalar=scal,
+                            fuse_inputs=fuse, gate=None if gate is None else gate[t].cuda(),
+                            norm_weight=None if w is None else w.cuda(), norm_eps=eps)
+        outs.append(o)
+    torch.cuda.synchronize()
+    og = torch.stack(outs).cpu().numpy()
+    oo, So = kda_oracle.decode(S0, q, k, v, alpha, beta, state_slots=slots, decay_floor=floor,
+                               alpha_scalar=scal, fuse_inputs=fuse, gate=gate, norm_weight=w, norm_eps=eps)
+    sg = state.cpu()
+    idx = list(range(N)) if slots is None else list(slots)
+    eo, es = rel_err(og, oo), rel_err(sg[idx].numpy(), So)
+    if slots is not None:   # pool entries outside the call are untouched, bit for bit
+        rest = [p for p in range(P) if p not in slots]
+        assert torch.equal(sg[rest], S0[rest])
+    return eo, es
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_decode_paged_state_pool(dtype):
+    say(f"[case] decode paged pool {dtype}")
+    eo, es = _decode_opts_case(4, 3, 128, 128, 5, dtype, seed=301, pool=7, slots=[5, 0, 3, 6])
+    say(f"    err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL[dtype] and es < TOL[dtype]
+
+
+DECODE_OPTS = [
+    {"decay_floor": 0.97},
+    {"alpha_scalar": True},
+    {"fuse_inputs": True},
+    {"gate": True},
+    {"fuse_inputs": True, "gate": True, "decay_floor": 0.9},
+    {"fuse_inputs": True, "alpha_scalar": True, "gate": True},
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("opts", DECODE_OPTS, ids=lambda o: "+".join(sorted(o)))
+def test_decode_options(opts, dtype):
+    for (dk, dv) in ((128, 128), (64, 32)):
+        say(f"[case] decode options {opts} {dtype} dk={dk} dv={dv}")
+        eo, es = _decode_opts_case(6, 4, dk, dv, 4, dtype, seed=310 + dk + dv, **opts)
+        say(f"    err o={eo:.3e} S={es:.3e}")
+        assert eo < TOL[dtype] and es < TOL[dtype]
+
+
+def test_decode_options_combined_with_pool():
+    say("[case] decode pool + fused inputs + gate + floor")
+    eo, es = _decode_opts_case(5, 2, 128, 64, 3, torch.bfloat16, seed=333, pool=9, slots=[8, 1, 4, 0, 2],
+                               fuse_inputs=True, gate=True, decay_floor=0.95)
+    say(f"    err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16]
