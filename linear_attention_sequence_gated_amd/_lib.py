@@ -151,10 +151,13 @@ class Prefill:
     def __init__(self, q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_size: int = 64,
                  scale: float = 1.0, output_final_state: bool = True, o=None, final_state=None,
                  workspace=None, stream=None, o_dtype: Optional[torch.dtype] = None,
-                 checkpoints=None, ckpt_every: int = 0):
+                 checkpoints=None, ckpt_every: int = 0, decay_floor: float = 0.0,
+                 alpha_scalar: bool = False, fuse_inputs: bool = False):
         B, T, H, dk = q.shape
         dv = v.shape[-1]
-        _need(k.shape == q.shape and alpha.shape == q.shape, "q, k and alpha must share [B,T,H,dk]")
+        _need(k.shape == q.shape, "q and k must share [B,T,H,dk]")
+        _need(alpha.shape == ((B, T, H) if alpha_scalar else q.shape),
+              "alpha must be [B,T,H,dk] ([B,T,H] with alpha_scalar)")
         _need(v.shape == (B, T, H, dv) and beta.shape == (B, T, H), "v/beta shapes")
         _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
         _need(alpha.dtype == torch.float32 and beta.dtype == torch.float32, "alpha, beta must be fp32")
@@ -184,8 +187,12 @@ class Prefill:
                   and checkpoints.shape[2:] == (H, dk, dv) and checkpoints.dtype == torch.float32
                   and checkpoints.is_cuda and checkpoints.is_contiguous(),
                   "checkpoints must be fp32 [N, max_ckpts, H, dk, dv]")
-            self.options = ChunkOptions(checkpoints=checkpoints.data_ptr(), ckpt_every=int(ckpt_every),
-                                        max_ckpts=checkpoints.shape[1])
+        if ckpt_every or decay_floor or alpha_scalar or fuse_inputs:
+            self.options = ChunkOptions(checkpoints=checkpoints.data_ptr() if ckpt_every else None,
+                                        ckpt_every=int(ckpt_every),
+                                        max_ckpts=checkpoints.shape[1] if ckpt_every else 0,
+                                        decay_floor=float(decay_floor), alpha_mode=int(bool(alpha_scalar)),
+                                        fuse_inputs=int(bool(fuse_inputs)))
         self._keep = (q, k, v, alpha, beta, initial_state, cu_seqlens, checkpoints)
         self._args = (ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                       _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(final_state), _ptr(workspace),
@@ -211,7 +218,8 @@ class Prefill:
 def chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_size: int = 64,
               scale: float = 1.0, output_final_state: bool = True, o=None, final_state=None,
               workspace=None, stream=None, o_dtype: Optional[torch.dtype] = None,
-              checkpoints=None, ckpt_every: int = 0):
+              checkpoints=None, ckpt_every: int = 0, decay_floor: float = 0.0, alpha_scalar: bool = False,
+              fuse_inputs: bool = False):
     """Chunked KDA prefill through kda_chunk_fwd.  Returns (o, final_state or None).
 
     q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32, same dtype), alpha [B,T,H,dk] fp32,
@@ -220,10 +228,12 @@ def chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_s
     ``o_dtype`` (default: the dtype of q) is bf16 or fp32.  With ``ckpt_every`` (a
     multiple of 64) the call goes through kda_chunk_fwd_ex and writes the state after
     every ``ckpt_every`` tokens of each sequence into ``checkpoints`` [N,max_ckpts,H,dk,dv].
+    ``decay_floor``, ``alpha_scalar`` (alpha [B,T,H]) and ``fuse_inputs`` (L2 norm of q, k;
+    alpha, beta given as logits) are the other kda_chunk_options_t fields.
     """
     return Prefill(q, k, v, alpha, beta, initial_state, cu_seqlens, chunk_size, scale,
                    output_final_state, o, final_state, workspace, stream, o_dtype,
-                   checkpoints, ckpt_every).run()
+                   checkpoints, ckpt_every, decay_floor, alpha_scalar, fuse_inputs).run()
 
 
 def decode_step(q, k, v, alpha, beta, state, scale: float = 1.0, o=None, stream=None,

@@ -99,8 +99,11 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 kda_status_t check_options(const kda_chunk_params_t* p, const kda_chunk_options_t* op,
                            const float* initial_state, const float* final_state) {
     if (!op) return KDA_OK;
-    if (op->decay_floor != 0.f || op->alpha_mode != 0 || op->fuse_inputs != 0 || op->gate || op->norm_weight)
-        return KDA_ERR_UNSUPPORTED;
+    if (op->gate) return KDA_ERR_UNSUPPORTED;
+    if (op->norm_weight) return KDA_ERR_INVALID_ARG;   // a norm weight needs a gate
+    if (!(op->decay_floor >= 0.f)) return KDA_ERR_INVALID_ARG;   // also NaN
+    if (op->alpha_mode != 0 && op->alpha_mode != 1) return KDA_ERR_INVALID_ARG;
+    if (op->fuse_inputs != 0 && op->fuse_inputs != 1) return KDA_ERR_INVALID_ARG;
     if (op->ckpt_every < 0) return KDA_ERR_INVALID_ARG;
     if (op->ckpt_every > 0) {
         if (op->ckpt_every % 64 != 0 || op->max_ckpts < 1 || !op->checkpoints || !aligned(op->checkpoints, 16))
@@ -124,14 +127,15 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
     st = check_options(p, op, initial_state, final_state);
     if (st != KDA_OK) return st;
     const bool ckpt = op && op->ckpt_every > 0;
+    const bool scalar_alpha = op && op->alpha_mode == 1;
     const bool packed = cu_seqlens != nullptr;
     if (packed && p->batch != 1) return KDA_ERR_INVALID_ARG;
     if (!packed && p->num_seqs != p->batch) return KDA_ERR_INVALID_ARG;
     const bool has_tokens = p->seqlen > 0;
     if (has_tokens) {
         if (!q || !k || !v || !alpha || !beta || !o) return KDA_ERR_INVALID_ARG;
-        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(alpha, 16) ||
-            !aligned(beta, 4))
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+            !aligned(alpha, scalar_alpha ? 4 : 16) || !aligned(beta, 4))
             return KDA_ERR_INVALID_ARG;
     }
     if (initial_state && !aligned(initial_state, 16)) return KDA_ERR_INVALID_ARG;
@@ -174,6 +178,11 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
     a.ckpt = ckpt ? op->checkpoints : nullptr;
     a.ckpt_every = ckpt ? op->ckpt_every : 0;
     a.max_ckpts = ckpt ? op->max_ckpts : 0;
+    if (op) {
+        a.alpha_floor = op->decay_floor;
+        a.alpha_scalar = op->alpha_mode;
+        a.fuse_inputs = op->fuse_inputs;
+    }
     const bool bf16 = p->qkv_dtype == KDA_DTYPE_BF16;
 
     hipError_t e = hipSuccess;

@@ -27,6 +27,9 @@ struct PrefillArgs {
     float* ckpt;                 // [N, max_ckpts, H, dk, dv] state checkpoints, or null
     int64_t ckpt_every;          // tokens between checkpoints (a multiple of the chunk)
     int32_t max_ckpts;
+    float alpha_floor;           // alpha = max(alpha, floor); 0 leaves it as is
+    int32_t alpha_scalar;        // alpha [B, T, H]: one decay per token and head
+    int32_t fuse_inputs;         // L2 norm of q, k; sigmoid of alpha, beta logits
 };
 
 struct DecodeArgs {

@@ -41,6 +41,17 @@ constexpr float kFastRange = 12.f;
 #define KDA_LATE_V 1
 #endif
 
+__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+
+// alpha of (token row tok, head h, key channel c) as the recurrence uses it:
+// per channel or one per (token, head), through a sigmoid for fused inputs,
+// then floored.
+__device__ __forceinline__ float alpha_at(const PrefillArgs& a, int64_t tok, int h, int DK, int c) {
+    float al = a.alpha_scalar ? a.alpha[tok * a.H + h] : a.alpha[(tok * a.H + h) * DK + c];
+    if (a.fuse_inputs) al = sigmoid(al);
+    return fmaxf(al, a.alpha_floor);
+}
+
 // ---------------------------------------------------------------------------
 // K0: exclusive prefix of ceil(len_n / C) over the packed sequences.
 // ---------------------------------------------------------------------------
@@ -145,7 +156,8 @@ template <int DK, int C, typename T> struct Intra {
     static constexpr size_t kR1 = a16(cmax(cmax(kSeg, 3 * kTile), cmax(oXD + kXD, oVT + kVT)));
     static constexpr size_t kKtT = (size_t)DK * LD_CT * sizeof(T);
     // small: beta, block exponents at first / last token, pair factors, range flag
-    static constexpr size_t kSmall = (size_t)C * 4 + 2ull * NB * DK * 4 + (size_t)(NOFF > 0 ? NOFF : 1) * DK * 4 + 16;
+    static constexpr size_t kSmall = (size_t)C * 4 + 2ull * NB * DK * 4 + (size_t)(NOFF > 0 ? NOFF : 1) * DK * 4 + 16 +
+                                     2ull * C * 4;
     static constexpr size_t kLds = kR1 + kKtT + kSmall;
     static constexpr bool kFits = kLds <= 163840;
     static constexpr int kMinBlocks = kLds <= 81920 ? 2 : 1;
@@ -176,6 +188,7 @@ void kda_intra_kernel(const PrefillArgs a) {
     float* Ge = Gs + NB * DK;                   // [NB][DK] exponent at each block's last token
     float* sIR = Ge + NB * DK;                  // [NOFF][DK] pair factors 2^{G_R - G_I + h_I - h_R}
     unsigned* srange = reinterpret_cast<unsigned*>(sIR + (I::NOFF > 0 ? I::NOFF : 1) * DK);
+    float* sinv = reinterpret_cast<float*>(srange + 4);   // [2][C] inverse norms of q and k (fused inputs)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, g = lane >> 4, cl = lane & 15;
@@ -212,7 +225,19 @@ void kda_intra_kernel(const PrefillArgs a) {
             const int64_t base = ((pos.tok0 + r) * H + h) * DK + 8 * cg;
             load8(kg + base, kr[u]);
             load8(qg + base, qr[u]);
-            load8(a.alpha + base, al[u]);
+            if (a.alpha_scalar) {
+                const float as = a.alpha[(pos.tok0 + r) * H + h];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) al[u][e] = as;
+            } else {
+                load8(a.alpha + base, al[u]);
+            }
+            if (a.fuse_inputs) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) al[u][e] = sigmoid(al[u][e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) al[u][e] = fmaxf(al[u][e], a.alpha_floor);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) { kr[u][e] = 0.f; qr[u][e] = 0.f; al[u][e] = 1.f; }
@@ -233,7 +258,39 @@ void kda_intra_kernel(const PrefillArgs a) {
         }
     };
     if (!KDA_LATE_V) load_v();
-    if (tid < C) sbeta[tid] = tid < valid ? a.beta[(pos.tok0 + tid) * H + h] : 0.f;
+    if (a.fuse_inputs) {
+        // L2 norm of q and k per token: the NCG lanes of a token are adjacent
+        // lanes of one wave (tid = segment * NCG + channel group)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float nq = 0.f, nk = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                nq += qr[u][e] * qr[u][e];
+                nk += kr[u][e] * kr[u][e];
+            }
+#pragma unroll
+            for (int m = 1; m < I::NCG; m <<= 1) {
+                nq += __shfl_xor(nq, m, 64);
+                nk += __shfl_xor(nk, m, 64);
+            }
+            const float iq = 1.f / fmaxf(sqrtf(nq), 1e-12f), ik = 1.f / fmaxf(sqrtf(nk), 1e-12f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                qr[u][e] *= iq;
+                kr[u][e] *= ik;
+            }
+            if (p1 && cg == 0) {
+                sinv[4 * sgi + u] = iq;
+                sinv[C + 4 * sgi + u] = ik;
+            }
+        }
+    }
+    if (tid < C) {
+        float b = tid < valid ? a.beta[(pos.tok0 + tid) * H + h] : 0.f;
+        if (a.fuse_inputs && tid < valid) b = sigmoid(b);
+        sbeta[tid] = b;
+    }
     if (tid == 0) *srange = 0u;
 
     // segment sums of log2 alpha (floored), then the exclusive prefix per segment
@@ -457,17 +514,22 @@ void kda_intra_kernel(const PrefillArgs a) {
         if (i < valid) {
             float ki[CPP], prd[CPP];
             const int64_t bi = ((pos.tok0 + i) * H + h) * DK + c0;
+            const float iki = a.fuse_inputs ? sinv[C + i] : 1.f;
 #pragma unroll
-            for (int c = 0; c < CPP; ++c) { ki[c] = load_as_float(kg, bi + c); prd[c] = 1.f; }
+            for (int c = 0; c < CPP; ++c) { ki[c] = iki * load_as_float(kg, bi + c); prd[c] = 1.f; }
             for (int r = i; r < valid; ++r) {
                 const int64_t br = ((pos.tok0 + r) * H + h) * DK + c0;
                 float m = 0.f, pp = 0.f;
 #pragma unroll
                 for (int c = 0; c < CPP; ++c) {
-                    if (r > i) prd[c] *= a.alpha[br + c];
+                    if (r > i) prd[c] *= alpha_at(a, pos.tok0 + r, h, DK, c0 + c);
                     const float w = ki[c] * prd[c];
                     m += load_as_float(kg, br + c) * w;
                     pp += load_as_float(qg, br + c) * w;
+                }
+                if (a.fuse_inputs) {
+                    m *= sinv[C + r];
+                    pp *= sinv[r];
                 }
                 if (r > i) atomicAdd(&MX[r * LD_F + i], sbeta[r] * m);
                 atomicAdd(&Pm[r * LD_F + i], pp);

@@ -124,9 +124,11 @@ def test_chunk_fwd_ex_rejects_bad_options_before_launch(lib):
     # checkpoints that overlap the final state
     assert _fwd_ex(lib, p, Opt(checkpoints=ck.value, ckpt_every=64, max_ckpts=1),
                    sf=ctypes.c_void_p(ck.value + 256)) == INVALID
-    # options that are declared but not built
-    for kw in ({"decay_floor": 0.5}, {"alpha_mode": 1}, {"fuse_inputs": 1}, {"gate": 0x300000}):
-        assert _fwd_ex(lib, p, Opt(**kw)) == UNSUPPORTED, kw
+    assert _fwd_ex(lib, p, Opt(decay_floor=-0.1)) == INVALID
+    assert _fwd_ex(lib, p, Opt(decay_floor=float("nan"))) == INVALID
+    assert _fwd_ex(lib, p, Opt(alpha_mode=2)) == INVALID
+    assert _fwd_ex(lib, p, Opt(fuse_inputs=5)) == INVALID
+    assert _fwd_ex(lib, p, Opt(norm_weight=0x300000)) == INVALID        # a norm weight needs a gate
 
 
 def test_decode_step_rejects_before_launch(lib):

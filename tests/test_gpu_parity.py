@@ -475,3 +475,88 @@ def test_decode_options_combined_with_pool():
                                fuse_inputs=True, gate=True, decay_floor=0.95)
     say(f"    err o={eo:.3e} S={es:.3e}")
     assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16]
+
+
+# --- prefill input options (kda_chunk_fwd_ex) -----------------------------------
+
+def _prefill_opts_inputs(B, T, H, dk, dv, dtype, seed, lengths=None, alpha_mu=3.0, **opts):
+    g = torch.Generator().manual_seed(seed)
+    fuse = opts.get("fuse_inputs", False)
+    scal = opts.get("alpha_scalar", False)
+    tot = B * T if lengths is None else sum(lengths)
+    sh = (B, T) if lengths is None else (1, tot)
+    q = torch.randn(*sh, H, dk, generator=g) * 2.0
+    k = torch.randn(*sh, H, dk, generator=g) * 0.7
+    if not fuse:
+        q = torch.nn.functional.normalize(q, dim=-1)
+        k = torch.nn.functional.normalize(k, dim=-1)
+    v = torch.nn.functional.silu(torch.randn(*sh, H, dv, generator=g))
+    al = torch.randn(*sh, H, *(() if scal else (dk,)), generator=g) + alpha_mu
+    bl = torch.randn(*sh, H, generator=g)
+    n = B if lengths is None else len(lengths)
+    inp = {"q": q.to(dtype), "k": k.to(dtype), "v": v.to(dtype),
+           "alpha": al if fuse else torch.sigmoid(al), "beta": bl if fuse else torch.sigmoid(bl),
+           "S0": 0.02 * torch.randn(n, H, dk, dv, generator=g),
+           "cu_seqlens": None if lengths is None else
+           torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32)}
+    return inp
+
+
+def _prefill_opts_check(inp, chunk, tol, label, **opts):
+    say(f"[case] prefill options {opts} {label} chunk={chunk} {inp['q'].dtype}")
+    og, Sg = gpu_prefill(inp, chunk, **opts)
+    cu = inp["cu_seqlens"]
+    oo, So = kda_oracle.forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0=inp["S0"],
+                                cu_seqlens=None if cu is None else cu.to(torch.int64), **opts)
+    eo, es = rel_err(og, oo), rel_err(Sg, So)
+    say(f"    err o={eo:.3e} S={es:.3e} (tol {tol})")
+    assert eo < tol and es < tol
+
+
+PREFILL_OPTS = [
+    {"decay_floor": 0.9},
+    {"alpha_scalar": True},
+    {"fuse_inputs": True},
+    {"fuse_inputs": True, "alpha_scalar": True, "decay_floor": 0.8},
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("opts", PREFILL_OPTS, ids=lambda o: "+".join(sorted(o)))
+def test_prefill_options(opts, dtype):
+    lens = [1, 63, 64, 65, 150, 7]
+    inp = _prefill_opts_inputs(1, 0, 2, 128, 128, dtype, seed=401, lengths=lens, **opts)
+    _prefill_opts_check(inp, 64, TOL[dtype], f"packed {lens}", **opts)
+    inp = _prefill_opts_inputs(2, 100, 3, 64, 32, dtype, seed=402, **opts)
+    _prefill_opts_check(inp, 16, TOL[dtype], "B2 T100 dk64 dv32", **opts)
+
+
+@pytest.mark.parametrize("opts", [{"fuse_inputs": True}, {"alpha_scalar": True}, {"decay_floor": 0.01}],
+                         ids=lambda o: "+".join(sorted(o)))
+def test_prefill_options_fast_decay_exact_path(opts):
+    # alpha ~ sigmoid(N(-3, 1)): 16-token blocks decay far beyond the factored
+    # path's range, so chunks take the exact pairwise path
+    inp = _prefill_opts_inputs(1, 200, 2, 128, 128, torch.bfloat16, seed=403, alpha_mu=-3.0, **opts)
+    _prefill_opts_check(inp, 64, TOL[torch.bfloat16], "fast decay", **opts)
+
+
+def test_prefill_options_with_checkpoints():
+    lens = [200, 64, 130]
+    opts = {"fuse_inputs": True, "decay_floor": 0.5}
+    inp = _prefill_opts_inputs(1, 0, 2, 128, 64, torch.bfloat16, seed=404, lengths=lens, **opts)
+    say(f"[case] prefill options + checkpoints {opts}")
+    d = to_dev(inp)
+    ck = torch.full((3, 3, 2, 128, 64), float("nan"), device="cuda")
+    o, S = kda.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"], chunk_size=64,
+                         o_dtype=torch.float32, checkpoints=ck, ckpt_every=64, **opts)
+    torch.cuda.synchronize()
+    oo, So, cko = kda_oracle.forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0=inp["S0"],
+                                     cu_seqlens=inp["cu_seqlens"].to(torch.int64), ckpt_every=64, max_ckpts=3,
+                                     return_ckpt=True, **opts)
+    ckg = ck.cpu().numpy()
+    wo = ~np.isnan(cko).all(axis=(2, 3, 4))
+    assert np.array_equal(~np.isnan(ckg).all(axis=(2, 3, 4)), wo)
+    worst = max(rel_err(ckg[a, b], cko[a, b]) for a, b in zip(*np.nonzero(wo)))
+    eo, es = rel_err(o.cpu().numpy(), oo), rel_err(S.cpu().numpy(), So)
+    say(f"    err ckpt={worst:.3e} o={eo:.3e} S={es:.3e}")
+    assert worst < 2e-2 and eo < 2e-2 and es < 2e-2
