@@ -142,8 +142,7 @@ kda_status_t kda_chunk_fwd_inter(const kda_chunk_params_t* params,
                                  void* stream);
 
 /* Options of kda_chunk_fwd_ex.  A zero-filled struct is exactly kda_chunk_fwd.
- * Fields that are set but not built in this library return
- * KDA_ERR_UNSUPPORTED before anything is launched. */
+ * Option values are validated before anything is launched. */
 typedef struct {
     /* State checkpoints at prefix boundaries.  The serving side keeps the
      * fixed-size recurrent state at selected prefix boundaries so that a
@@ -161,27 +160,36 @@ typedef struct {
     float* checkpoints;
     int64_t ckpt_every;
     int32_t max_ckpts;
-    /* Floored decay: alpha values below decay_floor are raised to it (0: no
-     * floor).  Not built yet. */
+    /* Floored decay: alpha values below decay_floor (>= 0) are raised to it
+     * (0: no floor); K3 floors its decay ("Kimi K3 Architecture Teardown",
+     * section "Hybrid Attention for 1M Tokens").  Applied after the sigmoid
+     * of fuse_inputs. */
     float decay_floor;
     /* 0: alpha is per key channel [B, T, H, dk]; 1: one decay per token and
-     * head, alpha [B, T, H] (scalar gate).  Not built yet. */
+     * head, alpha [B, T, H], for every channel (the scalar gate of Gated
+     * DeltaNet that KDA refines per channel, "Kimi K3 architecture: KDA, MLA
+     * and MoE", section "KDA is a writable state, not a smaller KV cache");
+     * alpha is then 4-byte aligned. */
     int32_t alpha_mode;
-    /* 1: q and k are L2-normalised per (token, head) and alpha, beta are
-     * logits passed through a sigmoid, inside the kernels.  Not built yet. */
+    /* 1: the neighbours of the token mixer run inside the kernels ("Kimi K3
+     * Architecture Teardown", Visual 1, the KDA inset): q and k are
+     * L2-normalised per (token, head) as x / max(|x|, 1e-12), and alpha, beta
+     * are logits passed through 1 / (1 + e^-x). */
     int32_t fuse_inputs;
-    /* Output gate: NULL, or gate logits [B, T, H, dv] (qkv dtype); then
-     * o = rmsnorm(o) * norm_weight * sigmoid(gate), the norm over dv with
-     * norm_eps, norm_weight [dv] fp32 or NULL for ones.  Not built yet. */
+    /* Output norm and gate of the same inset: NULL, or gate logits
+     * [B, T, H, dv] (qkv dtype); then o = o / sqrt(mean_j(o_j^2) + norm_eps)
+     * * norm_weight * sigmoid(gate), the mean over the dv values of the
+     * (token, head), norm_weight [dv] fp32 or NULL for ones. */
     const void* gate;
     const float* norm_weight;
     float norm_eps;
 } kda_chunk_options_t;
 
 /* kda_chunk_fwd with the options above (NULL options = kda_chunk_fwd).  The
- * workspace is the one kda_chunk_fwd_workspace_size quotes.  Errors as
- * kda_chunk_fwd, plus KDA_ERR_INVALID_ARG for bad option values and
- * KDA_ERR_UNSUPPORTED for options not built. */
+ * workspace is the one kda_chunk_fwd_workspace_size quotes (it covers every
+ * option).  Errors as kda_chunk_fwd, plus KDA_ERR_INVALID_ARG for bad option
+ * values (negative or NaN floor or eps, a norm weight without a gate,
+ * misaligned option pointers, bad checkpoint layout). */
 kda_status_t kda_chunk_fwd_ex(const kda_chunk_params_t* params, const kda_chunk_options_t* options,
                               const void* q, const void* k, const void* v,
                               const float* alpha, const float* beta,

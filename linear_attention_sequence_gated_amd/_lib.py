@@ -152,7 +152,8 @@ class Prefill:
                  scale: float = 1.0, output_final_state: bool = True, o=None, final_state=None,
                  workspace=None, stream=None, o_dtype: Optional[torch.dtype] = None,
                  checkpoints=None, ckpt_every: int = 0, decay_floor: float = 0.0,
-                 alpha_scalar: bool = False, fuse_inputs: bool = False):
+                 alpha_scalar: bool = False, fuse_inputs: bool = False, gate=None, norm_weight=None,
+                 norm_eps: float = 0.0):
         B, T, H, dk = q.shape
         dv = v.shape[-1]
         _need(k.shape == q.shape, "q and k must share [B,T,H,dk]")
@@ -187,13 +188,22 @@ class Prefill:
                   and checkpoints.shape[2:] == (H, dk, dv) and checkpoints.dtype == torch.float32
                   and checkpoints.is_cuda and checkpoints.is_contiguous(),
                   "checkpoints must be fp32 [N, max_ckpts, H, dk, dv]")
-        if ckpt_every or decay_floor or alpha_scalar or fuse_inputs:
+        if gate is not None:
+            _need(gate.shape == v.shape and gate.dtype == q.dtype and gate.is_cuda and gate.is_contiguous(),
+                  "gate must be [B,T,H,dv] in the dtype of q")
+        if norm_weight is not None:
+            _need(norm_weight.shape == (dv,) and norm_weight.dtype == torch.float32 and norm_weight.is_cuda,
+                  "norm_weight must be fp32 [dv]")
+        if ckpt_every or decay_floor or alpha_scalar or fuse_inputs or gate is not None or norm_weight is not None:
             self.options = ChunkOptions(checkpoints=checkpoints.data_ptr() if ckpt_every else None,
                                         ckpt_every=int(ckpt_every),
                                         max_ckpts=checkpoints.shape[1] if ckpt_every else 0,
                                         decay_floor=float(decay_floor), alpha_mode=int(bool(alpha_scalar)),
-                                        fuse_inputs=int(bool(fuse_inputs)))
-        self._keep = (q, k, v, alpha, beta, initial_state, cu_seqlens, checkpoints)
+                                        fuse_inputs=int(bool(fuse_inputs)),
+                                        gate=None if gate is None else gate.data_ptr(),
+                                        norm_weight=None if norm_weight is None else norm_weight.data_ptr(),
+                                        norm_eps=float(norm_eps))
+        self._keep = (q, k, v, alpha, beta, initial_state, cu_seqlens, checkpoints, gate, norm_weight)
         self._args = (ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                       _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(final_state), _ptr(workspace),
                       ctypes.c_size_t(workspace.numel()), _stream(stream))
@@ -219,7 +229,7 @@ def chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_s
               scale: float = 1.0, output_final_state: bool = True, o=None, final_state=None,
               workspace=None, stream=None, o_dtype: Optional[torch.dtype] = None,
               checkpoints=None, ckpt_every: int = 0, decay_floor: float = 0.0, alpha_scalar: bool = False,
-              fuse_inputs: bool = False):
+              fuse_inputs: bool = False, gate=None, norm_weight=None, norm_eps: float = 0.0):
     """Chunked KDA prefill through kda_chunk_fwd.  Returns (o, final_state or None).
 
     q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32, same dtype), alpha [B,T,H,dk] fp32,
@@ -228,12 +238,14 @@ def chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_s
     ``o_dtype`` (default: the dtype of q) is bf16 or fp32.  With ``ckpt_every`` (a
     multiple of 64) the call goes through kda_chunk_fwd_ex and writes the state after
     every ``ckpt_every`` tokens of each sequence into ``checkpoints`` [N,max_ckpts,H,dk,dv].
-    ``decay_floor``, ``alpha_scalar`` (alpha [B,T,H]) and ``fuse_inputs`` (L2 norm of q, k;
-    alpha, beta given as logits) are the other kda_chunk_options_t fields.
+    ``decay_floor``, ``alpha_scalar`` (alpha [B,T,H]), ``fuse_inputs`` (L2 norm of q, k;
+    alpha, beta given as logits) and ``gate`` [B,T,H,dv] with ``norm_weight`` [dv] and
+    ``norm_eps`` (output norm and sigmoid gate) are the other kda_chunk_options_t fields.
     """
     return Prefill(q, k, v, alpha, beta, initial_state, cu_seqlens, chunk_size, scale,
                    output_final_state, o, final_state, workspace, stream, o_dtype,
-                   checkpoints, ckpt_every, decay_floor, alpha_scalar, fuse_inputs).run()
+                   checkpoints, ckpt_every, decay_floor, alpha_scalar, fuse_inputs, gate, norm_weight,
+                   norm_eps).run()
 
 
 def decode_step(q, k, v, alpha, beta, state, scale: float = 1.0, o=None, stream=None,

@@ -44,15 +44,15 @@ int chunk_of(const kda_chunk_params_t* p) {
     return kda::effective_chunk(p->head_dim_k, p->chunk_size, p->qkv_dtype == KDA_DTYPE_BF16);
 }
 
-PrefillPlan plan_prefill(const kda_chunk_params_t* p, bool packed) {
+PrefillPlan plan_prefill(const kda_chunk_params_t* p, bool packed, bool gate) {
     PrefillPlan pl{};
     const int64_t C = chunk_of(p);
     if (packed)
         pl.max_chunks = p->seqlen / C + p->num_seqs + 1;
     else
         pl.max_chunks = (int64_t)p->batch * ((p->seqlen + C - 1) / C);
-    pl.block_bytes = kda::chunk_block_bytes(p->head_dim_k, (int)C, p->head_dim_v,
-                                            p->qkv_dtype == KDA_DTYPE_BF16);
+    pl.block_bytes = kda::chunk_block_bytes(p->head_dim_k, (int)C, p->head_dim_v, p->qkv_dtype == KDA_DTYPE_BF16,
+                                            kda::slice_group(p->head_dim_v, gate));
     pl.off_bytes = packed ? round_up(sizeof(int32_t) * ((size_t)p->num_seqs + 1), kWsAlign) : 0;
     pl.total = pl.off_bytes + (size_t)pl.max_chunks * (size_t)p->num_heads * (size_t)pl.block_bytes;
     return pl;
@@ -79,8 +79,13 @@ kda_status_t kda_chunk_fwd_workspace_size(const kda_chunk_params_t* p, size_t* b
     if (st != KDA_OK) return st;
     // the size is quoted for the worst case of either layout so that one
     // buffer serves packed and fixed-length calls of the same shape
-    const PrefillPlan a = plan_prefill(p, true), b = plan_prefill(p, false);
-    *bytes = a.total > b.total ? a.total : b.total;
+    size_t most = 0;
+    for (int packed = 0; packed < 2; ++packed)
+        for (int gate = 0; gate < 2; ++gate) {
+            const PrefillPlan pl = plan_prefill(p, packed, gate);
+            most = pl.total > most ? pl.total : most;
+        }
+    *bytes = most;
     return KDA_OK;
 }
 
@@ -99,8 +104,10 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 kda_status_t check_options(const kda_chunk_params_t* p, const kda_chunk_options_t* op,
                            const float* initial_state, const float* final_state) {
     if (!op) return KDA_OK;
-    if (op->gate) return KDA_ERR_UNSUPPORTED;
-    if (op->norm_weight) return KDA_ERR_INVALID_ARG;   // a norm weight needs a gate
+    if (op->norm_weight && !op->gate) return KDA_ERR_INVALID_ARG;   // a norm weight needs a gate
+    if (op->gate && !aligned(op->gate, p->qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4)) return KDA_ERR_INVALID_ARG;
+    if (op->norm_weight && !aligned(op->norm_weight, 4)) return KDA_ERR_INVALID_ARG;
+    if (!(op->norm_eps >= 0.f)) return KDA_ERR_INVALID_ARG;       // also NaN
     if (!(op->decay_floor >= 0.f)) return KDA_ERR_INVALID_ARG;   // also NaN
     if (op->alpha_mode != 0 && op->alpha_mode != 1) return KDA_ERR_INVALID_ARG;
     if (op->fuse_inputs != 0 && op->fuse_inputs != 1) return KDA_ERR_INVALID_ARG;
@@ -146,7 +153,8 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
         const size_t sb = (size_t)p->num_seqs * p->num_heads * p->head_dim_k * p->head_dim_v * sizeof(float);
         if (overlaps(initial_state, sb, final_state, sb)) return KDA_ERR_INVALID_ARG;
     }
-    const PrefillPlan pl = plan_prefill(p, packed);
+    const bool gate = op && op->gate;
+    const PrefillPlan pl = plan_prefill(p, packed, gate);
     if (pl.total > 0) {
         if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_WORKSPACE;
         if (workspace_bytes < pl.total) return KDA_ERR_WORKSPACE;
@@ -182,7 +190,11 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
         a.alpha_floor = op->decay_floor;
         a.alpha_scalar = op->alpha_mode;
         a.fuse_inputs = op->fuse_inputs;
+        a.gate = op->gate;
+        a.norm_w = op->norm_weight;
+        a.norm_eps = op->norm_eps;
     }
+    a.gsl = kda::slice_group(p->head_dim_v, gate);
     const bool bf16 = p->qkv_dtype == KDA_DTYPE_BF16;
 
     hipError_t e = hipSuccess;

@@ -30,6 +30,10 @@ struct PrefillArgs {
     float alpha_floor;           // alpha = max(alpha, floor); 0 leaves it as is
     int32_t alpha_scalar;        // alpha [B, T, H]: one decay per token and head
     int32_t fuse_inputs;         // L2 norm of q, k; sigmoid of alpha, beta logits
+    const void* gate;            // [B, T, H, dv] output gate logits (q dtype), or null
+    const float* norm_w;         // [dv] or null
+    float norm_eps;
+    int32_t gsl;                 // value slices per slice group (slice_group())
 };
 
 struct DecodeArgs {
@@ -62,6 +66,10 @@ hipError_t launch_inter(const PrefillArgs& a, int DK, int C, bool bf16, hipStrea
 hipError_t launch_decode(const DecodeArgs& a, int DK, int DV, bool bf16, hipStream_t s);
 // Value columns one decode workgroup owns (the output gate needs the whole row).
 int decode_columns(int DV);
-int64_t chunk_block_bytes(int DK, int C, int DV, bool bf16);
+// Value slices per inter-chunk workgroup (and per Utilde group of the
+// workspace): all dv / 16 when the output gate is fused (it needs a token's
+// whole row in one workgroup), else the plain grouping.
+int slice_group(int DV, bool gate);
+int64_t chunk_block_bytes(int DK, int C, int DV, bool bf16, int gsl);
 
 }  // namespace kda

@@ -163,7 +163,9 @@ template <int DK, int C, typename T> struct Intra {
     static constexpr int kMinBlocks = kLds <= 81920 ? 2 : 1;
 };
 
-template <int DK, int C, typename In>
+// kOpts: the input options (decay floor, scalar gate, fused transforms) are
+// compiled in; plain calls run the instance without them.
+template <int DK, int C, typename In, bool kOpts>
 __global__ __launch_bounds__(256, (Intra<DK, C, typename OperandOf<In>::type>::kMinBlocks))
 void kda_intra_kernel(const PrefillArgs a) {
     using T = typename OperandOf<In>::type;
@@ -202,7 +204,7 @@ void kda_intra_kernel(const PrefillArgs a) {
     const In* __restrict__ kg = reinterpret_cast<const In*>(a.k);
     const In* __restrict__ vg = reinterpret_cast<const In*>(a.v);
 
-    const ChunkBlock<T> cb(DK, C, DV);
+    const ChunkBlock<T> cb(DK, C, DV, a.gsl);
     char* blk = a.ws_chunks + ((int64_t)x * H + h) * cb.bytes;
     T* Wf = reinterpret_cast<T*>(blk + cb.w);
     T* Qf = reinterpret_cast<T*>(blk + cb.q);
@@ -225,19 +227,21 @@ void kda_intra_kernel(const PrefillArgs a) {
             const int64_t base = ((pos.tok0 + r) * H + h) * DK + 8 * cg;
             load8(kg + base, kr[u]);
             load8(qg + base, qr[u]);
-            if (a.alpha_scalar) {
+            if (kOpts && a.alpha_scalar) {
                 const float as = a.alpha[(pos.tok0 + r) * H + h];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) al[u][e] = as;
             } else {
                 load8(a.alpha + base, al[u]);
             }
-            if (a.fuse_inputs) {
+            if (kOpts && a.fuse_inputs) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) al[u][e] = sigmoid(al[u][e]);
             }
+            if (kOpts) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) al[u][e] = fmaxf(al[u][e], a.alpha_floor);
+                for (int e = 0; e < 8; ++e) al[u][e] = fmaxf(al[u][e], a.alpha_floor);
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) { kr[u][e] = 0.f; qr[u][e] = 0.f; al[u][e] = 1.f; }
@@ -258,7 +262,7 @@ void kda_intra_kernel(const PrefillArgs a) {
         }
     };
     if (!KDA_LATE_V) load_v();
-    if (a.fuse_inputs) {
+    if (kOpts && a.fuse_inputs) {
         // L2 norm of q and k per token: the NCG lanes of a token are adjacent
         // lanes of one wave (tid = segment * NCG + channel group)
 #pragma unroll
@@ -288,7 +292,7 @@ void kda_intra_kernel(const PrefillArgs a) {
     }
     if (tid < C) {
         float b = tid < valid ? a.beta[(pos.tok0 + tid) * H + h] : 0.f;
-        if (a.fuse_inputs && tid < valid) b = sigmoid(b);
+        if (kOpts && a.fuse_inputs && tid < valid) b = sigmoid(b);
         sbeta[tid] = b;
     }
     if (tid == 0) *srange = 0u;
@@ -514,7 +518,7 @@ void kda_intra_kernel(const PrefillArgs a) {
         if (i < valid) {
             float ki[CPP], prd[CPP];
             const int64_t bi = ((pos.tok0 + i) * H + h) * DK + c0;
-            const float iki = a.fuse_inputs ? sinv[C + i] : 1.f;
+            const float iki = kOpts && a.fuse_inputs ? sinv[C + i] : 1.f;
 #pragma unroll
             for (int c = 0; c < CPP; ++c) { ki[c] = iki * load_as_float(kg, bi + c); prd[c] = 1.f; }
             for (int r = i; r < valid; ++r) {
@@ -522,12 +526,12 @@ void kda_intra_kernel(const PrefillArgs a) {
                 float m = 0.f, pp = 0.f;
 #pragma unroll
                 for (int c = 0; c < CPP; ++c) {
-                    if (r > i) prd[c] *= alpha_at(a, pos.tok0 + r, h, DK, c0 + c);
+                    if (r > i) prd[c] *= kOpts ? alpha_at(a, pos.tok0 + r, h, DK, c0 + c) : a.alpha[br + c];
                     const float w = ki[c] * prd[c];
                     m += load_as_float(kg, br + c) * w;
                     pp += load_as_float(qg, br + c) * w;
                 }
-                if (a.fuse_inputs) {
+                if (kOpts && a.fuse_inputs) {
                     m *= sinv[C + r];
                     pp *= sinv[r];
                 }
@@ -693,12 +697,28 @@ __device__ __forceinline__ void load_frag(f32x4 (&q)[N], const char* base, int r
     for (int u = 0; u < N; ++u) q[u] = *reinterpret_cast<const f32x4*>(p + u * 64 * 4);
 }
 
-template <int DK, int C, typename T> struct Inter {
+// Value slices (16 columns each) per compute wave of a plain call: the A
+// fragments loaded from LDS feed that many MFMA column tiles.
+#ifndef KDA_SLICES_PER_WAVE
+#define KDA_SLICES_PER_WAVE 1
+#endif
+#define KDA_SLICES_PER_WAVE_VALUE KDA_SLICES_PER_WAVE
+
+// Gated calls keep all dv / 16 slices (8 at dv = 128) in one workgroup, two per
+// compute wave, so that a workgroup still has two waves per SIMD (8 waves).
+constexpr int kGateSlices = 8;
+constexpr int kGateSlicesPerWave = 2;
+
+template <int DK, int C, typename T, bool kGate = false> struct Inter {
+    static constexpr int G = kGate ? kGateSlices : kGroupSlices;   // most slices per workgroup
+    static constexpr int SPW = kGate ? kGateSlicesPerWave : KDA_SLICES_PER_WAVE_VALUE;
+    static constexpr int kMaxCompute = (G + SPW - 1) / SPW;
     static constexpr int64_t kShared = (2 * Frag<T>::elems(C, DK) + Frag<T>::elems(DK, C) + Frag<T>::elems(C, C)) *
                                            (int64_t)sizeof(T) + round_kib(DK * 4);
-    static constexpr int64_t kGroupMax = round_kib((int64_t)kGroupSlices * C * 16 * sizeof(T));
+    static constexpr int64_t kGroupMax = round_kib((int64_t)G * C * 16 * sizeof(T));
     static constexpr int64_t kBuf = kShared + kGroupMax;
-    static constexpr bool kFits = 2 * kBuf <= 163840;
+    static constexpr int64_t kPart = kGate ? 2ll * kMaxCompute * C * 4 : 0;   // output-norm partial sums
+    static constexpr bool kFits = 2 * kBuf + kPart <= 163840;
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -709,16 +729,6 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 #endif
 // Waves per workgroup that copy chunk blocks into LDS (they split the 1 KiB units).
 constexpr int kIoWaves = KDA_IO_WAVES;
-// Value slices (16 columns each) per compute wave: the A fragments loaded from
-// LDS feed kSlicesPerWave MFMA column tiles.  A slice group of up to four
-// slices is then served by compute_waves(DV) waves.
-#ifndef KDA_SLICES_PER_WAVE
-#define KDA_SLICES_PER_WAVE 1
-#endif
-constexpr int kSlicesPerWave = KDA_SLICES_PER_WAVE;
-__host__ __device__ constexpr int compute_waves(int DV) {
-    return (group_slices(DV) + kSlicesPerWave - 1) / kSlicesPerWave;
-}
 
 // Copy the 1 KiB units first, first + step, ... of `bytes` (a multiple of
 // 1 KiB) from global to LDS, 16 bytes per lane per instruction.
@@ -727,21 +737,24 @@ __device__ __forceinline__ void dma_to_lds(const char* src, char* dst, int64_t b
         __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + off + lane * 16), (lds_void_t*)(dst + off), 16, 0, 0);
 }
 
-template <int DK, int C, typename In>
-__global__ __launch_bounds__(64 * ((kGroupSlices + kSlicesPerWave - 1) / kSlicesPerWave + kIoWaves))
+template <int DK, int C, typename In, bool kGate>
+__global__ __launch_bounds__(64 * (Inter<DK, C, typename OperandOf<In>::type, kGate>::kMaxCompute + kIoWaves))
 void kda_inter_kernel(const PrefillArgs a) {
     using T = typename OperandOf<In>::type;
     using Q = quad_t<T>;
-    using X = Inter<DK, C, T>;
+    using X = Inter<DK, C, T, kGate>;
     static_assert(X::kFits, "LDS ring of the inter-chunk kernel exceeds one workgroup");
-    constexpr int NB = C / 16, NQK = DK / 16;
+    constexpr int NB = C / 16, NQK = DK / 16, SPW = X::SPW;
     __shared__ __attribute__((aligned(1024))) char ring[2 * X::kBuf];
+    // per-token sums of squares of each compute wave's outputs (double-buffered
+    // by chunk parity) for the output norm of gated calls
+    __shared__ float part[kGate ? 2 : 1][kGate ? X::kMaxCompute : 1][kGate ? C : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, cl = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets go to M0
     const int H = a.H, DV = a.DV;
-    const ChunkBlock<T> cb(DK, C, DV);
-    const int ncw = compute_waves(DV), ngroups = DV / 16 / cb.gsl;
+    const ChunkBlock<T> cb(DK, C, DV, a.gsl);
+    const int ncw = (cb.gsl + SPW - 1) / SPW, ngroups = DV / 16 / cb.gsl;
     // blocks are dealt round-robin over the 8 XCDs: keep the slice groups of
     // one (sequence, head) on one XCD so they share its L2
     const int b = blockIdx.x, xcd = b & 7, jx = b >> 3;
@@ -782,21 +795,54 @@ void kda_inter_kernel(const PrefillArgs a) {
         return;
     }
 
-    // ---- compute waves: NTW value slices (16 columns each) per wave ---------------
-    const int s0 = grp * cb.gsl + wave * kSlicesPerWave;   // first value slice of this wave
-    // slices this wave owns (a group may hold fewer than kSlicesPerWave * waves);
-    // the accumulators of a missing slice are computed on stale LDS and never stored
-    const int nsl = min(kSlicesPerWave, cb.gsl - wave * kSlicesPerWave);
+    // ---- compute waves: SPW value slices (16 columns each) per wave ----------------
+    const int s0 = grp * cb.gsl + wave * SPW;   // first value slice of this wave
+    // slices this wave owns (a group may hold fewer than SPW * waves); the
+    // accumulators of a missing slice are computed on stale LDS and never stored
+    const int nsl = min(SPW, cb.gsl - wave * SPW);
     // S slices in accumulator layout: acc[n][t][j] = S[16t + 4g + j][16 (s0 + n) + cl]
-    f32x4 acc[kSlicesPerWave][NQK];
+    f32x4 acc[SPW][NQK];
     const int64_t sbase = (int64_t)unit * DK * DV;
 #pragma unroll
-    for (int n = 0; n < kSlicesPerWave; ++n)
+    for (int n = 0; n < SPW; ++n)
 #pragma unroll
         for (int t = 0; t < NQK; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[n][t][j] = (a.s0 && n < nsl) ? a.s0[sbase + (int64_t)(16 * t + 4 * g + j) * DV + 16 * (s0 + n) + cl] : 0.f;
+
+    // gated calls: a chunk's outputs wait in registers until every wave's
+    // partial sums of squares are in LDS (after the chunk's barrier); the
+    // norm, weight and gate are then applied and the outputs stored
+    f32x4 opend[kGate ? NB : 1][kGate ? SPW : 1];
+    int64_t ptok0 = 0;
+    int pvalid = 0, pbuf = 0;
+    bool pending = false;
+    auto flush = [&]() {
+        if constexpr (kGate) {
+            const In* __restrict__ gt = reinterpret_cast<const In*>(a.gate);
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb) {
+                const int r = 16 * tb + cl;
+                float ss = 0.f;
+                for (int w2 = 0; w2 < ncw; ++w2) ss += part[pbuf][w2][r];
+                const float inv = rsqrtf(ss / (float)DV + a.norm_eps);
+#pragma unroll
+                for (int n = 0; n < SPW; ++n) {
+                    if (r < pvalid && n < nsl) {
+                        const int col = 16 * (s0 + n) + 4 * g;
+                        const int64_t oi = ((ptok0 + r) * H + h) * DV + col;
+                        f32x4 o4 = opend[tb][n] * inv;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            o4[j] *= (a.norm_w ? a.norm_w[col + j] : 1.f) * sigmoid(load_as_float(gt, oi + j));
+                        if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + oi, o4);
+                        else store4(reinterpret_cast<__bf16*>(a.o) + oi, o4);
+                    }
+                }
+            }
+        }
+    };
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     for (int x = c_begin; x < c_end; ++x) {
@@ -810,21 +856,22 @@ void kda_inter_kernel(const PrefillArgs a) {
         const char* Pl = buf + cb.p;
         const float* gl = reinterpret_cast<const float*>(buf + cb.gam);
         const T* Ul = reinterpret_cast<const T*>(buf + X::kShared + (s0 - grp * cb.gsl) * cb.slice);
+        if (kGate && pending) flush();   // the previous chunk: its partial sums are complete
 
-        Q sb[kSlicesPerWave][NQK];
+        Q sb[SPW][NQK];
 #pragma unroll
-        for (int n = 0; n < kSlicesPerWave; ++n)
+        for (int n = 0; n < SPW; ++n)
 #pragma unroll
             for (int t = 0; t < NQK; ++t) sb[n][t] = make_quad<T>(acc[n][t]);
 
         // U = Utilde - W S   (lane: tokens 16tb + 4g + j, column of slice n)
-        Q ub[kSlicesPerWave][NB];
+        Q ub[SPW][NB];
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
             Q wq[NQK];
             load_frag(wq, Wl, tb, lane);
 #pragma unroll
-            for (int n = 0; n < kSlicesPerWave; ++n) {
+            for (int n = 0; n < SPW; ++n) {
                 const f32x4 xw = mma_quads(wq, sb[n], zero4());
                 const f32x4 ut = from_quad(*reinterpret_cast<const Q*>(Ul + n * (cb.slice / sizeof(T)) + (lane * NB + tb) * 4));
                 ub[n][tb] = make_quad<T>(ut - xw);
@@ -837,7 +884,7 @@ void kda_inter_kernel(const PrefillArgs a) {
             Q kq[NB];
             load_frag(kq, Kl, t, lane);
 #pragma unroll
-            for (int n = 0; n < kSlicesPerWave; ++n) acc[n][t] = mma_quads(kq, ub[n], acc[n][t] * gv);
+            for (int n = 0; n < SPW; ++n) acc[n][t] = mma_quads(kq, ub[n], acc[n][t] * gv);
         }
         // state checkpoint: S after the first (jc + 1) C tokens when that is a
         // multiple of ckpt_every inside the sequence (a full chunk)
@@ -846,7 +893,7 @@ void kda_inter_kernel(const PrefillArgs a) {
             if (done <= seq_len && done % a.ckpt_every == 0 && done / a.ckpt_every <= a.max_ckpts) {
                 float* cp = a.ckpt + (((int64_t)seq * a.max_ckpts + done / a.ckpt_every - 1) * H + h) * DK * DV;
 #pragma unroll
-                for (int sl = 0; sl < kSlicesPerWave; ++sl)
+                for (int sl = 0; sl < SPW; ++sl)
                     if (sl < nsl)
 #pragma unroll
                         for (int t = 0; t < NQK; ++t)
@@ -862,24 +909,40 @@ void kda_inter_kernel(const PrefillArgs a) {
             load_frag(qq, Ql, tb, lane);
             load_frag(pq, Pl, tb, lane);
             const int r = 16 * tb + cl;
+            float ss = 0.f;
 #pragma unroll
-            for (int n = 0; n < kSlicesPerWave; ++n) {
+            for (int n = 0; n < SPW; ++n) {
                 // two chains summed on the VALU: with dk or C of 16 one of them is a
                 // single K=16 step, which must not accumulate onto a K=32 result
                 const f32x4 ot = mma_quads(sb[n], qq, zero4()) + mma_quads_upto(ub[n], pq, tb, zero4());
-                if (r < valid && n < nsl) {
-                    const f32x4 sc = ot * a.scale;
+                const f32x4 sc = ot * a.scale;
+                if constexpr (kGate) {
+                    opend[tb][n] = sc;
+                    if (n < nsl) ss += sc[0] * sc[0] + sc[1] * sc[1] + sc[2] * sc[2] + sc[3] * sc[3];
+                } else if (r < valid && n < nsl) {
                     const int64_t oi = ((tok0 + r) * H + h) * DV + 16 * (s0 + n) + 4 * g;
                     if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + oi, sc);
                     else store4(reinterpret_cast<__bf16*>(a.o) + oi, sc);
                 }
             }
+            if constexpr (kGate) {   // this wave's columns of token r: lanes cl, cl + 16, cl + 32, cl + 48
+                ss += __shfl_xor(ss, 16, 64);
+                ss += __shfl_xor(ss, 32, 64);
+                if (g == 0) part[jc & 1][wave][r] = ss;
+            }
+        }
+        if constexpr (kGate) {
+            ptok0 = tok0;
+            pvalid = valid;
+            pbuf = jc & 1;
+            pending = true;
         }
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
+    if (kGate && pending) flush();   // the last chunk, past its barrier
     if (a.s_final) {
 #pragma unroll
-        for (int n = 0; n < kSlicesPerWave; ++n)
+        for (int n = 0; n < SPW; ++n)
             if (n < nsl)
 #pragma unroll
             for (int t = 0; t < NQK; ++t)
@@ -895,18 +958,31 @@ void kda_inter_kernel(const PrefillArgs a) {
 template <int DK, int C, typename In>
 static hipError_t launch_phase_t(const PrefillArgs& a, int max_chunks, bool intra, hipStream_t stream) {
     if constexpr (!Intra<DK, C, typename OperandOf<In>::type>::kFits ||
-                  !Inter<DK, C, typename OperandOf<In>::type>::kFits) {
+                  !Inter<DK, C, typename OperandOf<In>::type>::kFits ||
+                  !Inter<DK, C, typename OperandOf<In>::type, true>::kFits) {
         return hipErrorInvalidValue;  // effective_chunk() never selects this
     } else {
         if (intra) {
             if (max_chunks > 0) {
-                hipLaunchKernelGGL((kda_intra_kernel<DK, C, In>), dim3(max_chunks, a.H), dim3(256), 0, stream, a);
+                if (a.alpha_scalar || a.fuse_inputs || a.alpha_floor != 0.f)
+                    hipLaunchKernelGGL((kda_intra_kernel<DK, C, In, true>), dim3(max_chunks, a.H), dim3(256), 0,
+                                       stream, a);
+                else
+                    hipLaunchKernelGGL((kda_intra_kernel<DK, C, In, false>), dim3(max_chunks, a.H), dim3(256), 0,
+                                       stream, a);
             }
         } else {
             const int units = a.N * a.H;
-            const int blocks = ((units + 7) / 8) * 8 * (a.DV / 16 / group_slices(a.DV));
-            hipLaunchKernelGGL((kda_inter_kernel<DK, C, In>), dim3(blocks), dim3(64 * (compute_waves(a.DV) + kIoWaves)),
-                               0, stream, a);
+            const int blocks = ((units + 7) / 8) * 8 * (a.DV / 16 / a.gsl);
+            if (a.gate) {
+                constexpr int spw = Inter<DK, C, typename OperandOf<In>::type, true>::SPW;
+                hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, true>), dim3(blocks),
+                                   dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
+            } else {
+                constexpr int spw = Inter<DK, C, typename OperandOf<In>::type, false>::SPW;
+                hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, false>), dim3(blocks),
+                                   dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
+            }
         }
         return hipGetLastError();
     }
@@ -934,7 +1010,8 @@ static hipError_t launch_phase_k(const PrefillArgs& a, int DK, int C, int max_ch
 }
 
 template <typename T> static bool fits(int DK, int C) {
-#define KDA_FITS_CASE(D, CC) if (DK == D && C == CC) return Intra<D, CC, T>::kFits && Inter<D, CC, T>::kFits;
+#define KDA_FITS_CASE(D, CC) \
+    if (DK == D && C == CC) return Intra<D, CC, T>::kFits && Inter<D, CC, T>::kFits && Inter<D, CC, T, true>::kFits;
     KDA_FITS_CASE(16, 16) KDA_FITS_CASE(16, 32) KDA_FITS_CASE(16, 64)
     KDA_FITS_CASE(32, 16) KDA_FITS_CASE(32, 32) KDA_FITS_CASE(32, 64)
     KDA_FITS_CASE(64, 16) KDA_FITS_CASE(64, 32) KDA_FITS_CASE(64, 64)
@@ -962,8 +1039,10 @@ hipError_t launch_inter(const PrefillArgs& a, int DK, int C, bool bf16, hipStrea
     return bf16 ? launch_phase_k<__bf16>(a, DK, C, 0, false, s) : launch_phase_k<float>(a, DK, C, 0, false, s);
 }
 
-int64_t chunk_block_bytes(int DK, int C, int DV, bool bf16) {
-    return bf16 ? ChunkBlock<_Float16>(DK, C, DV).bytes : ChunkBlock<float>(DK, C, DV).bytes;
+int slice_group(int DV, bool gate) { return gate ? DV / 16 : group_slices(DV); }
+
+int64_t chunk_block_bytes(int DK, int C, int DV, bool bf16, int gsl) {
+    return bf16 ? ChunkBlock<_Float16>(DK, C, DV, gsl).bytes : ChunkBlock<float>(DK, C, DV, gsl).bytes;
 }
 
 }  // namespace kda

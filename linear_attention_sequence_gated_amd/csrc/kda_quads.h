@@ -153,7 +153,7 @@ __host__ __device__ constexpr int group_slices(int DV) { return DV / 16 < kGroup
 template <typename T> struct ChunkBlock {
     int64_t w, q, kb, p, gam, shared, u, slice, group, bytes;
     int gsl;
-    __host__ __device__ ChunkBlock(int DK, int C, int DV) {
+    __host__ __device__ ChunkBlock(int DK, int C, int DV, int slices_per_group) {
         const int64_t s = sizeof(T);
         w = 0;                                   // W = T Ktilde      : C x DK frag
         q = w + Frag<T>::elems(C, DK) * s;       // Qtilde            : C x DK frag
@@ -161,7 +161,7 @@ template <typename T> struct ChunkBlock {
         p = kb + Frag<T>::elems(DK, C) * s;      // P (as P^T B-frag) : C x C frag
         gam = p + Frag<T>::elems(C, C) * s;      // gamma_C           : DK fp32
         shared = gam + round_kib((int64_t)DK * 4);
-        gsl = group_slices(DV);
+        gsl = slices_per_group;
         slice = (int64_t)C * 16 * s;             // Utilde slice      : [64 lanes][C/16][4]
         group = round_kib(gsl * slice);
         u = shared;

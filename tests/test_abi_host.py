@@ -129,6 +129,8 @@ def test_chunk_fwd_ex_rejects_bad_options_before_launch(lib):
     assert _fwd_ex(lib, p, Opt(alpha_mode=2)) == INVALID
     assert _fwd_ex(lib, p, Opt(fuse_inputs=5)) == INVALID
     assert _fwd_ex(lib, p, Opt(norm_weight=0x300000)) == INVALID        # a norm weight needs a gate
+    assert _fwd_ex(lib, p, Opt(gate=0x300001)) == INVALID                # misaligned gate
+    assert _fwd_ex(lib, p, Opt(gate=0x300000, norm_eps=-1.0)) == INVALID
 
 
 def test_decode_step_rejects_before_launch(lib):

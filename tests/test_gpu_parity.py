@@ -560,3 +560,52 @@ def test_prefill_options_with_checkpoints():
     eo, es = rel_err(o.cpu().numpy(), oo), rel_err(S.cpu().numpy(), So)
     say(f"    err ckpt={worst:.3e} o={eo:.3e} S={es:.3e}")
     assert worst < 2e-2 and eo < 2e-2 and es < 2e-2
+
+
+# --- output norm and gate inside the inter-chunk kernel -------------------------
+
+def _gate_case(inp, chunk, tol, label, o_dtype=torch.float32, **opts):
+    say(f"[case] prefill gate {label} chunk={chunk} {inp['q'].dtype} {opts}")
+    g = torch.Generator().manual_seed(int(inp["q"].shape[1]) + chunk)
+    gate = torch.randn(inp["v"].shape, generator=g).to(inp["q"].dtype)
+    w = torch.rand(inp["v"].shape[-1], generator=g) + 0.5
+    eps = 1e-5
+    d = to_dev(inp)
+    o, S = kda.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"],
+                         chunk_size=chunk, o_dtype=o_dtype, gate=gate.cuda(), norm_weight=w.cuda(), norm_eps=eps,
+                         **opts)
+    torch.cuda.synchronize()
+    cu = inp["cu_seqlens"]
+    oo, So = kda_oracle.forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0=inp["S0"],
+                                cu_seqlens=None if cu is None else cu.to(torch.int64), gate=gate, norm_weight=w,
+                                norm_eps=eps, **opts)
+    eo, es = rel_err(o.float().cpu().numpy(), oo), rel_err(S.cpu().numpy(), So)
+    say(f"    err o={eo:.3e} S={es:.3e} (tol {tol})")
+    assert eo < tol and es < tol
+    return o
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_prefill_gate_packed(dtype):
+    lens = [1, 63, 64, 65, 150, 7]
+    inp = workloads.make_inputs(1, 0, 2, 128, 128, dtype, s0_std=0.02, seed=501, lengths=lens)
+    _gate_case(inp, 64, TOL[dtype], f"packed {lens}")
+
+
+@pytest.mark.parametrize("dv,chunk", [(16, 32), (32, 16), (64, 64)])
+def test_prefill_gate_shapes(dv, chunk):
+    inp = workloads.make_inputs(2, 130, 3, 64, dv, torch.bfloat16, s0_std=0.02, seed=502 + dv)
+    _gate_case(inp, chunk, TOL[torch.bfloat16], f"B2 T130 dk64 dv{dv}")
+
+
+def test_prefill_gate_with_fused_inputs():
+    opts = {"fuse_inputs": True, "decay_floor": 0.5}
+    inp = _prefill_opts_inputs(1, 200, 2, 128, 128, torch.bfloat16, seed=503, **opts)
+    _gate_case(inp, 64, TOL[torch.bfloat16], "B1 T200 fused", **opts)
+
+
+def test_prefill_gate_bf16_output_is_rounded_fp32():
+    inp = workloads.make_inputs(1, 100, 2, 128, 128, torch.bfloat16, s0_std=0.02, seed=504)
+    o32 = _gate_case(inp, 64, TOL[torch.bfloat16], "fp32 out").cpu()
+    o16 = _gate_case(inp, 64, 4e-2, "bf16 out", o_dtype=torch.bfloat16).cpu()
+    assert torch.equal(o16.view(torch.int16), o32.to(torch.bfloat16).view(torch.int16))
