@@ -12,8 +12,9 @@ timed region starts.
 
 The line also carries the roofline of the dominant kernel (algorithmic bytes
 or flops per launch / measured average launch time, against MI355X peaks),
-the same for every kernel, and the fp64 CPU oracle timed on a bounded sample
-of the workload on this host.
+the same for every kernel, the fp64 CPU oracle timed on a bounded sample of
+the workload on this host, and ("variants") the time of one call with each
+option of kda_chunk_fwd_ex / kda_decode_step_ex on the same workloads.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -121,6 +122,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true", help="skip the timing of the option variants")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration runs)")
     args = ap.parse_args()
@@ -186,6 +188,54 @@ def main():
     t_in, t_out = traffic("kda_intra_kernel"), traffic("kda_inter_kernel")
     step_roof = roof("hbm", step_bytes, step_ms / 1e3, "GB/s", "kda_chunk_fwd (whole step)",
                      t_in + t_out if t_in is not None and t_out is not None else None)
+    # ---- prefill variants (kda_chunk_fwd_ex options), whole call ----------------
+    variants = {}
+    if not args.no_variants:
+        def time_call(fn, reps=5):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        log("timing prefill variants")
+        g = torch.Generator(device=dev).manual_seed(7)
+        base = dict(chunk_size=w.chunk, o_dtype=torch.bfloat16, o=pre.o, final_state=pre.final_state)
+        args0 = (d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"])
+
+        def time_variant(inputs, **opts):   # one marshalled call per variant, its own workspace
+            pv = kda.Prefill(*inputs, **base, **opts)
+            ms = time_call(pv.run)
+            del pv
+            return ms
+
+        plain_ms = time_variant(args0)
+        variants["prefill_plain"] = {"ms": round(plain_ms, 4)}
+        every = 4096
+        ck = torch.empty((w.batch, w.seqlen // every, w.heads, w.dk, w.dv), dtype=torch.float32, device=dev)
+        ms = time_variant(args0, checkpoints=ck, ckpt_every=every)
+        variants["prefill_checkpoints"] = {"ms": round(ms, 4), "every_tokens": every,
+                                           "checkpoints": ck.shape[1], "vs_plain": round(ms / plain_ms, 4)}
+        gate = torch.randn(d["v"].shape, generator=g, device=dev).to(d["v"].dtype)
+        wn = torch.ones(w.dv, device=dev)
+        ms = time_variant(args0, gate=gate, norm_weight=wn, norm_eps=1e-5)
+        variants["prefill_output_gate"] = {"ms": round(ms, 4), "vs_plain": round(ms / plain_ms, 4)}
+        al = torch.randn(d["alpha"].shape, generator=g, device=dev) + 4.0
+        bl = torch.randn(d["beta"].shape, generator=g, device=dev)
+        argsf = (d["q"], d["k"], d["v"], al, bl, d["S0"], d["cu_seqlens"])
+        ms = time_variant(argsf, fuse_inputs=True, gate=gate, norm_weight=wn, norm_eps=1e-5)
+        variants["prefill_fused_inputs_and_gate"] = {"ms": round(ms, 4), "vs_plain": round(ms / plain_ms, 4)}
+        a_s = d["alpha"][..., 0].contiguous()
+        argss = (d["q"], d["k"], d["v"], a_s, d["beta"], d["S0"], d["cu_seqlens"])
+        ms = time_variant(argss, alpha_scalar=True)
+        variants["prefill_scalar_gate"] = {"ms": round(ms, 4), "vs_plain": round(ms / plain_ms, 4)}
+        ms = time_variant(args0, decay_floor=0.6)
+        variants["prefill_decay_floor"] = {"ms": round(ms, 4), "floor": 0.6, "vs_plain": round(ms / plain_ms, 4)}
+        del ck, gate, al, bl, a_s
     del pre, d
     torch.cuda.empty_cache()
 
@@ -226,6 +276,37 @@ def main():
         "tokens_per_s": round(wd.decode_seqs / (dec_ms / 1e3), 1),
         "roofline": dec_roof,
     }
+    if not args.no_variants:
+        log("timing decode variants")
+        N0, H0 = wd.decode_seqs, wd.heads
+        pool = torch.empty((2 * N0, H0, wd.dk, wd.dv), dtype=torch.float32, device=dev)
+        pool[1::2].copy_(dd["S0"])
+        slots = torch.arange(1, 2 * N0, 2, dtype=torch.int32, device=dev)
+        gate = torch.zeros(dd["v"].shape[1:], dtype=dd["v"].dtype, device=dev)
+        wn = torch.ones(wd.dv, device=dev)
+
+        def dtime(fn, reps=min(32, args.decode_steps)):
+            for t in range(min(3, reps)):
+                fn(t)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for t in range(reps):
+                fn(t)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        ms = dtime(lambda t: kda.decode_step(dd["q"][t], dd["k"][t], dd["v"][t], dd["alpha"][t], dd["beta"][t],
+                                             pool, o=o_dec, o_dtype=torch.bfloat16, state_slots=slots))
+        variants["decode_paged_pool"] = {"ms": round(ms, 4), "vs_plain": round(ms / dec_ms, 4),
+                                         "GB/s": round(state_bytes / (ms / 1e3) / 1e9, 1)}
+        ms = dtime(lambda t: kda.decode_step(dd["q"][t], dd["k"][t], dd["v"][t], dd["alpha"][t], dd["beta"][t],
+                                             pool, o=o_dec, o_dtype=torch.bfloat16, state_slots=slots,
+                                             fuse_inputs=True, gate=gate, norm_weight=wn, norm_eps=1e-5))
+        variants["decode_paged_fused_inputs_and_gate"] = {"ms": round(ms, 4), "vs_plain": round(ms / dec_ms, 4),
+                                                          "GB/s": round(state_bytes / (ms / 1e3) / 1e9, 1)}
+        del pool, slots, gate
     del dd, state
     torch.cuda.empty_cache()
 
@@ -282,6 +363,7 @@ def main():
         "kernels": kernels,
         "decode": decode,
         "cpu_baseline": cpu,
+        "variants": variants or None,
         "copy_calibration": calib,
         "wall_s_timed_region": round(wall, 4),
     }

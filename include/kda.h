@@ -185,9 +185,18 @@ typedef struct {
     float norm_eps;
 } kda_chunk_options_t;
 
+/* Workspace bytes kda_chunk_fwd_ex needs for `params` with `options` (NULL:
+ * as kda_chunk_fwd_workspace_size).  A gate adds scratch for un-normalised
+ * fp32 outputs and per-slice sums of squares (about (dv + dv/16) * 4 bytes
+ * per token and head), used when there are fewer (sequence, head) pairs than
+ * compute units: the norm is then finished by a small epilogue kernel instead
+ * of inside the inter-chunk kernel. */
+kda_status_t kda_chunk_fwd_ex_workspace_size(const kda_chunk_params_t* params, const kda_chunk_options_t* options,
+                                             size_t* bytes);
+
 /* kda_chunk_fwd with the options above (NULL options = kda_chunk_fwd).  The
- * workspace is the one kda_chunk_fwd_workspace_size quotes (it covers every
- * option).  Errors as kda_chunk_fwd, plus KDA_ERR_INVALID_ARG for bad option
+ * workspace must hold kda_chunk_fwd_ex_workspace_size bytes for the same
+ * options.  Errors as kda_chunk_fwd, plus KDA_ERR_INVALID_ARG for bad option
  * values (negative or NaN floor or eps, a norm weight without a gate,
  * misaligned option pointers, bad checkpoint layout). */
 kda_status_t kda_chunk_fwd_ex(const kda_chunk_params_t* params, const kda_chunk_options_t* options,

@@ -23,7 +23,8 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "
 
 # Every symbol include/kda.h declares.
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
-            "kda_chunk_fwd_inter", "kda_chunk_fwd_ex", "kda_decode_step", "kda_decode_step_ex")
+            "kda_chunk_fwd_inter", "kda_chunk_fwd_ex", "kda_chunk_fwd_ex_workspace_size", "kda_decode_step",
+            "kda_decode_step_ex")
 
 
 class KdaError(RuntimeError):
@@ -79,6 +80,9 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [ctypes.POINTER(ChunkParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kda_chunk_fwd_ex_workspace_size.restype = ctypes.c_int
+    lib.kda_chunk_fwd_ex_workspace_size.argtypes = [ctypes.POINTER(ChunkParams), ctypes.POINTER(ChunkOptions),
+                                                    ctypes.POINTER(sz)]
     lib.kda_chunk_fwd_ex.restype = ctypes.c_int
     lib.kda_chunk_fwd_ex.argtypes = [ctypes.POINTER(ChunkParams), ctypes.POINTER(ChunkOptions),
                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -177,10 +181,7 @@ class Prefill:
         if final_state is None and output_final_state:
             final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
         self.params = chunk_params(q, v, cu_seqlens, chunk_size, scale, o_dtype)
-        need = workspace_size(q, v, cu_seqlens, chunk_size, scale)
-        if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-        self.o, self.final_state, self.workspace = o, final_state, workspace
+        self.o, self.final_state = o, final_state
         self.options = None
         self.checkpoints = checkpoints
         if ckpt_every:
@@ -203,6 +204,14 @@ class Prefill:
                                         gate=None if gate is None else gate.data_ptr(),
                                         norm_weight=None if norm_weight is None else norm_weight.data_ptr(),
                                         norm_eps=float(norm_eps))
+        out = ctypes.c_size_t(0)
+        _check("kda_chunk_fwd_ex_workspace_size",
+               load().kda_chunk_fwd_ex_workspace_size(ctypes.byref(self.params),
+                                                      None if self.options is None else ctypes.byref(self.options),
+                                                      ctypes.byref(out)))
+        if workspace is None:
+            workspace = torch.empty(max(out.value, 1), dtype=torch.uint8, device=q.device)
+        self.workspace = workspace
         self._keep = (q, k, v, alpha, beta, initial_state, cu_seqlens, checkpoints, gate, norm_weight)
         self._args = (ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                       _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(final_state), _ptr(workspace),

@@ -58,6 +58,24 @@ PrefillPlan plan_prefill(const kda_chunk_params_t* p, bool packed, bool gate) {
     return pl;
 }
 
+// Scratch of gated calls whose norm is finished by the epilogue kernel:
+// un-normalised fp32 outputs and per-slice sums of squares.
+size_t gate_scratch_bytes(const kda_chunk_params_t* p) {
+    const size_t rows = (size_t)p->batch * (size_t)p->seqlen * (size_t)p->num_heads;
+    return round_up(rows * (size_t)p->head_dim_v * 4, kWsAlign) +
+           round_up(rows * (size_t)(p->head_dim_v / 16) * 4, kWsAlign);
+}
+
+size_t base_workspace(const kda_chunk_params_t* p) {
+    size_t most = 0;
+    for (int packed = 0; packed < 2; ++packed)
+        for (int gate = 0; gate < 2; ++gate) {
+            const PrefillPlan pl = plan_prefill(p, packed, gate);
+            most = pl.total > most ? pl.total : most;
+        }
+    return most;
+}
+
 }  // namespace
 
 extern "C" {
@@ -79,13 +97,16 @@ kda_status_t kda_chunk_fwd_workspace_size(const kda_chunk_params_t* p, size_t* b
     if (st != KDA_OK) return st;
     // the size is quoted for the worst case of either layout so that one
     // buffer serves packed and fixed-length calls of the same shape
-    size_t most = 0;
-    for (int packed = 0; packed < 2; ++packed)
-        for (int gate = 0; gate < 2; ++gate) {
-            const PrefillPlan pl = plan_prefill(p, packed, gate);
-            most = pl.total > most ? pl.total : most;
-        }
-    *bytes = most;
+    *bytes = base_workspace(p);
+    return KDA_OK;
+}
+
+kda_status_t kda_chunk_fwd_ex_workspace_size(const kda_chunk_params_t* p, const kda_chunk_options_t* options,
+                                             size_t* bytes) {
+    if (!bytes) return KDA_ERR_INVALID_ARG;
+    const kda_status_t st = check_params(p);
+    if (st != KDA_OK) return st;
+    *bytes = base_workspace(p) + (options && options->gate ? gate_scratch_bytes(p) : 0);
     return KDA_OK;
 }
 
@@ -154,10 +175,12 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
         if (overlaps(initial_state, sb, final_state, sb)) return KDA_ERR_INVALID_ARG;
     }
     const bool gate = op && op->gate;
-    const PrefillPlan pl = plan_prefill(p, packed, gate);
-    if (pl.total > 0) {
+    const bool split = gate && kda::gate_split((int64_t)p->num_seqs * p->num_heads);
+    const PrefillPlan pl = plan_prefill(p, packed, gate && !split);
+    const size_t need = round_up(pl.total, kWsAlign) + (split ? gate_scratch_bytes(p) : 0);
+    if (need > 0) {
         if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_WORKSPACE;
-        if (workspace_bytes < pl.total) return KDA_ERR_WORKSPACE;
+        if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
     }
     if (!final_state && !has_tokens) return KDA_OK;  // nothing to compute or write (no checkpoint is reached)
 
@@ -194,7 +217,14 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
         a.norm_w = op->norm_weight;
         a.norm_eps = op->norm_eps;
     }
-    a.gsl = kda::slice_group(p->head_dim_v, gate);
+    a.gsl = kda::slice_group(p->head_dim_v, gate && !split);
+    const int64_t rows = (int64_t)p->batch * p->seqlen * p->num_heads;
+    if (split) {
+        a.gate_split = 1;
+        a.o_scratch = reinterpret_cast<float*>(ws + round_up(pl.total, kWsAlign));
+        a.part_scratch = reinterpret_cast<float*>(reinterpret_cast<char*>(a.o_scratch) +
+                                                  round_up((size_t)rows * p->head_dim_v * 4, kWsAlign));
+    }
     const bool bf16 = p->qkv_dtype == KDA_DTYPE_BF16;
 
     hipError_t e = hipSuccess;
@@ -209,6 +239,10 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
     if (phases & kInter) {
         e = kda::launch_inter(a, p->head_dim_k, C, bf16, s);
         if (e != hipSuccess) return KDA_ERR_HIP;
+        if (split) {
+            e = kda::launch_gate_epilogue(a, rows, bf16, s);
+            if (e != hipSuccess) return KDA_ERR_HIP;
+        }
     }
     return KDA_OK;
 }

@@ -34,6 +34,9 @@ struct PrefillArgs {
     const float* norm_w;         // [dv] or null
     float norm_eps;
     int32_t gsl;                 // value slices per slice group (slice_group())
+    int32_t gate_split;          // gated output through o_scratch + part_scratch and an epilogue
+    float* o_scratch;            // [B*T*H, dv] un-normalised outputs (split gate)
+    float* part_scratch;         // [B*T*H, dv/16] per-slice sums of squares (split gate)
 };
 
 struct DecodeArgs {
@@ -70,6 +73,10 @@ int decode_columns(int DV);
 // workspace): all dv / 16 when the output gate is fused (it needs a token's
 // whole row in one workgroup), else the plain grouping.
 int slice_group(int DV, bool gate);
+// Gated calls with fewer (sequence, head) units than the device has CUs keep
+// one slice per workgroup and finish the norm in an epilogue kernel.
+bool gate_split(int64_t units);
+hipError_t launch_gate_epilogue(const PrefillArgs& a, int64_t rows, bool bf16, hipStream_t s);
 int64_t chunk_block_bytes(int DK, int C, int DV, bool bf16, int gsl);
 
 }  // namespace kda

@@ -737,9 +737,16 @@ __device__ __forceinline__ void dma_to_lds(const char* src, char* dst, int64_t b
         __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + off + lane * 16), (lds_void_t*)(dst + off), 16, 0, 0);
 }
 
-template <int DK, int C, typename In, bool kGate>
-__global__ __launch_bounds__(64 * (Inter<DK, C, typename OperandOf<In>::type, kGate>::kMaxCompute + kIoWaves))
+// Output modes of the inter-chunk kernel.
+enum OutMode { kOutPlain = 0, kOutGate = 1, kOutSplit = 2 };
+
+// kMode kOutPlain: o stored per chunk; kOutGate: all slices of a row in this
+// workgroup, norm and gate applied here; kOutSplit: one-slice workgroups write
+// un-normalised fp32 outputs and per-slice sums of squares for the epilogue.
+template <int DK, int C, typename In, int kMode>
+__global__ __launch_bounds__(64 * (Inter<DK, C, typename OperandOf<In>::type, kMode == kOutGate>::kMaxCompute + kIoWaves))
 void kda_inter_kernel(const PrefillArgs a) {
+    constexpr bool kGate = kMode == kOutGate;
     using T = typename OperandOf<In>::type;
     using Q = quad_t<T>;
     using X = Inter<DK, C, T, kGate>;
@@ -919,6 +926,15 @@ void kda_inter_kernel(const PrefillArgs a) {
                 if constexpr (kGate) {
                     opend[tb][n] = sc;
                     if (n < nsl) ss += sc[0] * sc[0] + sc[1] * sc[1] + sc[2] * sc[2] + sc[3] * sc[3];
+                } else if constexpr (kMode == kOutSplit) {
+                    float sn = sc[0] * sc[0] + sc[1] * sc[1] + sc[2] * sc[2] + sc[3] * sc[3];
+                    sn += __shfl_xor(sn, 16, 64);
+                    sn += __shfl_xor(sn, 32, 64);
+                    if (r < valid && n < nsl) {
+                        const int64_t row = (tok0 + r) * H + h;
+                        *reinterpret_cast<f32x4*>(a.o_scratch + row * DV + 16 * (s0 + n) + 4 * g) = sc;
+                        if (g == 0) a.part_scratch[row * (DV / 16) + s0 + n] = sn;
+                    }
                 } else if (r < valid && n < nsl) {
                     const int64_t oi = ((tok0 + r) * H + h) * DV + 16 * (s0 + n) + 4 * g;
                     if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + oi, sc);
@@ -974,14 +990,18 @@ static hipError_t launch_phase_t(const PrefillArgs& a, int max_chunks, bool intr
         } else {
             const int units = a.N * a.H;
             const int blocks = ((units + 7) / 8) * 8 * (a.DV / 16 / a.gsl);
-            if (a.gate) {
+            if (a.gate && !a.gate_split) {
                 constexpr int spw = Inter<DK, C, typename OperandOf<In>::type, true>::SPW;
-                hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, true>), dim3(blocks),
+                hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutGate>), dim3(blocks),
                                    dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
             } else {
                 constexpr int spw = Inter<DK, C, typename OperandOf<In>::type, false>::SPW;
-                hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, false>), dim3(blocks),
-                                   dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
+                if (a.gate)
+                    hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutSplit>), dim3(blocks),
+                                       dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
+                else
+                    hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutPlain>), dim3(blocks),
+                                       dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
             }
         }
         return hipGetLastError();
@@ -1037,6 +1057,45 @@ hipError_t launch_intra(const PrefillArgs& a, int DK, int C, bool bf16, int max_
 
 hipError_t launch_inter(const PrefillArgs& a, int DK, int C, bool bf16, hipStream_t s) {
     return bf16 ? launch_phase_k<__bf16>(a, DK, C, 0, false, s) : launch_phase_k<float>(a, DK, C, 0, false, s);
+}
+
+// Epilogue of split gated calls: one thread per (row = token * H + head, 4
+// columns); the per-slice sums of squares are added in a fixed order.
+template <typename In>
+__global__ __launch_bounds__(256) void kda_gate_epilogue(const PrefillArgs a, const int64_t rows) {
+    const int DV = a.DV, CG = DV / 4, NS = DV / 16;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = t / CG;
+    if (row >= rows) return;
+    const int c4 = (int)(t % CG) * 4;
+    const float* ps = a.part_scratch + row * NS;
+    float ss = 0.f;
+    for (int sl = 0; sl < NS; ++sl) ss += ps[sl];
+    const float inv = rsqrtf(ss / (float)DV + a.norm_eps);
+    f32x4 o4 = *reinterpret_cast<const f32x4*>(a.o_scratch + row * DV + c4) * inv;
+    const In* __restrict__ gt = reinterpret_cast<const In*>(a.gate) + row * DV + c4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o4[j] *= (a.norm_w ? a.norm_w[c4 + j] : 1.f) * sigmoid(load_as_float(gt, j));
+    if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + row * DV + c4, o4);
+    else store4(reinterpret_cast<__bf16*>(a.o) + row * DV + c4, o4);
+}
+
+hipError_t launch_gate_epilogue(const PrefillArgs& a, int64_t rows, bool bf16, hipStream_t s) {
+    const int64_t threads = rows * (a.DV / 4);
+    if (threads <= 0) return hipSuccess;
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    if (bf16) hipLaunchKernelGGL(kda_gate_epilogue<__bf16>, dim3((unsigned)blocks), dim3(256), 0, s, a, rows);
+    else hipLaunchKernelGGL(kda_gate_epilogue<float>, dim3((unsigned)blocks), dim3(256), 0, s, a, rows);
+    return hipGetLastError();
+}
+
+bool gate_split(int64_t units) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    return units < cus;
 }
 
 int slice_group(int DV, bool gate) { return gate ? DV / 16 : group_slices(DV); }

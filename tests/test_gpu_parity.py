@@ -609,3 +609,10 @@ def test_prefill_gate_bf16_output_is_rounded_fp32():
     o32 = _gate_case(inp, 64, TOL[torch.bfloat16], "fp32 out").cpu()
     o16 = _gate_case(inp, 64, 4e-2, "bf16 out", o_dtype=torch.bfloat16).cpu()
     assert torch.equal(o16.view(torch.int16), o32.to(torch.bfloat16).view(torch.int16))
+
+
+def test_prefill_gate_many_units_fused_in_inter_kernel():
+    # at least as many (sequence, head) pairs as CUs: the whole-row workgroups
+    # apply the norm and gate inside the inter-chunk kernel
+    inp = workloads.make_inputs(64, 70, 4, 64, 64, torch.bfloat16, s0_std=0.02, seed=505)
+    _gate_case(inp, 32, TOL[torch.bfloat16], "B64 H4 (256 units)")
