@@ -40,8 +40,18 @@ constexpr float kFastRange = 12.f;
 #ifndef KDA_LATE_V
 #define KDA_LATE_V 1
 #endif
+#ifndef KDA_WU_UNROLL
+#define KDA_WU_UNROLL 1
+#endif
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+
+// Workgroup barrier for LDS producer/consumer hand-offs only.  __syncthreads
+// also waits for every outstanding global load and store of the wave (vmcnt),
+// which would expose the workspace stores and the early v loads of the
+// intra-chunk kernel at each phase boundary; no thread there reads global
+// memory another thread of the kernel writes.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // alpha of (token row tok, head h, key channel c) as the recurrence uses it:
 // per channel or one per (token, head), through a sigmoid for fused inputs,
@@ -142,8 +152,8 @@ template <int DK, int C, typename T> struct Intra {
     static constexpr int kDvMax = 128;
     static constexpr size_t a16(size_t x) { return (x + 15) / 16 * 16; }
     static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
-    // region 1, in turn: segment sums -> {Ak, Aq, Bd} -> {P, MX, Tm, XD} -> {P, VT, Tm}
-    static constexpr size_t kSeg = (size_t)NSEG * DK * 4;
+    // region 1, in turn: fused-input norms -> {Ak, Aq, Bd} -> {P, MX, Tm, XD} -> {P, VT, Tm}
+    static constexpr size_t kSeg = 8ull * C * 4;   // per-wave partial norms of the fused inputs
     static constexpr size_t kTile = (size_t)C * LD_ROW * sizeof(T);
     static constexpr size_t kMat = (size_t)C * LD_F * 4;
     static constexpr size_t oP = 0, oMX = kMat, oY = 2 * kMat;   // oY: end of P and MX
@@ -175,7 +185,6 @@ void kda_intra_kernel(const PrefillArgs a) {
     using Q = quad_t<T>;
     constexpr int NB = I::NB, NQK = I::NQK, LD_ROW = I::LD_ROW, LD_CT = I::LD_CT, LD_F = I::LD_F;
     __shared__ __attribute__((aligned(16))) char smem[I::kLds];
-    float* seg = reinterpret_cast<float*>(smem);             // [NSEG][DK]
     T* Ak = reinterpret_cast<T*>(smem);                       // [C][LD_ROW]  row side, k
     T* Aq = Ak + C * LD_ROW;                                  // [C][LD_ROW]  row side, q
     T* Bd = Aq + C * LD_ROW;                                  // [C][LD_ROW]  column side
@@ -213,12 +222,16 @@ void kda_intra_kernel(const PrefillArgs a) {
     float* gam = reinterpret_cast<float*>(blk + cb.gam);
 
     // ---- phase 1: every global load first ------------------------------------
-    // thread -> 4 consecutive tokens (segment sgi, block Rb = sgi/4) x 8 channels
+    // thread -> 8 channels (group cg) x 4 consecutive tokens (segment sgi, block
+    // Rb = sgi/4).  The NSEG segments of a channel group are adjacent lanes of
+    // one wave: the prefix over segments is a shuffle scan, and the transposed
+    // tile stores below (4 tokens of one channel per lane) land in consecutive
+    // quads of a row instead of 8-way bank conflicts.
     const bool p1 = tid < I::NSEG * I::NCG;
-    const int sgi = tid / I::NCG, cg = tid % I::NCG, Rb = sgi >> 2, sp = sgi & 3;
+    const int cg = tid / I::NSEG, sgi = tid % I::NSEG, Rb = sgi >> 2, sp = sgi & 3;
     const int NCGV = DV / 8;
     const bool pv = tid < I::NSEG * NCGV;
-    const int sgv = tid / NCGV, cgv = tid % NCGV;
+    const int cgv = tid / I::NSEG, sgv = tid % I::NSEG;
     float kr[4][8], qr[4][8], al[4][8], vr[4][8];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -263,8 +276,13 @@ void kda_intra_kernel(const PrefillArgs a) {
     };
     if (!KDA_LATE_V) load_v();
     if (kOpts && a.fuse_inputs) {
-        // L2 norm of q and k per token: the NCG lanes of a token are adjacent
-        // lanes of one wave (tid = segment * NCG + channel group)
+        // L2 norm of q and k per token.  The channel groups of a token are the
+        // lanes sgi + NSEG * cg, spread over up to four waves: reduce inside
+        // each wave, then add the waves' partial sums in a fixed order.
+        constexpr int kGroupsPerWave = 64 / I::NSEG;
+        constexpr int kWaves = (I::NCG + kGroupsPerWave - 1) / kGroupsPerWave;
+        float* pnorm = reinterpret_cast<float*>(smem);   // [kWaves][2][C], free until the tiles are written
+        float nq4[4], nk4[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             float nq = 0.f, nk = 0.f;
@@ -274,9 +292,27 @@ void kda_intra_kernel(const PrefillArgs a) {
                 nk += kr[u][e] * kr[u][e];
             }
 #pragma unroll
-            for (int m = 1; m < I::NCG; m <<= 1) {
+            for (int m = I::NSEG; m < 64; m <<= 1) {
                 nq += __shfl_xor(nq, m, 64);
                 nk += __shfl_xor(nk, m, 64);
+            }
+            nq4[u] = nq;
+            nk4[u] = nk;
+        }
+        if (p1 && cg % kGroupsPerWave == 0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                pnorm[(wave * 2 + 0) * C + 4 * sgi + u] = nq4[u];
+                pnorm[(wave * 2 + 1) * C + 4 * sgi + u] = nk4[u];
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float nq = 0.f, nk = 0.f;
+            for (int w2 = 0; w2 < kWaves; ++w2) {
+                nq += pnorm[(w2 * 2 + 0) * C + 4 * sgi + u];
+                nk += pnorm[(w2 * 2 + 1) * C + 4 * sgi + u];
             }
             const float iq = 1.f / fmaxf(sqrtf(nq), 1e-12f), ik = 1.f / fmaxf(sqrtf(nk), 1e-12f);
 #pragma unroll
@@ -297,8 +333,10 @@ void kda_intra_kernel(const PrefillArgs a) {
     }
     if (tid == 0) *srange = 0u;
 
-    // segment sums of log2 alpha (floored), then the exclusive prefix per segment
+    // segment sums of log2 alpha (floored), then the exclusive prefix over the
+    // segments of the channel group (a shuffle scan over NSEG adjacent lanes)
     float lg[4][8];  // inclusive running sum inside the segment
+    float off[8], tot[8];
     {
         float run[8];
 #pragma unroll
@@ -310,37 +348,27 @@ void kda_intra_kernel(const PrefillArgs a) {
                 run[e] += fmaxf(__builtin_amdgcn_logf(al[u][e]), kLog2Floor);
                 lg[u][e] = run[e];
             }
-        if (p1) {
-            *reinterpret_cast<f32x4*>(seg + sgi * DK + 8 * cg) = f32x4{run[0], run[1], run[2], run[3]};
-            *reinterpret_cast<f32x4*>(seg + sgi * DK + 8 * cg + 4) = f32x4{run[4], run[5], run[6], run[7]};
-        }
-    }
-    __syncthreads();
-    float off[8], tot[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { off[e] = 0.f; tot[e] = 0.f; }
-    if (p1) {
+        for (int e = 0; e < 8; ++e) {
+            float incl = run[e];
 #pragma unroll
-        for (int s = 0; s < I::NSEG; ++s) {
-            const f32x4 t0 = *reinterpret_cast<const f32x4*>(seg + s * DK + 8 * cg);
-            const f32x4 t1 = *reinterpret_cast<const f32x4*>(seg + s * DK + 8 * cg + 4);
-            const float t[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if (s < sgi) off[e] += t[e];
-                tot[e] += t[e];
+            for (int d = 1; d < I::NSEG; d <<= 1) {
+                const float t = __shfl_up(incl, d, I::NSEG);
+                if (sgi >= d) incl += t;
             }
-        }
-        if (sp == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) Gs[Rb * DK + 8 * cg + e] = off[e] + lg[0][e];
-        }
-        if (sp == 3) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) Ge[Rb * DK + 8 * cg + e] = off[e] + lg[3][e];
+            off[e] = incl - run[e];
+            tot[e] = __shfl(incl, I::NSEG - 1, I::NSEG);
         }
     }
-    __syncthreads();
+    if (p1 && sp == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Gs[Rb * DK + 8 * cg + e] = off[e] + lg[0][e];
+    }
+    if (p1 && sp == 3) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Ge[Rb * DK + 8 * cg + e] = off[e] + lg[3][e];
+    }
+    lds_barrier();
     // block ranges decide the path; pair factors for the off-diagonal tiles
     if (p1 && sp == 0) {
         float mx = 0.f;
@@ -357,7 +385,7 @@ void kda_intra_kernel(const PrefillArgs a) {
         const float hI = 0.5f * (Gs[Ib * DK + c] - Ge[Ib * DK + c]);
         sIR[e] = __builtin_amdgcn_exp2f(fminf(Gs[R * DK + c] - Gs[Ib * DK + c] + hI - hR, 0.f));
     }
-    __syncthreads();
+    lds_barrier();
     const bool fast = __uint_as_float(*srange) <= kFastRange;
 
     // ---- phase 1 (cont.): operand factors, tiles and the workspace quads ----
@@ -445,7 +473,7 @@ void kda_intra_kernel(const PrefillArgs a) {
                       __builtin_amdgcn_exp2f(tot[7])};
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- phase 2: Gram matrices M (strictly lower) and P (lower) ------------
     if (fast) {
@@ -488,7 +516,7 @@ void kda_intra_kernel(const PrefillArgs a) {
                 pres[pi] = mma_quads(aq, bq, zero4());
             }
         }
-        __syncthreads();  // the operand tiles are dead from here on
+        lds_barrier();  // the operand tiles are dead from here on
 #pragma unroll
         for (int pi = 0; pi < MAXP; ++pi) {
             const int p = wave + 4 * pi;
@@ -511,7 +539,7 @@ void kda_intra_kernel(const PrefillArgs a) {
     } else {
         // exact pairwise path: decay products taken in linear space
         for (int e = tid; e < 2 * C * LD_F; e += I::kThreads) Pm[e] = 0.f;  // P and MX
-        __syncthreads();
+        lds_barrier();
         constexpr int PARTS = I::kThreads / C;
         constexpr int CPP = DK / PARTS;
         const int i = tid % C, part = tid / C, c0 = part * CPP;
@@ -540,7 +568,7 @@ void kda_intra_kernel(const PrefillArgs a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     if (KDA_LATE_V) load_v();
 
@@ -569,7 +597,7 @@ void kda_intra_kernel(const PrefillArgs a) {
             if (r > ci) MX[(b0 + ci) * LD_F + b0 + r] = xv[r];       // X[b0+r][b0+ci], transposed
         }
     }
-    __syncthreads();
+    lds_barrier();
     // Off-diagonal blocks, one block pair (R, Ib = R - d) per wave, on fp32 MFMA:
     //   Y = sum_{J=Ib}^{R-1} M_RJ X_JIb ;  X_RIb^T = -(Y^T X_RR^T)
     // Y's accumulator is already Y^T in operand layout (lane: row ii = cl,
@@ -600,7 +628,7 @@ void kda_intra_kernel(const PrefillArgs a) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) MX[(16 * Ib + 4 * g + jj) * LD_F + 16 * R + cl] = -z[jj];
         }
-        __syncthreads();
+        lds_barrier();
     }
     // Tm = X diag(beta), lower triangle, in the operand type; lanes run over
     // rows r so that reading X^T (stored in MX's upper part) is conflict-free
@@ -615,7 +643,7 @@ void kda_intra_kernel(const PrefillArgs a) {
         }
         store_q<T>(Tb + r * LD_CT + i0, f32x4{t4[0], t4[1], t4[2], t4[3]});
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- phase 4: value tile, P fragments, W = Tm Ktilde, Utilde = Tm V ------
     if (pv) {
@@ -629,8 +657,9 @@ void kda_intra_kernel(const PrefillArgs a) {
         const f32x4 v4 = ut <= ct ? *reinterpret_cast<const f32x4*>(Pm + r * LD_F + i0) : zero4();
         *reinterpret_cast<Q*>(Pf + Frag<T>::off(ct, ut, ln, C)) = make_quad<T>(v4);
     }
-    __syncthreads();
+    lds_barrier();
     // W^T(channel tile t, token tile tb) = Ktilde^T Tm^T: lane holds W[16tb+cl][16t+4g+j]
+#pragma unroll KDA_WU_UNROLL
     for (int tile = wave; tile < NQK * NB; tile += 4) {
         const int t = tile / NB, tb = tile % NB;
         Q aq[NB], bq[NB];
@@ -644,6 +673,7 @@ void kda_intra_kernel(const PrefillArgs a) {
     }
     // Utilde(token tile tb, value tile s) = Tm V: lane holds U[16tb+4g+j][16s+cl]
     const int NSV = DV / 16;
+#pragma unroll KDA_WU_UNROLL
     for (int tile = wave; tile < NB * NSV; tile += 4) {
         const int tb = tile / NSV, s = tile % NSV;
         Q aq[NB], bq[NB];
