@@ -147,7 +147,8 @@ template <int DK, int C, typename T> struct Intra {
     static constexpr int NOFF = NB * (NB - 1) / 2;  // off-diagonal block pairs
     static constexpr int NQK = DK / 16;  // quads along dk
     static constexpr int LD_ROW = DK + 8;  // row-major [*][DK] tiles (elements)
-    static constexpr int LD_CT = C + 8;    // [*][C] tiles (elements)
+    static constexpr int LD_CT = C + 4;    // [*][C] tiles (elements): a row stride of 2C + 8 bytes
+                                           // spreads 32 consecutive rows over distinct bank pairs
     static constexpr int LD_F = C + 4;     // fp32 [C][C] matrices
     static constexpr int kDvMax = 128;
     static constexpr size_t a16(size_t x) { return (x + 15) / 16 * 16; }
