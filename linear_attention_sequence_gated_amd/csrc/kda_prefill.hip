@@ -233,20 +233,36 @@ void kda_intra_kernel(const PrefillArgs a) {
     const int NCGV = DV / 8;
     const bool pv = tid < I::NSEG * NCGV;
     const int cgv = tid / I::NSEG, sgv = tid % I::NSEG;
-    float kr[4][8], qr[4][8], al[4][8], vr[4][8];
+    // All loads go out before any is used: tokens past the chunk's end (and
+    // threads outside the mapping) read an in-bounds row (the chunk's first
+    // token, channel group 0) and are masked after the loads land.
+    float kr[4][8], qr[4][8], al[4][8];
+    Raw8<In> vraw[4];   // v as loaded; converted where V^T is staged
+    {
+        Raw8<In> kraw[4], qraw[4];
+        Raw8<float> araw[4];
+        float ascal[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int r = 4 * sgi + u;
-        if (p1 && r < valid) {
-            const int64_t base = ((pos.tok0 + r) * H + h) * DK + 8 * cg;
-            load8(kg + base, kr[u]);
-            load8(qg + base, qr[u]);
+        for (int u = 0; u < 4; ++u) {
+            const int r = 4 * sgi + u;
+            const bool ok = p1 && r < valid;
+            const int64_t row = (pos.tok0 + (ok ? r : 0)) * H + h;
+            const int64_t base = row * DK + 8 * (p1 ? cg : 0);
+            kraw[u].load(kg + base);
+            qraw[u].load(qg + base);
+            if (kOpts && a.alpha_scalar) ascal[u] = a.alpha[row];
+            else araw[u].load(a.alpha + base);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool ok = p1 && 4 * sgi + u < valid;
+            kraw[u].unpack(kr[u]);
+            qraw[u].unpack(qr[u]);
             if (kOpts && a.alpha_scalar) {
-                const float as = a.alpha[(pos.tok0 + r) * H + h];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) al[u][e] = as;
+                for (int e = 0; e < 8; ++e) al[u][e] = ascal[u];
             } else {
-                load8(a.alpha + base, al[u]);
+                araw[u].unpack(al[u]);
             }
             if (kOpts && a.fuse_inputs) {
 #pragma unroll
@@ -256,23 +272,21 @@ void kda_intra_kernel(const PrefillArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) al[u][e] = fmaxf(al[u][e], a.alpha_floor);
             }
-        } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { kr[u][e] = 0.f; qr[u][e] = 0.f; al[u][e] = 1.f; }
+            for (int e = 0; e < 8; ++e) {
+                kr[u][e] = ok ? kr[u][e] : 0.f;
+                qr[u][e] = ok ? qr[u][e] : 0.f;
+                al[u][e] = ok ? al[u][e] : 1.f;
+            }
         }
     }
     // v is needed only once the solve is done: its loads go out after the Gram
     // phase (KDA_LATE_V) so that they do not queue behind the factor inputs
     auto load_v = [&]() {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int rv = 4 * sgv + u;
-            if (pv && rv < valid) {
-                load8(vg + ((pos.tok0 + rv) * H + h) * DV + 8 * cgv, vr[u]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vr[u][e] = 0.f;
-            }
+        for (int u = 0; u < 4; ++u) {   // masked where V^T is staged
+            const bool ok = pv && 4 * sgv + u < valid;
+            vraw[u].load(vg + ((pos.tok0 + (ok ? 4 * sgv + u : 0)) * H + h) * DV + 8 * (pv ? cgv : 0));
         }
     };
     if (!KDA_LATE_V) load_v();
@@ -648,6 +662,15 @@ void kda_intra_kernel(const PrefillArgs a) {
 
     // ---- phase 4: value tile, P fragments, W = Tm Ktilde, Utilde = Tm V ------
     if (pv) {
+        float vr[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            vraw[u].unpack(vr[u]);
+            if (4 * sgv + u >= valid) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vr[u][e] = 0.f;
+            }
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             store_q<T>(VT + (8 * cgv + e) * LD_CT + 4 * sgv, f32x4{vr[0][e], vr[1][e], vr[2][e], vr[3][e]});

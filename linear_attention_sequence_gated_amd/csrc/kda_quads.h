@@ -185,6 +185,36 @@ __device__ __forceinline__ void load8(const __bf16* p, float (&o)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = (float)a[i];
 }
+// Eight consecutive elements kept as loaded (one or two 16-byte vectors) and
+// converted to fp32 where they are used, so that the wait for a load sits at
+// its first use rather than right after it is issued.
+template <typename In> struct Raw8;
+template <> struct Raw8<__bf16> {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 w;  // element 2i in the low half of word i
+    __device__ __forceinline__ void load(const __bf16* p) { w = *reinterpret_cast<const u32x4*>(p); }
+    __device__ __forceinline__ void zero() { w = u32x4{0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ void unpack(float (&o)[8]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(w[i] << 16);
+            o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+template <> struct Raw8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const f32x4*>(p);
+        b = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    __device__ __forceinline__ void zero() { a = f32x4{0.f, 0.f, 0.f, 0.f}; b = a; }
+    __device__ __forceinline__ void unpack(float (&o)[8]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { o[i] = a[i]; o[4 + i] = b[i]; }
+    }
+};
+
 // Eight consecutive values to LDS in the operand type (16- or 32-byte vector stores).
 __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
     *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
