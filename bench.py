@@ -62,9 +62,9 @@ KERNEL_SOURCES = {
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {  # kernel: (sources, sha256[:16] of the sources, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "kda_intra_kernel": ("prefill", "09fffe1b917f05db", 1442030.0, 2416762.0),
-    "kda_inter_kernel": ("prefill", "09fffe1b917f05db", 1196106.0, 526336.0),
-    "kda_decode_kernel": ("decode", "1ee5a50a45e7a2e3", 267561.0, 526336.0),
+    "kda_intra_kernel": ("prefill", "22cb3f0a976224aa", 1452044.0, 2433018.0),
+    "kda_inter_kernel": ("prefill", "22cb3f0a976224aa", 1529502.0, 584991.0),
+    "kda_decode_kernel": ("decode", "54568d8d160e2b8b", 267572.0, 526549.0),
 }
 
 
