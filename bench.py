@@ -279,9 +279,12 @@ def main():
     if not args.no_variants:
         log("timing decode variants")
         N0, H0 = wd.decode_seqs, wd.heads
+        # N distinct pool entries drawn at random from a pool twice that size (a
+        # strided choice such as every other entry interleaves unevenly over HBM)
         pool = torch.empty((2 * N0, H0, wd.dk, wd.dv), dtype=torch.float32, device=dev)
-        pool[1::2].copy_(dd["S0"])
-        slots = torch.arange(1, 2 * N0, 2, dtype=torch.int32, device=dev)
+        pick = torch.randperm(2 * N0, generator=torch.Generator().manual_seed(11))[:N0]
+        pool[pick.to(dev)] = dd["S0"]
+        slots = pick.to(torch.int32).to(dev)
         gate = torch.zeros(dd["v"].shape[1:], dtype=dd["v"].dtype, device=dev)
         wn = torch.ones(wd.dv, device=dev)
 
