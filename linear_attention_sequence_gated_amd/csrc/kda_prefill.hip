@@ -199,8 +199,8 @@ void kda_intra_kernel(const PrefillArgs a) {
     float* Gs = sbeta + C;                      // [NB][DK] exponent at each block's first token
     float* Ge = Gs + NB * DK;                   // [NB][DK] exponent at each block's last token
     float* sIR = Ge + NB * DK;                  // [NOFF][DK] pair factors 2^{G_R - G_I + h_I - h_R}
-    unsigned* srange = reinterpret_cast<unsigned*>(sIR + (I::NOFF > 0 ? I::NOFF : 1) * DK);
-    float* sinv = reinterpret_cast<float*>(srange + 4);   // [2][C] inverse norms of q and k (fused inputs)
+    float* swmax = sIR + (I::NOFF > 0 ? I::NOFF : 1) * DK;   // [4] largest block decay range per wave
+    float* sinv = swmax + 4;                                  // [2][C] inverse norms of q and k (fused inputs)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, g = lane >> 4, cl = lane & 15;
@@ -346,7 +346,6 @@ void kda_intra_kernel(const PrefillArgs a) {
         if (kOpts && a.fuse_inputs && tid < valid) b = sigmoid(b);
         sbeta[tid] = b;
     }
-    if (tid == 0) *srange = 0u;
 
     // segment sums of log2 alpha (floored), then the exclusive prefix over the
     // segments of the channel group (a shuffle scan over NSEG adjacent lanes)
@@ -383,27 +382,36 @@ void kda_intra_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) Ge[Rb * DK + 8 * cg + e] = off[e] + lg[3][e];
     }
-    lds_barrier();
-    // block ranges decide the path; pair factors for the off-diagonal tiles
-    if (p1 && sp == 0) {
+    {
+        // decay range of each 16-token block (exponent at its first token minus
+        // at its last), maximised over the wave's blocks and channels; the last
+        // segment of a block is 3 lanes above its first
         float mx = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, Gs[Rb * DK + 8 * cg + e] - Ge[Rb * DK + 8 * cg + e]);
-        atomicMax(srange, __float_as_uint(mx));  // non-negative floats order like their bits
-    }
-    for (int e = tid; e < I::NOFF * DK; e += I::kThreads) {
-        const int p = e / DK, c = e % DK;
-        int R = 1;
-        while (R * (R + 1) / 2 <= p) ++R;          // off-diagonal pair p = R(R-1)/2 + Ib
-        const int Ib = p - R * (R - 1) / 2;
-        const float hR = 0.5f * (Gs[R * DK + c] - Ge[R * DK + c]);
-        const float hI = 0.5f * (Gs[Ib * DK + c] - Ge[Ib * DK + c]);
-        sIR[e] = __builtin_amdgcn_exp2f(fminf(Gs[R * DK + c] - Gs[Ib * DK + c] + hI - hR, 0.f));
+        for (int e = 0; e < 8; ++e) {
+            const float ge = __shfl_down(off[e] + lg[3][e], 3, I::NSEG);
+            if (sp == 0) mx = fmaxf(mx, off[e] + lg[0][e] - ge);
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+        if (lane == 0) swmax[wave] = mx;
     }
     lds_barrier();
-    const bool fast = __uint_as_float(*srange) <= kFastRange;
+    const bool fast = fmaxf(fmaxf(swmax[0], swmax[1]), fmaxf(swmax[2], swmax[3])) <= kFastRange;
 
     // ---- phase 1 (cont.): operand factors, tiles and the workspace quads ----
+    if (fast && p1 && sp < Rb) {
+        // pair factors 2^{G_R - G_I + h_I - h_R} (<= 1) of the off-diagonal tiles (R = Rb, I = sp)
+        const int Ib = sp;
+        float* dst = sIR + (Rb * (Rb - 1) / 2 + Ib) * DK + 8 * cg;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = 8 * cg + e;
+            const float hR = 0.5f * (Gs[Rb * DK + c] - Ge[Rb * DK + c]);
+            const float hI = 0.5f * (Gs[Ib * DK + c] - Ge[Ib * DK + c]);
+            dst[e] = __builtin_amdgcn_exp2f(fminf(Gs[Rb * DK + c] - Gs[Ib * DK + c] + hI - hR, 0.f));
+        }
+    }
     if (p1) {
         float sh[8], gb[8], pre[8], tail[8];
 #pragma unroll
