@@ -20,9 +20,9 @@
 //   kda_intra_kernel   : one workgroup per (chunk, head); everything above
 //                        that does not depend on S, written to the workspace
 //                        in the register layout the next kernel consumes
-//   kda_inter_kernel   : one wave per (sequence, head, 16 value columns);
-//                        walks the chunks in order with its slice of S held
-//                        in MFMA accumulator registers (fp32)
+//   kda_inter_kernel   : one workgroup per (sequence, head, 16 value
+//                        columns); walks the chunks in order with its slice
+//                        of S held in MFMA accumulator registers (fp32)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -733,6 +733,10 @@ void kda_intra_kernel(const PrefillArgs a) {
 // One s_barrier per chunk hands the ring over.  The slice groups of one
 // (sequence, head) are placed on one XCD (blocks are dealt round-robin over
 // the 8 XCDs) so the block is fetched from HBM once per XCD.
+// Plain calls with one slice per workgroup split the compute over two waves
+// instead: the state wave forms U and updates S (the serial chain), and an
+// output wave forms the outputs of the previous chunk from the S and U the
+// state wave left in LDS, so the chain no longer waits for the output tile.
 // ---------------------------------------------------------------------------
 // All N quads of row tile rt of a fragment matrix (K = 16 N), read as whole
 // 16-byte vectors per lane.
@@ -765,6 +769,11 @@ __device__ __forceinline__ void load_frag(f32x4 (&q)[N], const char* base, int r
 #define KDA_SLICES_PER_WAVE 1
 #endif
 #define KDA_SLICES_PER_WAVE_VALUE KDA_SLICES_PER_WAVE
+// 1: plain one-slice workgroups split the chain over two compute waves (the
+// state wave and an output wave one chunk behind it); 0: one compute wave.
+#ifndef KDA_O_WAVE
+#define KDA_O_WAVE 1
+#endif
 
 // Gated calls keep all dv / 16 slices (8 at dv = 128) in one workgroup, two per
 // compute wave, so that a workgroup still has two waves per SIMD (8 waves).
@@ -780,7 +789,23 @@ template <int DK, int C, typename T, bool kGate = false> struct Inter {
     static constexpr int64_t kGroupMax = round_kib((int64_t)G * C * 16 * sizeof(T));
     static constexpr int64_t kBuf = kShared + kGroupMax;
     static constexpr int64_t kPart = kGate ? 2ll * kMaxCompute * C * 4 : 0;   // output-norm partial sums
-    static constexpr bool kFits = 2 * kBuf + kPart <= 163840;
+    // Output-wave layout (one value slice per workgroup): ring A (W, Kbar^T,
+    // gamma_C, the slice of U~) has two slots, ring B (Q~, P) three, since the
+    // output wave reads a chunk one interval after the state wave; the state
+    // wave hands S and U to it through two LDS slots in its own lane layout.
+    static constexpr int64_t kSzW = Frag<T>::elems(C, DK) * (int64_t)sizeof(T);
+    static constexpr int64_t kSzK = Frag<T>::elems(DK, C) * (int64_t)sizeof(T);
+    static constexpr int64_t kSzP = Frag<T>::elems(C, C) * (int64_t)sizeof(T);
+    static constexpr int64_t kSzG = round_kib(DK * 4);
+    static constexpr int64_t kBufA = 2 * kSzW + kSzG + round_kib((int64_t)C * 16 * sizeof(T));
+    static constexpr int64_t kBufB = kSzW + kSzP;
+    static constexpr int64_t kHand = (int64_t)(DK / 16 + C / 16) * 64 * sizeof(quad_t<T>);
+    static constexpr int64_t kOWaveLds = 2 * kBufA + 3 * kBufB + 2 * kHand;
+    static constexpr bool kOWave = KDA_O_WAVE && !kGate && G == 1 && SPW == 1 && kSzW % 1024 == 0 &&
+                                   kSzP % 1024 == 0 && kSzK == kSzW && kOWaveLds <= 163840;
+    static constexpr int kComputeWaves = kOWave ? 2 : kMaxCompute;
+    static constexpr int64_t kLds = kOWave ? kOWaveLds : 2 * kBuf;
+    static constexpr bool kFits = kOWave || 2 * kBuf + kPart <= 163840;
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -791,6 +816,11 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 #endif
 // Waves per workgroup that copy chunk blocks into LDS (they split the 1 KiB units).
 constexpr int kIoWaves = KDA_IO_WAVES;
+// d > 0: the I/O waves also pull the block d chunks ahead of the copy into L2
+// (measured on the long-context workload: d = 2 best, 0 slowest).
+#ifndef KDA_L2_PREFETCH
+#define KDA_L2_PREFETCH 2
+#endif
 
 // Copy the 1 KiB units first, first + step, ... of `bytes` (a multiple of
 // 1 KiB) from global to LDS, 16 bytes per lane per instruction.
@@ -806,7 +836,7 @@ enum OutMode { kOutPlain = 0, kOutGate = 1, kOutSplit = 2 };
 // workgroup, norm and gate applied here; kOutSplit: one-slice workgroups write
 // un-normalised fp32 outputs and per-slice sums of squares for the epilogue.
 template <int DK, int C, typename In, int kMode>
-__global__ __launch_bounds__(64 * (Inter<DK, C, typename OperandOf<In>::type, kMode == kOutGate>::kMaxCompute + kIoWaves))
+__global__ __launch_bounds__(64 * (Inter<DK, C, typename OperandOf<In>::type, kMode == kOutGate>::kComputeWaves + kIoWaves))
 void kda_inter_kernel(const PrefillArgs a) {
     constexpr bool kGate = kMode == kOutGate;
     using T = typename OperandOf<In>::type;
@@ -814,7 +844,7 @@ void kda_inter_kernel(const PrefillArgs a) {
     using X = Inter<DK, C, T, kGate>;
     static_assert(X::kFits, "LDS ring of the inter-chunk kernel exceeds one workgroup");
     constexpr int NB = C / 16, NQK = DK / 16, SPW = X::SPW;
-    __shared__ __attribute__((aligned(1024))) char ring[2 * X::kBuf];
+    __shared__ __attribute__((aligned(1024))) char ring[X::kLds];
     // per-token sums of squares of each compute wave's outputs (double-buffered
     // by chunk parity) for the output norm of gated calls
     __shared__ float part[kGate ? 2 : 1][kGate ? X::kMaxCompute : 1][kGate ? C : 1];
@@ -846,6 +876,173 @@ void kda_inter_kernel(const PrefillArgs a) {
         seq_len = a.T;
     }
 
+    if constexpr (X::kOWave) {
+        // ---- two compute waves: wave 0 walks the state chain, wave 1 forms the
+        // outputs of the chunk before; waves 2.. are I/O waves.  Interval jn
+        // (between two barriers): the state wave takes chunk jn from ring A slot
+        // jn & 1 and leaves S_jn and U_jn in hand-off slot jn & 1; the output
+        // wave takes chunk jn - 1 (ring B slot (jn - 1) % 3, hand-off slot
+        // (jn - 1) & 1); the I/O waves fill both rings with chunk jn + 1.
+        const int nch = c_end - c_begin;
+        const int nint = nch + (nch > 0);   // one extra interval for the last chunk's outputs
+        char* const ringB = ring + 2 * X::kBufA;
+        char* const hand = ringB + 3 * X::kBufB;
+        const int sl = grp;   // the value slice of this workgroup
+        if (wave >= 2) {
+            const int io = wave - 2;
+            auto fetch = [&](int jn) {
+                const char* src = a.ws_chunks + ((int64_t)(c_begin + jn) * H + h) * cb.bytes;
+                char* A = ring + (jn & 1) * X::kBufA;
+                char* Bq = ringB + (jn % 3) * X::kBufB;
+                int first = io;   // 1 KiB units dealt round-robin over the I/O waves across segments
+                auto seg = [&](const char* sp, char* dp, int64_t bytes) {
+                    dma_to_lds(sp, dp, bytes, lane, first, kIoWaves);
+                    first = ((first - (int)(bytes / 1024)) % kIoWaves + kIoWaves) % kIoWaves;
+                };
+                seg(src + cb.w, A, X::kSzW);
+                seg(src + cb.kb, A + X::kSzW, X::kSzK);
+                seg(src + cb.gam, A + 2 * X::kSzW, X::kSzG);
+                seg(src + cb.u + grp * cb.group, A + 2 * X::kSzW + X::kSzG, cb.group);
+                seg(src + cb.q, Bq, X::kSzW);
+                seg(src + cb.p, Bq + X::kSzW, X::kSzP);
+            };
+            if (nch > 0) fetch(0);
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+#if KDA_L2_PREFETCH
+            // one dword per 128-byte line of a chunk KDA_L2_PREFETCH ahead of the
+            // copy (see the one-wave path below)
+            const int64_t shared_lines = cb.shared / 128, group_lines = cb.group / 128;
+            const int64_t my_shared = (shared_lines - grp + ngroups - 1) / ngroups;
+            const int64_t pl = (int64_t)io * 64 + lane;
+            const int64_t pf_off = pl < my_shared ? (grp + pl * ngroups) * 128
+                                   : pl < my_shared + group_lines ? cb.u + grp * cb.group + (pl - my_shared) * 128
+                                   : 0;
+#endif
+            for (int jn = 0; jn < nint; ++jn) {
+                if (jn + 1 < nch) fetch(jn + 1);
+#if KDA_L2_PREFETCH
+                asm volatile("" ::: "memory");
+                typedef __attribute__((address_space(1))) const int gbl_int_t;
+                const int xp = c_begin + min(jn + 1 + KDA_L2_PREFETCH, nch - 1);
+                const int pv = *(gbl_int_t*)(a.ws_chunks + ((int64_t)xp * H + h) * cb.bytes + pf_off);
+                asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
+                asm volatile("" ::"v"(pv));
+#else
+                asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+#endif
+            }
+            return;
+        }
+        const int64_t sbase = (int64_t)unit * DK * DV;
+        if (wave == 0) {
+            // ---- state wave: acc[t][j] = S[16t + 4g + j][16 sl + cl] --------------
+            f32x4 acc[NQK];
+#pragma unroll
+            for (int t = 0; t < NQK; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[t][j] = a.s0 ? a.s0[sbase + (int64_t)(16 * t + 4 * g + j) * DV + 16 * sl + cl] : 0.f;
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            for (int jn = 0; jn < nint; ++jn) {
+                if (jn < nch) {
+                    const char* A = ring + (jn & 1) * X::kBufA;
+                    const char* Wl = A;
+                    const char* Kl = A + X::kSzW;
+                    const float* gl = reinterpret_cast<const float*>(A + 2 * X::kSzW);
+                    const T* Ul = reinterpret_cast<const T*>(A + 2 * X::kSzW + X::kSzG);
+                    Q* hq = reinterpret_cast<Q*>(hand + (jn & 1) * X::kHand);
+                    Q sb[NQK];
+#pragma unroll
+                    for (int t = 0; t < NQK; ++t) {
+                        sb[t] = make_quad<T>(acc[t]);
+                        hq[t * 64 + lane] = sb[t];
+                    }
+                    // U = Utilde - W S
+                    Q ub[NB];
+#pragma unroll
+                    for (int tb = 0; tb < NB; ++tb) {
+                        Q wq[NQK];
+                        load_frag(wq, Wl, tb, lane);
+                        const f32x4 xw = mma_quads(wq, sb, zero4());
+                        const f32x4 ut = from_quad(*reinterpret_cast<const Q*>(Ul + (lane * NB + tb) * 4));
+                        ub[tb] = make_quad<T>(ut - xw);
+                        hq[(NQK + tb) * 64 + lane] = ub[tb];
+                    }
+                    // S <- diag(gamma_C) S + Kbar^T U
+#pragma unroll
+                    for (int t = 0; t < NQK; ++t) {
+                        const f32x4 gv = *reinterpret_cast<const f32x4*>(gl + 16 * t + 4 * g);
+                        Q kq[NB];
+                        load_frag(kq, Kl, t, lane);
+                        acc[t] = mma_quads(kq, ub, acc[t] * gv);
+                    }
+                    if (a.ckpt) {   // S after the first (jn + 1) C tokens, at multiples of ckpt_every
+                        const int64_t done = (int64_t)(jn + 1) * C;
+                        if (done <= seq_len && done % a.ckpt_every == 0 && done / a.ckpt_every <= a.max_ckpts) {
+                            float* cp = a.ckpt + (((int64_t)seq * a.max_ckpts + done / a.ckpt_every - 1) * H + h) * DK * DV;
+#pragma unroll
+                            for (int t = 0; t < NQK; ++t)
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    cp[(int64_t)(16 * t + 4 * g + j) * DV + 16 * sl + cl] = acc[t][j];
+                        }
+                    }
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            }
+            if (a.s_final) {
+#pragma unroll
+                for (int t = 0; t < NQK; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        a.s_final[sbase + (int64_t)(16 * t + 4 * g + j) * DV + 16 * sl + cl] = acc[t][j];
+            }
+            return;
+        }
+        // ---- output wave: O^T = S^T Qtilde^T + U^T P^T of chunk jn - 1 ------------
+        // (lane: columns 16 sl + 4g + j, token 16tb + cl)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        for (int jn = 0; jn < nint; ++jn) {
+            if (jn >= 1) {
+                const int jp = jn - 1;
+                const int64_t tok0 = tok_begin + (int64_t)jp * C;
+                const int valid = (int)min((int64_t)C, seq_len - (int64_t)jp * C);
+                const char* Bq = ringB + (jp % 3) * X::kBufB;
+                const char* Ql = Bq;
+                const char* Pl = Bq + X::kSzW;
+                const Q* hq = reinterpret_cast<const Q*>(hand + (jp & 1) * X::kHand);
+                Q sb[NQK], ub[NB];
+#pragma unroll
+                for (int t = 0; t < NQK; ++t) sb[t] = hq[t * 64 + lane];
+#pragma unroll
+                for (int tb = 0; tb < NB; ++tb) ub[tb] = hq[(NQK + tb) * 64 + lane];
+#pragma unroll
+                for (int tb = 0; tb < NB; ++tb) {
+                    Q qq[NQK], pq[NB];
+                    load_frag(qq, Ql, tb, lane);
+                    load_frag(pq, Pl, tb, lane);
+                    const int r = 16 * tb + cl;
+                    // two chains summed on the VALU (no K=16 step accumulates onto a K=32 result)
+                    const f32x4 sc = (mma_quads(sb, qq, zero4()) + mma_quads_upto(ub, pq, tb, zero4())) * a.scale;
+                    if constexpr (kMode == kOutSplit) {
+                        float sn = sc[0] * sc[0] + sc[1] * sc[1] + sc[2] * sc[2] + sc[3] * sc[3];
+                        sn += __shfl_xor(sn, 16, 64);
+                        sn += __shfl_xor(sn, 32, 64);
+                        if (r < valid) {
+                            const int64_t row = (tok0 + r) * H + h;
+                            *reinterpret_cast<f32x4*>(a.o_scratch + row * DV + 16 * sl + 4 * g) = sc;
+                            if (g == 0) a.part_scratch[row * (DV / 16) + sl] = sn;
+                        }
+                    } else if (r < valid) {
+                        const int64_t oi = ((tok0 + r) * H + h) * DV + 16 * sl + 4 * g;
+                        if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + oi, sc);
+                        else store4(reinterpret_cast<__bf16*>(a.o) + oi, sc);
+                    }
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+    } else {
     if (wave >= ncw) {
         // ---- I/O waves -----------------------------------------------------------
         const int io = wave - ncw;
@@ -857,11 +1054,39 @@ void kda_inter_kernel(const PrefillArgs a) {
         };
         if (c_begin < c_end) fetch(c_begin, 0);
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+#if KDA_L2_PREFETCH
+        // The ring holds two chunks, so the copy of chunk x + 1 is issued only
+        // one chunk ahead and would pay the full HBM latency.  One dword per
+        // 128-byte line of chunk x + 1 + KDA_L2_PREFETCH is loaded into a register
+        // as well, which brings that block into this XCD's L2 early: the shared part is split
+        // over the slice groups of the (sequence, head), each group touches its
+        // own value slice.  Exactly one load per lane (a lane without a line
+        // re-reads the block's first line), so the wait below can leave that
+        // one outstanding; the register is read (by an empty asm statement)
+        // after the barrier, where only that load can still be in flight.
+        const int64_t shared_lines = cb.shared / 128, group_lines = cb.group / 128;
+        const int64_t my_shared = (shared_lines - grp + ngroups - 1) / ngroups;
+        const int64_t pl = (int64_t)io * 64 + lane;
+        const int64_t pf_off = pl < my_shared ? (grp + pl * ngroups) * 128
+                               : pl < my_shared + group_lines ? cb.u + grp * cb.group + (pl - my_shared) * 128
+                               : 0;
+        for (int x = c_begin; x < c_end; ++x) {
+            if (x + 1 < c_end) fetch(x + 1, (x + 1 - c_begin) & 1);
+            asm volatile("" ::: "memory");   // the line load stays after the copies
+            const int xp = min(x + 1 + KDA_L2_PREFETCH, c_end - 1);
+            typedef __attribute__((address_space(1))) const int gbl_int_t;
+            const int pv = *(gbl_int_t*)(a.ws_chunks + ((int64_t)xp * H + h) * cb.bytes + pf_off);
+            asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
+            asm volatile("" ::"v"(pv));
+        }
+        return;
+#else
         for (int x = c_begin; x < c_end; ++x) {
             if (x + 1 < c_end) fetch(x + 1, (x + 1 - c_begin) & 1);
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         }
         return;
+#endif
     }
 
     // ---- compute waves: SPW value slices (16 columns each) per wave ----------------
@@ -1028,6 +1253,7 @@ void kda_inter_kernel(const PrefillArgs a) {
                 for (int j = 0; j < 4; ++j)
                     a.s_final[sbase + (int64_t)(16 * t + 4 * g + j) * DV + 16 * (s0 + n) + cl] = acc[n][t][j];
     }
+    }   // one compute wave per slice group
 }
 
 // ---------------------------------------------------------------------------
@@ -1057,13 +1283,14 @@ static hipError_t launch_phase_t(const PrefillArgs& a, int max_chunks, bool intr
                 hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutGate>), dim3(blocks),
                                    dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
             } else {
-                constexpr int spw = Inter<DK, C, typename OperandOf<In>::type, false>::SPW;
+                using XP = Inter<DK, C, typename OperandOf<In>::type, false>;
+                const int threads = 64 * ((XP::kOWave ? 2 : (a.gsl + XP::SPW - 1) / XP::SPW) + kIoWaves);
                 if (a.gate)
-                    hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutSplit>), dim3(blocks),
-                                       dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
+                    hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutSplit>), dim3(blocks), dim3(threads), 0,
+                                       stream, a);
                 else
-                    hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutPlain>), dim3(blocks),
-                                       dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
+                    hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutPlain>), dim3(blocks), dim3(threads), 0,
+                                       stream, a);
             }
         }
         return hipGetLastError();
