@@ -780,6 +780,19 @@ __device__ __forceinline__ void load_frag(f32x4 (&q)[N], const char* base, int r
 constexpr int kGateSlices = 8;
 constexpr int kGateSlicesPerWave = 2;
 
+// Waves per workgroup that copy chunk blocks into LDS (they split the 1 KiB
+// units): KDA_IO_WAVES with one compute wave per slice group, KDA_IO_WAVES_OW
+// beside the state and output waves (the copy rate per workgroup rises with
+// the waves issuing it: 2, 4, 8 waves copy the long-context blocks in 1.34,
+// 1.22, 1.12 ms).
+#ifndef KDA_IO_WAVES
+#define KDA_IO_WAVES 4
+#endif
+#ifndef KDA_IO_WAVES_OW
+#define KDA_IO_WAVES_OW 8
+#endif
+constexpr int kIoWaves = KDA_IO_WAVES;
+
 template <int DK, int C, typename T, bool kGate = false> struct Inter {
     static constexpr int G = kGate ? kGateSlices : kGroupSlices;   // most slices per workgroup
     static constexpr int SPW = kGate ? kGateSlicesPerWave : KDA_SLICES_PER_WAVE_VALUE;
@@ -804,6 +817,8 @@ template <int DK, int C, typename T, bool kGate = false> struct Inter {
     static constexpr bool kOWave = KDA_O_WAVE && !kGate && G == 1 && SPW == 1 && kSzW % 1024 == 0 &&
                                    kSzP % 1024 == 0 && kSzK == kSzW && kOWaveLds <= 163840;
     static constexpr int kComputeWaves = kOWave ? 2 : kMaxCompute;
+    static constexpr int kIo = kOWave ? KDA_IO_WAVES_OW : KDA_IO_WAVES;
+    static constexpr int kThreads = 64 * (kComputeWaves + kIo);
     static constexpr int64_t kLds = kOWave ? kOWaveLds : 2 * kBuf;
     static constexpr bool kFits = kOWave || 2 * kBuf + kPart <= 163840;
 };
@@ -811,11 +826,6 @@ template <int DK, int C, typename T, bool kGate = false> struct Inter {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-#ifndef KDA_IO_WAVES
-#define KDA_IO_WAVES 4
-#endif
-// Waves per workgroup that copy chunk blocks into LDS (they split the 1 KiB units).
-constexpr int kIoWaves = KDA_IO_WAVES;
 // d > 0: the I/O waves also pull the block d chunks ahead of the copy into L2
 // (measured on the long-context workload: d = 2 best, 0 slowest).
 #ifndef KDA_L2_PREFETCH
@@ -836,7 +846,7 @@ enum OutMode { kOutPlain = 0, kOutGate = 1, kOutSplit = 2 };
 // workgroup, norm and gate applied here; kOutSplit: one-slice workgroups write
 // un-normalised fp32 outputs and per-slice sums of squares for the epilogue.
 template <int DK, int C, typename In, int kMode>
-__global__ __launch_bounds__(64 * (Inter<DK, C, typename OperandOf<In>::type, kMode == kOutGate>::kComputeWaves + kIoWaves))
+__global__ __launch_bounds__((Inter<DK, C, typename OperandOf<In>::type, kMode == kOutGate>::kThreads))
 void kda_inter_kernel(const PrefillArgs a) {
     constexpr bool kGate = kMode == kOutGate;
     using T = typename OperandOf<In>::type;
@@ -896,8 +906,8 @@ void kda_inter_kernel(const PrefillArgs a) {
                 char* Bq = ringB + (jn % 3) * X::kBufB;
                 int first = io;   // 1 KiB units dealt round-robin over the I/O waves across segments
                 auto seg = [&](const char* sp, char* dp, int64_t bytes) {
-                    dma_to_lds(sp, dp, bytes, lane, first, kIoWaves);
-                    first = ((first - (int)(bytes / 1024)) % kIoWaves + kIoWaves) % kIoWaves;
+                    dma_to_lds(sp, dp, bytes, lane, first, X::kIo);
+                    first = ((first - (int)(bytes / 1024)) % X::kIo + X::kIo) % X::kIo;
                 };
                 seg(src + cb.w, A, X::kSzW);
                 seg(src + cb.kb, A + X::kSzW, X::kSzK);
@@ -1284,7 +1294,7 @@ static hipError_t launch_phase_t(const PrefillArgs& a, int max_chunks, bool intr
                                    dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
             } else {
                 using XP = Inter<DK, C, typename OperandOf<In>::type, false>;
-                const int threads = 64 * ((XP::kOWave ? 2 : (a.gsl + XP::SPW - 1) / XP::SPW) + kIoWaves);
+                const int threads = XP::kOWave ? XP::kThreads : 64 * ((a.gsl + XP::SPW - 1) / XP::SPW + kIoWaves);
                 if (a.gate)
                     hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutSplit>), dim3(blocks), dim3(threads), 0,
                                        stream, a);
