@@ -1065,216 +1065,216 @@ void kda_inter_kernel(const PrefillArgs a) {
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         }
     } else {
-    if (wave >= ncw) {
-        // ---- I/O waves -----------------------------------------------------------
-        const int io = wave - ncw;
-        auto fetch = [&](int x, int slot) {
-            const char* src = a.ws_chunks + ((int64_t)x * H + h) * cb.bytes;
-            char* dst = ring + slot * X::kBuf;
-            dma_to_lds(src, dst, cb.shared, lane, io, kIoWaves);
-            dma_to_lds(src + cb.u + grp * cb.group, dst + X::kShared, cb.group, lane, io, kIoWaves);
-        };
-        if (c_begin < c_end) fetch(c_begin, 0);
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-#if KDA_L2_PREFETCH
-        // The ring holds two chunks, so the copy of chunk x + 1 is issued only
-        // one chunk ahead and would pay the full HBM latency.  One dword per
-        // 128-byte line of chunk x + 1 + KDA_L2_PREFETCH is loaded into a register
-        // as well, which brings that block into this XCD's L2 early: the shared part is split
-        // over the slice groups of the (sequence, head), each group touches its
-        // own value slice.  Exactly one load per lane (a lane without a line
-        // re-reads the block's first line), so the wait below can leave that
-        // one outstanding; the register is read (by an empty asm statement)
-        // after the barrier, where only that load can still be in flight.
-        const int64_t shared_lines = cb.shared / 128, group_lines = cb.group / 128;
-        const int64_t my_shared = (shared_lines - grp + ngroups - 1) / ngroups;
-        const int64_t pl = (int64_t)io * 64 + lane;
-        const int64_t pf_off = pl < my_shared ? (grp + pl * ngroups) * 128
-                               : pl < my_shared + group_lines ? cb.u + grp * cb.group + (pl - my_shared) * 128
-                               : 0;
-        for (int x = c_begin; x < c_end; ++x) {
-            if (x + 1 < c_end) fetch(x + 1, (x + 1 - c_begin) & 1);
-            asm volatile("" ::: "memory");   // the line load stays after the copies
-            const int xp = min(x + 1 + KDA_L2_PREFETCH, c_end - 1);
-            typedef __attribute__((address_space(1))) const int gbl_int_t;
-            const int pv = *(gbl_int_t*)(a.ws_chunks + ((int64_t)xp * H + h) * cb.bytes + pf_off);
-            asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
-            asm volatile("" ::"v"(pv));
-        }
-        return;
-#else
-        for (int x = c_begin; x < c_end; ++x) {
-            if (x + 1 < c_end) fetch(x + 1, (x + 1 - c_begin) & 1);
+        if (wave >= ncw) {
+            // ---- I/O waves -----------------------------------------------------------
+            const int io = wave - ncw;
+            auto fetch = [&](int x, int slot) {
+                const char* src = a.ws_chunks + ((int64_t)x * H + h) * cb.bytes;
+                char* dst = ring + slot * X::kBuf;
+                dma_to_lds(src, dst, cb.shared, lane, io, kIoWaves);
+                dma_to_lds(src + cb.u + grp * cb.group, dst + X::kShared, cb.group, lane, io, kIoWaves);
+            };
+            if (c_begin < c_end) fetch(c_begin, 0);
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        }
-        return;
+#if KDA_L2_PREFETCH
+            // The ring holds two chunks, so the copy of chunk x + 1 is issued only
+            // one chunk ahead and would pay the full HBM latency.  One dword per
+            // 128-byte line of chunk x + 1 + KDA_L2_PREFETCH is loaded into a register
+            // as well, which brings that block into this XCD's L2 early: the shared part is split
+            // over the slice groups of the (sequence, head), each group touches its
+            // own value slice.  Exactly one load per lane (a lane without a line
+            // re-reads the block's first line), so the wait below can leave that
+            // one outstanding; the register is read (by an empty asm statement)
+            // after the barrier, where only that load can still be in flight.
+            const int64_t shared_lines = cb.shared / 128, group_lines = cb.group / 128;
+            const int64_t my_shared = (shared_lines - grp + ngroups - 1) / ngroups;
+            const int64_t pl = (int64_t)io * 64 + lane;
+            const int64_t pf_off = pl < my_shared ? (grp + pl * ngroups) * 128
+                                   : pl < my_shared + group_lines ? cb.u + grp * cb.group + (pl - my_shared) * 128
+                                   : 0;
+            for (int x = c_begin; x < c_end; ++x) {
+                if (x + 1 < c_end) fetch(x + 1, (x + 1 - c_begin) & 1);
+                asm volatile("" ::: "memory");   // the line load stays after the copies
+                const int xp = min(x + 1 + KDA_L2_PREFETCH, c_end - 1);
+                typedef __attribute__((address_space(1))) const int gbl_int_t;
+                const int pv = *(gbl_int_t*)(a.ws_chunks + ((int64_t)xp * H + h) * cb.bytes + pf_off);
+                asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
+                asm volatile("" ::"v"(pv));
+            }
+            return;
+#else
+            for (int x = c_begin; x < c_end; ++x) {
+                if (x + 1 < c_end) fetch(x + 1, (x + 1 - c_begin) & 1);
+                asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+            }
+            return;
 #endif
-    }
-
-    // ---- compute waves: SPW value slices (16 columns each) per wave ----------------
-    const int s0 = grp * cb.gsl + wave * SPW;   // first value slice of this wave
-    // slices this wave owns (a group may hold fewer than SPW * waves); the
-    // accumulators of a missing slice are computed on stale LDS and never stored
-    const int nsl = min(SPW, cb.gsl - wave * SPW);
-    // S slices in accumulator layout: acc[n][t][j] = S[16t + 4g + j][16 (s0 + n) + cl]
-    f32x4 acc[SPW][NQK];
-    const int64_t sbase = (int64_t)unit * DK * DV;
-#pragma unroll
-    for (int n = 0; n < SPW; ++n)
-#pragma unroll
-        for (int t = 0; t < NQK; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[n][t][j] = (a.s0 && n < nsl) ? a.s0[sbase + (int64_t)(16 * t + 4 * g + j) * DV + 16 * (s0 + n) + cl] : 0.f;
-
-    // gated calls: a chunk's outputs wait in registers until every wave's
-    // partial sums of squares are in LDS (after the chunk's barrier); the
-    // norm, weight and gate are then applied and the outputs stored
-    f32x4 opend[kGate ? NB : 1][kGate ? SPW : 1];
-    int64_t ptok0 = 0;
-    int pvalid = 0, pbuf = 0;
-    bool pending = false;
-    auto flush = [&]() {
-        if constexpr (kGate) {
-            const In* __restrict__ gt = reinterpret_cast<const In*>(a.gate);
-#pragma unroll
-            for (int tb = 0; tb < NB; ++tb) {
-                const int r = 16 * tb + cl;
-                float ss = 0.f;
-                for (int w2 = 0; w2 < ncw; ++w2) ss += part[pbuf][w2][r];
-                const float inv = rsqrtf(ss / (float)DV + a.norm_eps);
-#pragma unroll
-                for (int n = 0; n < SPW; ++n) {
-                    if (r < pvalid && n < nsl) {
-                        const int col = 16 * (s0 + n) + 4 * g;
-                        const int64_t oi = ((ptok0 + r) * H + h) * DV + col;
-                        f32x4 o4 = opend[tb][n] * inv;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            o4[j] *= (a.norm_w ? a.norm_w[col + j] : 1.f) * sigmoid(load_as_float(gt, oi + j));
-                        if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + oi, o4);
-                        else store4(reinterpret_cast<__bf16*>(a.o) + oi, o4);
-                    }
-                }
-            }
         }
-    };
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    for (int x = c_begin; x < c_end; ++x) {
-        const int jc = x - c_begin;
-        const int64_t tok0 = tok_begin + (int64_t)jc * C;
-        const int valid = (int)min((int64_t)C, seq_len - (int64_t)jc * C);
-        const char* buf = ring + (jc & 1) * X::kBuf;
-        const char* Wl = buf + cb.w;
-        const char* Ql = buf + cb.q;
-        const char* Kl = buf + cb.kb;
-        const char* Pl = buf + cb.p;
-        const float* gl = reinterpret_cast<const float*>(buf + cb.gam);
-        const T* Ul = reinterpret_cast<const T*>(buf + X::kShared + (s0 - grp * cb.gsl) * cb.slice);
-        if (kGate && pending) flush();   // the previous chunk: its partial sums are complete
-
-        Q sb[SPW][NQK];
+        // ---- compute waves: SPW value slices (16 columns each) per wave ----------------
+        const int s0 = grp * cb.gsl + wave * SPW;   // first value slice of this wave
+        // slices this wave owns (a group may hold fewer than SPW * waves); the
+        // accumulators of a missing slice are computed on stale LDS and never stored
+        const int nsl = min(SPW, cb.gsl - wave * SPW);
+        // S slices in accumulator layout: acc[n][t][j] = S[16t + 4g + j][16 (s0 + n) + cl]
+        f32x4 acc[SPW][NQK];
+        const int64_t sbase = (int64_t)unit * DK * DV;
 #pragma unroll
         for (int n = 0; n < SPW; ++n)
-#pragma unroll
-            for (int t = 0; t < NQK; ++t) sb[n][t] = make_quad<T>(acc[n][t]);
-
-        // U = Utilde - W S   (lane: tokens 16tb + 4g + j, column of slice n)
-        Q ub[SPW][NB];
-#pragma unroll
-        for (int tb = 0; tb < NB; ++tb) {
-            Q wq[NQK];
-            load_frag(wq, Wl, tb, lane);
-#pragma unroll
-            for (int n = 0; n < SPW; ++n) {
-                const f32x4 xw = mma_quads(wq, sb[n], zero4());
-                const f32x4 ut = from_quad(*reinterpret_cast<const Q*>(Ul + n * (cb.slice / sizeof(T)) + (lane * NB + tb) * 4));
-                ub[n][tb] = make_quad<T>(ut - xw);
-            }
-        }
-        // S <- diag(gamma_C) S + Kbar^T U
-#pragma unroll
-        for (int t = 0; t < NQK; ++t) {
-            const f32x4 gv = *reinterpret_cast<const f32x4*>(gl + 16 * t + 4 * g);
-            Q kq[NB];
-            load_frag(kq, Kl, t, lane);
-#pragma unroll
-            for (int n = 0; n < SPW; ++n) acc[n][t] = mma_quads(kq, ub[n], acc[n][t] * gv);
-        }
-        // state checkpoint: S after the first (jc + 1) C tokens when that is a
-        // multiple of ckpt_every inside the sequence (a full chunk)
-        if (a.ckpt) {
-            const int64_t done = (int64_t)(jc + 1) * C;
-            if (done <= seq_len && done % a.ckpt_every == 0 && done / a.ckpt_every <= a.max_ckpts) {
-                float* cp = a.ckpt + (((int64_t)seq * a.max_ckpts + done / a.ckpt_every - 1) * H + h) * DK * DV;
-#pragma unroll
-                for (int sl = 0; sl < SPW; ++sl)
-                    if (sl < nsl)
-#pragma unroll
-                        for (int t = 0; t < NQK; ++t)
-#pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                cp[(int64_t)(16 * t + 4 * g + j) * DV + 16 * (s0 + sl) + cl] = acc[sl][t][j];
-            }
-        }
-        // O^T = S^T Qtilde^T + U^T P^T   (lane: columns 4g + j, token 16tb + cl); S^T from sb (pre-update)
-#pragma unroll
-        for (int tb = 0; tb < NB; ++tb) {
-            Q qq[NQK], pq[NB];
-            load_frag(qq, Ql, tb, lane);
-            load_frag(pq, Pl, tb, lane);
-            const int r = 16 * tb + cl;
-            float ss = 0.f;
-#pragma unroll
-            for (int n = 0; n < SPW; ++n) {
-                // two chains summed on the VALU: with dk or C of 16 one of them is a
-                // single K=16 step, which must not accumulate onto a K=32 result
-                const f32x4 ot = mma_quads(sb[n], qq, zero4()) + mma_quads_upto(ub[n], pq, tb, zero4());
-                const f32x4 sc = ot * a.scale;
-                if constexpr (kGate) {
-                    opend[tb][n] = sc;
-                    if (n < nsl) ss += sc[0] * sc[0] + sc[1] * sc[1] + sc[2] * sc[2] + sc[3] * sc[3];
-                } else if constexpr (kMode == kOutSplit) {
-                    float sn = sc[0] * sc[0] + sc[1] * sc[1] + sc[2] * sc[2] + sc[3] * sc[3];
-                    sn += __shfl_xor(sn, 16, 64);
-                    sn += __shfl_xor(sn, 32, 64);
-                    if (r < valid && n < nsl) {
-                        const int64_t row = (tok0 + r) * H + h;
-                        *reinterpret_cast<f32x4*>(a.o_scratch + row * DV + 16 * (s0 + n) + 4 * g) = sc;
-                        if (g == 0) a.part_scratch[row * (DV / 16) + s0 + n] = sn;
-                    }
-                } else if (r < valid && n < nsl) {
-                    const int64_t oi = ((tok0 + r) * H + h) * DV + 16 * (s0 + n) + 4 * g;
-                    if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + oi, sc);
-                    else store4(reinterpret_cast<__bf16*>(a.o) + oi, sc);
-                }
-            }
-            if constexpr (kGate) {   // this wave's columns of token r: lanes cl, cl + 16, cl + 32, cl + 48
-                ss += __shfl_xor(ss, 16, 64);
-                ss += __shfl_xor(ss, 32, 64);
-                if (g == 0) part[jc & 1][wave][r] = ss;
-            }
-        }
-        if constexpr (kGate) {
-            ptok0 = tok0;
-            pvalid = valid;
-            pbuf = jc & 1;
-            pending = true;
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    if (kGate && pending) flush();   // the last chunk, past its barrier
-    if (a.s_final) {
-#pragma unroll
-        for (int n = 0; n < SPW; ++n)
-            if (n < nsl)
 #pragma unroll
             for (int t = 0; t < NQK; ++t)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    a.s_final[sbase + (int64_t)(16 * t + 4 * g + j) * DV + 16 * (s0 + n) + cl] = acc[n][t][j];
-    }
+                    acc[n][t][j] = (a.s0 && n < nsl) ? a.s0[sbase + (int64_t)(16 * t + 4 * g + j) * DV + 16 * (s0 + n) + cl] : 0.f;
+
+        // gated calls: a chunk's outputs wait in registers until every wave's
+        // partial sums of squares are in LDS (after the chunk's barrier); the
+        // norm, weight and gate are then applied and the outputs stored
+        f32x4 opend[kGate ? NB : 1][kGate ? SPW : 1];
+        int64_t ptok0 = 0;
+        int pvalid = 0, pbuf = 0;
+        bool pending = false;
+        auto flush = [&]() {
+            if constexpr (kGate) {
+                const In* __restrict__ gt = reinterpret_cast<const In*>(a.gate);
+#pragma unroll
+                for (int tb = 0; tb < NB; ++tb) {
+                    const int r = 16 * tb + cl;
+                    float ss = 0.f;
+                    for (int w2 = 0; w2 < ncw; ++w2) ss += part[pbuf][w2][r];
+                    const float inv = rsqrtf(ss / (float)DV + a.norm_eps);
+#pragma unroll
+                    for (int n = 0; n < SPW; ++n) {
+                        if (r < pvalid && n < nsl) {
+                            const int col = 16 * (s0 + n) + 4 * g;
+                            const int64_t oi = ((ptok0 + r) * H + h) * DV + col;
+                            f32x4 o4 = opend[tb][n] * inv;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                o4[j] *= (a.norm_w ? a.norm_w[col + j] : 1.f) * sigmoid(load_as_float(gt, oi + j));
+                            if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + oi, o4);
+                            else store4(reinterpret_cast<__bf16*>(a.o) + oi, o4);
+                        }
+                    }
+                }
+            }
+        };
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+        for (int x = c_begin; x < c_end; ++x) {
+            const int jc = x - c_begin;
+            const int64_t tok0 = tok_begin + (int64_t)jc * C;
+            const int valid = (int)min((int64_t)C, seq_len - (int64_t)jc * C);
+            const char* buf = ring + (jc & 1) * X::kBuf;
+            const char* Wl = buf + cb.w;
+            const char* Ql = buf + cb.q;
+            const char* Kl = buf + cb.kb;
+            const char* Pl = buf + cb.p;
+            const float* gl = reinterpret_cast<const float*>(buf + cb.gam);
+            const T* Ul = reinterpret_cast<const T*>(buf + X::kShared + (s0 - grp * cb.gsl) * cb.slice);
+            if (kGate && pending) flush();   // the previous chunk: its partial sums are complete
+
+            Q sb[SPW][NQK];
+#pragma unroll
+            for (int n = 0; n < SPW; ++n)
+#pragma unroll
+                for (int t = 0; t < NQK; ++t) sb[n][t] = make_quad<T>(acc[n][t]);
+
+            // U = Utilde - W S   (lane: tokens 16tb + 4g + j, column of slice n)
+            Q ub[SPW][NB];
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb) {
+                Q wq[NQK];
+                load_frag(wq, Wl, tb, lane);
+#pragma unroll
+                for (int n = 0; n < SPW; ++n) {
+                    const f32x4 xw = mma_quads(wq, sb[n], zero4());
+                    const f32x4 ut = from_quad(*reinterpret_cast<const Q*>(Ul + n * (cb.slice / sizeof(T)) + (lane * NB + tb) * 4));
+                    ub[n][tb] = make_quad<T>(ut - xw);
+                }
+            }
+            // S <- diag(gamma_C) S + Kbar^T U
+#pragma unroll
+            for (int t = 0; t < NQK; ++t) {
+                const f32x4 gv = *reinterpret_cast<const f32x4*>(gl + 16 * t + 4 * g);
+                Q kq[NB];
+                load_frag(kq, Kl, t, lane);
+#pragma unroll
+                for (int n = 0; n < SPW; ++n) acc[n][t] = mma_quads(kq, ub[n], acc[n][t] * gv);
+            }
+            // state checkpoint: S after the first (jc + 1) C tokens when that is a
+            // multiple of ckpt_every inside the sequence (a full chunk)
+            if (a.ckpt) {
+                const int64_t done = (int64_t)(jc + 1) * C;
+                if (done <= seq_len && done % a.ckpt_every == 0 && done / a.ckpt_every <= a.max_ckpts) {
+                    float* cp = a.ckpt + (((int64_t)seq * a.max_ckpts + done / a.ckpt_every - 1) * H + h) * DK * DV;
+#pragma unroll
+                    for (int sl = 0; sl < SPW; ++sl)
+                        if (sl < nsl)
+#pragma unroll
+                            for (int t = 0; t < NQK; ++t)
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    cp[(int64_t)(16 * t + 4 * g + j) * DV + 16 * (s0 + sl) + cl] = acc[sl][t][j];
+                }
+            }
+            // O^T = S^T Qtilde^T + U^T P^T   (lane: columns 4g + j, token 16tb + cl); S^T from sb (pre-update)
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb) {
+                Q qq[NQK], pq[NB];
+                load_frag(qq, Ql, tb, lane);
+                load_frag(pq, Pl, tb, lane);
+                const int r = 16 * tb + cl;
+                float ss = 0.f;
+#pragma unroll
+                for (int n = 0; n < SPW; ++n) {
+                    // two chains summed on the VALU: with dk or C of 16 one of them is a
+                    // single K=16 step, which must not accumulate onto a K=32 result
+                    const f32x4 ot = mma_quads(sb[n], qq, zero4()) + mma_quads_upto(ub[n], pq, tb, zero4());
+                    const f32x4 sc = ot * a.scale;
+                    if constexpr (kGate) {
+                        opend[tb][n] = sc;
+                        if (n < nsl) ss += sc[0] * sc[0] + sc[1] * sc[1] + sc[2] * sc[2] + sc[3] * sc[3];
+                    } else if constexpr (kMode == kOutSplit) {
+                        float sn = sc[0] * sc[0] + sc[1] * sc[1] + sc[2] * sc[2] + sc[3] * sc[3];
+                        sn += __shfl_xor(sn, 16, 64);
+                        sn += __shfl_xor(sn, 32, 64);
+                        if (r < valid && n < nsl) {
+                            const int64_t row = (tok0 + r) * H + h;
+                            *reinterpret_cast<f32x4*>(a.o_scratch + row * DV + 16 * (s0 + n) + 4 * g) = sc;
+                            if (g == 0) a.part_scratch[row * (DV / 16) + s0 + n] = sn;
+                        }
+                    } else if (r < valid && n < nsl) {
+                        const int64_t oi = ((tok0 + r) * H + h) * DV + 16 * (s0 + n) + 4 * g;
+                        if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + oi, sc);
+                        else store4(reinterpret_cast<__bf16*>(a.o) + oi, sc);
+                    }
+                }
+                if constexpr (kGate) {   // this wave's columns of token r: lanes cl, cl + 16, cl + 32, cl + 48
+                    ss += __shfl_xor(ss, 16, 64);
+                    ss += __shfl_xor(ss, 32, 64);
+                    if (g == 0) part[jc & 1][wave][r] = ss;
+                }
+            }
+            if constexpr (kGate) {
+                ptok0 = tok0;
+                pvalid = valid;
+                pbuf = jc & 1;
+                pending = true;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+        if (kGate && pending) flush();   // the last chunk, past its barrier
+        if (a.s_final) {
+#pragma unroll
+            for (int n = 0; n < SPW; ++n)
+                if (n < nsl)
+#pragma unroll
+                for (int t = 0; t < NQK; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        a.s_final[sbase + (int64_t)(16 * t + 4 * g + j) * DV + 16 * (s0 + n) + cl] = acc[n][t][j];
+        }
     }   // one compute wave per slice group
 }
 
