@@ -781,6 +781,11 @@ __device__ __forceinline__ void load_frag(f32x4 (&q)[N], const char* base, int r
 #define KDA_SLICES_PER_WAVE 1
 #endif
 #define KDA_SLICES_PER_WAVE_VALUE KDA_SLICES_PER_WAVE
+// 1: ring B copies of the two-compute-wave path complete an interval after
+// they are issued (waited for one barrier later); 0: at the next barrier.
+#ifndef KDA_DEFER_B
+#define KDA_DEFER_B 1
+#endif
 // 1: plain one-slice workgroups split the chain over two compute waves (the
 // state wave and an output wave one chunk behind it); 0: one compute wave.
 #ifndef KDA_O_WAVE
@@ -830,6 +835,10 @@ template <int DK, int C, typename T, bool kGate = false> struct Inter {
                                    kSzP % 1024 == 0 && kSzK == kSzW && kOWaveLds <= 163840;
     static constexpr int kComputeWaves = kOWave ? 2 : kMaxCompute;
     static constexpr int kIo = kOWave ? KDA_IO_WAVES_OW : KDA_IO_WAVES;
+    // 1 KiB copies of ring B issued by each I/O wave per chunk (they are dealt
+    // evenly only when the I/O waves divide them)
+    static constexpr int kDeferB = (int)((kSzW + kSzP) / 1024 / kIo);
+    static constexpr bool kDeferOk = (kSzW + kSzP) / 1024 % kIo == 0 && kDeferB + 1 <= 63;
     static constexpr int kThreads = 64 * (kComputeWaves + kIo);
     static constexpr int64_t kLds = kOWave ? kOWaveLds : 2 * kBuf;
     static constexpr bool kFits = kOWave || 2 * kBuf + kPart <= 163840;
@@ -867,6 +876,8 @@ void kda_inter_kernel(const PrefillArgs a) {
     static_assert(X::kFits, "LDS ring of the inter-chunk kernel exceeds one workgroup");
     constexpr int NB = C / 16, NQK = DK / 16, SPW = X::SPW;
     __shared__ __attribute__((aligned(1024))) char ring[X::kLds];
+    // target of the I/O waves' one-dword L2 prefetch loads (never read)
+    __shared__ __attribute__((aligned(256))) int pf_sink[X::kOWave && KDA_L2_PREFETCH && KDA_DEFER_B ? 64 : 1];
     // per-token sums of squares of each compute wave's outputs (double-buffered
     // by chunk parity) for the output norm of gated calls
     __shared__ float part[kGate ? 2 : 1][kGate ? X::kMaxCompute : 1][kGate ? C : 1];
@@ -941,14 +952,27 @@ void kda_inter_kernel(const PrefillArgs a) {
                                    : 0;
 #endif
             for (int jn = 0; jn < nint; ++jn) {
-                if (jn + 1 < nch) fetch(jn + 1);
+                const bool more = jn + 1 < nch;
+                if (more) fetch(jn + 1);
 #if KDA_L2_PREFETCH
-                asm volatile("" ::: "memory");
-                typedef __attribute__((address_space(1))) const int gbl_int_t;
+                asm volatile("" ::: "memory");   // the line load stays after the copies
                 const int xp = c_begin + min(jn + 1 + KDA_L2_PREFETCH, nch - 1);
+                if constexpr (KDA_DEFER_B && X::kDeferOk) {
+                // the line load lands in a scratch LDS word (no register, so no
+                // compiler wait); ring B of the chunk just issued is first read
+                // an interval later, so the wait leaves its copies (kDeferB per
+                // wave) and the line load in flight: loads complete in order, so
+                // everything issued before them, ring A included, has landed
+                __builtin_amdgcn_global_load_lds((gbl_void_t*)(a.ws_chunks + ((int64_t)xp * H + h) * cb.bytes + pf_off),
+                                                 (lds_void_t*)pf_sink, 4, 0, 0);
+                if (more) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(X::kDeferB + 1) : "memory");
+                else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+                } else {
+                typedef __attribute__((address_space(1))) const int gbl_int_t;
                 const int pv = *(gbl_int_t*)(a.ws_chunks + ((int64_t)xp * H + h) * cb.bytes + pf_off);
                 asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
                 asm volatile("" ::"v"(pv));
+                }
 #else
                 asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 #endif
