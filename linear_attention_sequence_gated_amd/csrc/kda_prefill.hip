@@ -799,14 +799,14 @@ constexpr int kGateSlicesPerWave = 2;
 
 // Waves per workgroup that copy chunk blocks into LDS (they split the 1 KiB
 // units): KDA_IO_WAVES with one compute wave per slice group, KDA_IO_WAVES_OW
-// beside the state and output waves (the copy rate per workgroup rises with
-// the waves issuing it: 2, 4, 8 waves copy the long-context blocks in 1.34,
-// 1.22, 1.12 ms).
+// beside the state and output waves.  Long-context inter-chunk pass with the
+// ring B wait deferred: 4 waves 1.036 ms, 6: 1.039, 8: 1.059 (before the
+// deferral 8 waves were best: 1.26 against 1.33 ms with 4).
 #ifndef KDA_IO_WAVES
 #define KDA_IO_WAVES 4
 #endif
 #ifndef KDA_IO_WAVES_OW
-#define KDA_IO_WAVES_OW 8
+#define KDA_IO_WAVES_OW 4
 #endif
 constexpr int kIoWaves = KDA_IO_WAVES;
 
