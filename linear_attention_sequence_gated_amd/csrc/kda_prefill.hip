@@ -31,6 +31,26 @@
 
 namespace kda {
 
+// DPP lane moves inside rows of 16 lanes (CTRL: row_shl:n = 0x100 + n, row_shr:n
+// = 0x110 + n); a lane whose source falls outside its row reads 0.
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float lane_value(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+// Inclusive prefix sum over a row of 16 lanes: row_shr moves, each unmasked
+// (a lane whose source lies before its row reads 0).  The moves must stay
+// unconditional: a select around one let the compiler run it under a lane
+// mask, and a DPP read from a masked-off lane returns 0.
+__device__ __forceinline__ float row_scan16(float x) {
+    x += dpp<0x111>(x);
+    x += dpp<0x112>(x);
+    x += dpp<0x114>(x);
+    x += dpp<0x118>(x);
+    return x;
+}
+
 // log2(alpha) is floored here: alpha below 2^-40 is treated as 2^-40, a
 // relative change of the decayed terms far below fp32 resolution.
 constexpr float kLog2Floor = -40.f;
@@ -248,6 +268,9 @@ void kda_intra_kernel(const PrefillArgs a) {
     // All loads go out before any is used: tokens past the chunk's end (and
     // threads outside the mapping) read an in-bounds row (the chunk's first
     // token, channel group 0) and are masked after the loads land.
+    // beta of token tid goes out with the other inputs (a row past the chunk's
+    // end reads its first token and is masked where sbeta is written)
+    const float braw = a.beta[(pos.tok0 + (tid < valid ? tid : 0)) * H + h];
     float kr[4][8], qr[4][8], al[4][8];
     Raw8<In> vraw[4];   // v as loaded; converted where V^T is staged
     {
@@ -354,7 +377,7 @@ void kda_intra_kernel(const PrefillArgs a) {
         }
     }
     if (tid < C) {
-        float b = tid < valid ? a.beta[(pos.tok0 + tid) * H + h] : 0.f;
+        float b = tid < valid ? braw : 0.f;
         if (kOpts && a.fuse_inputs && tid < valid) b = sigmoid(b);
         sbeta[tid] = b;
     }
@@ -377,10 +400,14 @@ void kda_intra_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float incl = run[e];
+            if constexpr (I::NSEG == 16) {   // a channel group is one DPP row
+                incl = row_scan16(incl);
+            } else {
 #pragma unroll
-            for (int d = 1; d < I::NSEG; d <<= 1) {
-                const float t = __shfl_up(incl, d, I::NSEG);
-                if (sgi >= d) incl += t;
+                for (int d = 1; d < I::NSEG; d <<= 1) {
+                    const float t = __shfl_up(incl, d, I::NSEG);
+                    if (sgi >= d) incl += t;
+                }
             }
             off[e] = incl - run[e];
             tot[e] = __shfl(incl, I::NSEG - 1, I::NSEG);
@@ -398,14 +425,22 @@ void kda_intra_kernel(const PrefillArgs a) {
         // decay range of each 16-token block (exponent at its first token minus
         // at its last), maximised over the wave's blocks and channels; the last
         // segment of a block is 3 lanes above its first
+        // (lanes with sp == 0 count, by an arithmetic mask rather than a branch,
+        // which would mask off the lanes the row_shl:3 move reads)
         float mx = 0.f;
+        const float first = fmaxf(1.f - (float)sp, 0.f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float ge = __shfl_down(off[e] + lg[3][e], 3, I::NSEG);
-            if (sp == 0) mx = fmaxf(mx, off[e] + lg[0][e] - ge);
+            const float ge = dpp<0x103>(off[e] + lg[3][e]);   // row_shl:3, 3 lanes above
+            mx = fmaxf(mx, (off[e] + lg[0][e] - ge) * first);
         }
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+        // in-row maxima (row_shr, lanes below a row's start read 0 <= mx), then
+        // the four rows' last lanes
+        mx = fmaxf(mx, dpp<0x111>(mx));
+        mx = fmaxf(mx, dpp<0x112>(mx));
+        mx = fmaxf(mx, dpp<0x114>(mx));
+        mx = fmaxf(mx, dpp<0x118>(mx));
+        mx = fmaxf(fmaxf(lane_value(mx, 15), lane_value(mx, 31)), fmaxf(lane_value(mx, 47), lane_value(mx, 63)));
         if (lane == 0) swmax[wave] = mx;
     }
     lds_barrier();
