@@ -51,6 +51,8 @@ __device__ __forceinline__ float row_scan16(float x) {
     return x;
 }
 
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+
 // log2(alpha) is floored here: alpha below 2^-40 is treated as 2^-40, a
 // relative change of the decayed terms far below fp32 resolution.
 constexpr float kLog2Floor = -40.f;
@@ -459,7 +461,11 @@ void kda_intra_kernel(const PrefillArgs a) {
             dst[e] = __builtin_amdgcn_exp2f(fminf(Gs[Rb * DK + c] - Gs[Ib * DK + c] + hI - hR, 0.f));
         }
     }
-    if (p1) {
+    // The factor loops are instantiated once per path (fast is uniform over the
+    // workgroup): a per-element choice was if-converted, so both paths' exp2
+    // and products ran for every element.
+    auto factor_phase = [&](auto path) {
+        constexpr bool fast = decltype(path)::value;
         float sh[8], gb[8], pre[8], tail[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -542,6 +548,10 @@ void kda_intra_kernel(const PrefillArgs a) {
                 f32x4{__builtin_amdgcn_exp2f(tot[4]), __builtin_amdgcn_exp2f(tot[5]), __builtin_amdgcn_exp2f(tot[6]),
                       __builtin_amdgcn_exp2f(tot[7])};
         }
+    };
+    if (p1) {
+        if (fast) factor_phase(BoolTag<true>{});
+        else factor_phase(BoolTag<false>{});
     }
     lds_barrier();
 
