@@ -747,33 +747,51 @@ void kda_intra_kernel(const PrefillArgs a) {
         *reinterpret_cast<Q*>(Pf + Frag<T>::off(ct, ut, ln, C)) = make_quad<T>(v4);
     }
     lds_barrier();
-    // W^T(channel tile t, token tile tb) = Ktilde^T Tm^T: lane holds W[16tb+cl][16t+4g+j]
-#pragma unroll KDA_WU_UNROLL
-    for (int tile = wave; tile < NQK * NB; tile += 4) {
-        const int t = tile / NB, tb = tile % NB;
-        Q aq[NB], bq[NB];
+    // W^T(channel tile t, token tile tb) = Ktilde^T Tm^T: lane holds W[16tb+cl][16t+4g+j].
+    // The waves take every fourth tile and 4 is a multiple of NB, so a wave's
+    // token tile tb is fixed: its Tm rows are read from LDS once.
+    {
+        const int tb = wave % NB;
+        Q bq[NB];
 #pragma unroll
-        for (int u = 0; u < NB; ++u) {
-            aq[u] = *reinterpret_cast<const Q*>(KtT + (16 * t + cl) * LD_CT + 16 * u + 4 * g);
-            bq[u] = *reinterpret_cast<const Q*>(Tb + (16 * tb + cl) * LD_CT + 16 * u + 4 * g);
+        for (int u = 0; u < NB; ++u) bq[u] = *reinterpret_cast<const Q*>(Tb + (16 * tb + cl) * LD_CT + 16 * u + 4 * g);
+#pragma unroll KDA_WU_UNROLL
+        for (int t = wave / NB; t < NQK; t += 4 / NB) {
+            Q aq[NB];
+#pragma unroll
+            for (int u = 0; u < NB; ++u) aq[u] = *reinterpret_cast<const Q*>(KtT + (16 * t + cl) * LD_CT + 16 * u + 4 * g);
+            const f32x4 res = mma_quads_upto(aq, bq, tb, zero4());
+            *reinterpret_cast<Q*>(Wf + Frag<T>::off(tb, t, lane, DK)) = make_quad<T>(res);
         }
-        const f32x4 res = mma_quads_upto(aq, bq, tb, zero4());
-        *reinterpret_cast<Q*>(Wf + Frag<T>::off(tb, t, lane, DK)) = make_quad<T>(res);
     }
-    // Utilde(token tile tb, value tile s) = Tm V: lane holds U[16tb+4g+j][16s+cl]
-    const int NSV = DV / 16;
-#pragma unroll KDA_WU_UNROLL
-    for (int tile = wave; tile < NB * NSV; tile += 4) {
-        const int tb = tile / NSV, s = tile % NSV;
-        Q aq[NB], bq[NB];
+    // Utilde(token tile tb, value tile s) = Tm V: lane holds U[16tb+4g+j][16s+cl].
+    // A wave owns value tiles s = wave, wave + 4 (V^T rows read once) and walks
+    // the token tiles (Tm rows read once per tile).
+    {
+        const int NSV = DV / 16;
+        constexpr int kSW = (I::kDvMax / 16 + 3) / 4;   // value tiles per wave
+        Q vq[kSW][NB];
 #pragma unroll
-        for (int u = 0; u < NB; ++u) {
-            aq[u] = *reinterpret_cast<const Q*>(Tb + (16 * tb + cl) * LD_CT + 16 * u + 4 * g);
-            bq[u] = *reinterpret_cast<const Q*>(VT + (16 * s + cl) * LD_CT + 16 * u + 4 * g);
+        for (int j = 0; j < kSW; ++j) {
+            const int sv = min(wave + 4 * j, NSV - 1);   // in bounds; unused past NSV
+#pragma unroll
+            for (int u = 0; u < NB; ++u) vq[j][u] = *reinterpret_cast<const Q*>(VT + (16 * sv + cl) * LD_CT + 16 * u + 4 * g);
         }
-        const f32x4 res = mma_quads_upto(aq, bq, tb, zero4());
-        T* Us = reinterpret_cast<T*>(blk + cb.u_slice(s));
-        *reinterpret_cast<Q*>(Us + (lane * NB + tb) * 4) = make_quad<T>(res);
+#pragma unroll KDA_WU_UNROLL
+        for (int tb = 0; tb < NB; ++tb) {
+            Q aq[NB];
+#pragma unroll
+            for (int u = 0; u < NB; ++u) aq[u] = *reinterpret_cast<const Q*>(Tb + (16 * tb + cl) * LD_CT + 16 * u + 4 * g);
+#pragma unroll
+            for (int j = 0; j < kSW; ++j) {
+                const int sv = wave + 4 * j;
+                if (sv < NSV) {
+                    const f32x4 res = mma_quads_upto(aq, vq[j], tb, zero4());
+                    T* Us = reinterpret_cast<T*>(blk + cb.u_slice(sv));
+                    *reinterpret_cast<Q*>(Us + (lane * NB + tb) * 4) = make_quad<T>(res);
+                }
+            }
+        }
     }
 }
 
