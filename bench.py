@@ -62,8 +62,8 @@ KERNEL_SOURCES = {
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {  # kernel: (sources, sha256[:16] of the sources, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "kda_intra_kernel": ("prefill", "6c3d068ff9e5da85", 1343693.0, 2378742.0),
-    "kda_inter_kernel": ("prefill", "6c3d068ff9e5da85", 1196129.0, 527788.0),
+    "kda_intra_kernel": ("prefill", "6cefa0dd67cfcba9", 1343683.0, 2376349.0),
+    "kda_inter_kernel": ("prefill", "6cefa0dd67cfcba9", 1196125.0, 527831.0),
     "kda_decode_kernel": ("decode", "54568d8d160e2b8b", 267573.0, 526544.0),
 }
 
