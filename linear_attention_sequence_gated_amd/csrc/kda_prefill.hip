@@ -1470,13 +1470,48 @@ __global__ __launch_bounds__(256) void kda_gate_epilogue(const PrefillArgs a, co
     if (row >= rows) return;
     const int c4 = (int)(t % CG) * 4;
     const float* ps = a.part_scratch + row * NS;
-    float ss = 0.f;
-    for (int sl = 0; sl < NS; ++sl) ss += ps[sl];
-    const float inv = rsqrtf(ss / (float)DV + a.norm_eps);
-    f32x4 o4 = *reinterpret_cast<const f32x4*>(a.o_scratch + row * DV + c4) * inv;
     const In* __restrict__ gt = reinterpret_cast<const In*>(a.gate) + row * DV + c4;
+    // vector loads where the layout allows (the partial sums of a row are 32-byte
+    // aligned in the workspace when NS is a multiple of 4; gate and weight
+    // pointers need only element alignment, so they are tested, uniformly)
+    const f32x4 o_raw = *reinterpret_cast<const f32x4*>(a.o_scratch + row * DV + c4);
+    f32x4 gv, wv = f32x4{1.f, 1.f, 1.f, 1.f};
+    if ((reinterpret_cast<uintptr_t>(a.gate) & (4 * sizeof(In) - 1)) == 0) {
+        if constexpr (sizeof(In) == 4) {
+            gv = *reinterpret_cast<const f32x4*>(gt);
+        } else {
+            const bf16x4 g4 = *reinterpret_cast<const bf16x4*>(gt);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o4[j] *= (a.norm_w ? a.norm_w[c4 + j] : 1.f) * sigmoid(load_as_float(gt, j));
+            for (int j = 0; j < 4; ++j) gv[j] = (float)g4[j];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) gv[j] = load_as_float(gt, j);
+    }
+    if (a.norm_w) {
+        if ((reinterpret_cast<uintptr_t>(a.norm_w) & 15) == 0) {
+            wv = *reinterpret_cast<const f32x4*>(a.norm_w + c4);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wv[j] = a.norm_w[c4 + j];
+        }
+    }
+    float ss = 0.f;
+    if (NS % 4 == 0) {
+        for (int sl = 0; sl < NS; sl += 4) {   // in a fixed order: the same sum for every column
+            const f32x4 p4 = *reinterpret_cast<const f32x4*>(ps + sl);
+            ss += p4[0];
+            ss += p4[1];
+            ss += p4[2];
+            ss += p4[3];
+        }
+    } else {
+        for (int sl = 0; sl < NS; ++sl) ss += ps[sl];
+    }
+    const float inv = rsqrtf(ss / (float)DV + a.norm_eps);
+    f32x4 o4 = o_raw * inv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o4[j] *= wv[j] * sigmoid(gv[j]);
     if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + row * DV + c4, o4);
     else store4(reinterpret_cast<__bf16*>(a.o) + row * DV + c4, o4);
 }
