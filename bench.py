@@ -62,9 +62,9 @@ KERNEL_SOURCES = {
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {  # kernel: (sources, sha256[:16] of the sources, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "kda_intra_kernel": ("prefill", "6cefa0dd67cfcba9", 1343683.0, 2376349.0),
-    "kda_inter_kernel": ("prefill", "6cefa0dd67cfcba9", 1196125.0, 527831.0),
-    "kda_decode_kernel": ("decode", "54568d8d160e2b8b", 267573.0, 526544.0),
+    "kda_intra_kernel": ("prefill", "fbb523508f9c646f", 1343681.0, 2376360.0),
+    "kda_inter_kernel": ("prefill", "fbb523508f9c646f", 1196124.0, 527664.0),
+    "kda_decode_kernel": ("decode", "8169c036a2227051", 267576.0, 526425.0),
 }
 
 

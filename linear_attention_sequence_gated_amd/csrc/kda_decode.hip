@@ -15,10 +15,11 @@
 // column group cg) owns float4 columns [4cg, 4cg+4) of the block in rows r0,
 // r0 + RPP, ... and keeps them in registers between the reduction and the
 // write-back.  The write-back uses nontemporal (streaming) stores.  On MI355X
-// the in-place step over 512 MiB of state measured 6.4 TB/s with whole
-// 128 x 128 states per 512-thread workgroup and streaming stores, against
-// 5.1 TB/s with ordinary stores; streaming loads, smaller column blocks and
-// other workgroup sizes were slower.
+// the in-place step over 512 MiB of state measured 6.5 TB/s with whole
+// 128 x 128 states per 256-thread workgroup (16 float4 of state per thread)
+// and streaming stores (512 threads: 6.2-6.3 TB/s; 1,024: 6.4; 128: 5.5),
+// against 5.1 TB/s with ordinary stores; streaming loads and smaller column
+// blocks (64 columns: 5.0 TB/s) were slower.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,7 +32,7 @@ namespace kda {
 #define KDA_DECODE_COLS 128
 #endif
 #ifndef KDA_DECODE_THREADS
-#define KDA_DECODE_THREADS 512
+#define KDA_DECODE_THREADS 256
 #endif
 #ifndef KDA_DECODE_NT_LOAD
 #define KDA_DECODE_NT_LOAD 0
