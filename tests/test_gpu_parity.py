@@ -564,15 +564,24 @@ def test_prefill_options_with_checkpoints():
 
 # --- output norm and gate inside the inter-chunk kernel -------------------------
 
-def _gate_case(inp, chunk, tol, label, o_dtype=torch.float32, **opts):
+def _gate_case(inp, chunk, tol, label, o_dtype=torch.float32, misalign=False, **opts):
     say(f"[case] prefill gate {label} chunk={chunk} {inp['q'].dtype} {opts}")
     g = torch.Generator().manual_seed(int(inp["q"].shape[1]) + chunk)
     gate = torch.randn(inp["v"].shape, generator=g).to(inp["q"].dtype)
     w = torch.rand(inp["v"].shape[-1], generator=g) + 0.5
     eps = 1e-5
     d = to_dev(inp)
+    gd, wd = gate.cuda(), w.cuda()
+    if misalign:   # one element past an aligned allocation: only element alignment
+        gbuf = torch.empty(gate.numel() + 1, dtype=gate.dtype, device="cuda")
+        gbuf[1:].copy_(gd.reshape(-1))
+        gd = gbuf[1:].view(gate.shape)
+        wbuf = torch.empty(w.numel() + 1, device="cuda")
+        wbuf[1:].copy_(wd)
+        wd = wbuf[1:]
+        assert gd.data_ptr() % (4 * gate.element_size()) != 0 and wd.data_ptr() % 16 != 0
     o, S = kda.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"],
-                         chunk_size=chunk, o_dtype=o_dtype, gate=gate.cuda(), norm_weight=w.cuda(), norm_eps=eps,
+                         chunk_size=chunk, o_dtype=o_dtype, gate=gd, norm_weight=wd, norm_eps=eps,
                          **opts)
     torch.cuda.synchronize()
     cu = inp["cu_seqlens"]
@@ -609,6 +618,17 @@ def test_prefill_gate_bf16_output_is_rounded_fp32():
     o32 = _gate_case(inp, 64, TOL[torch.bfloat16], "fp32 out").cpu()
     o16 = _gate_case(inp, 64, 4e-2, "bf16 out", o_dtype=torch.bfloat16).cpu()
     assert torch.equal(o16.view(torch.int16), o32.to(torch.bfloat16).view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_prefill_gate_unaligned_gate_and_weight(dtype):
+    # few (sequence, head) pairs take the split path, whose epilogue reads the
+    # gate logits and the norm weight as vectors only when the pointers allow:
+    # offset views take its element-wise loads, with the same result
+    inp = workloads.make_inputs(1, 150, 2, 128, 128, dtype, s0_std=0.02, seed=506)
+    oa = _gate_case(inp, 64, TOL[dtype], "aligned").cpu()
+    om = _gate_case(inp, 64, TOL[dtype], "gate and weight one element off", misalign=True).cpu()
+    assert torch.equal(oa, om)
 
 
 def test_prefill_gate_many_units_fused_in_inter_kernel():
