@@ -30,8 +30,6 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA prefill tokens/s + decode state GB/s (dk=dv=128), % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
-PREFILL_CFG = 2
-DECODE_CFG = 3
 
 
 def algorithmic(dk, dv, chunk, qkv_bytes=2, o_bytes=2):
@@ -128,15 +126,16 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one MI355X only (--gpus {args.gpus}, WORLD_SIZE {world}): the KDA "
-              "hot path here is a single-GPU build; see DESIGN.md for how it would shard.",
-              file=sys.stderr)
+        print(f"bench.py measures one MI355X only (--gpus {args.gpus}, WORLD_SIZE {world}): this KDA "
+              "library runs on one GPU; heads, sequences and value columns would shard across GPUs "
+              "with no exchange.", file=sys.stderr)
         sys.exit(2)
 
     import torch
 
     import linear_attention_sequence_gated_amd as kda
     import workloads
+    PREFILL_CFG, DECODE_CFG = workloads.LONG_CONTEXT_PREFILL, workloads.DECODE
     from linear_attention_sequence_gated_amd import build as kbuild
 
     if not os.path.exists(kbuild.LIB):

@@ -76,28 +76,28 @@ def check(inp, chunk, tol, scale=1.0, label=""):
 
 # --- the five workloads ------------------------------------------------------
 
-def test_config0_tiny_fp32():
-    w = workloads.CONFIGS[0]
-    check(workloads.config_inputs(0), w.chunk, TOL[w.dtype], label="config0")
+def test_tiny_fp32_workload():
+    w = workloads.CONFIGS[workloads.TINY_FP32]
+    check(workloads.config_inputs(workloads.TINY_FP32), w.chunk, TOL[w.dtype], label=w.name)
 
 
-def test_config1_batched_bf16():
-    w = workloads.CONFIGS[1]
-    inp = workloads.config_inputs(1)
-    check(inp, w.chunk, TOL[w.dtype], label="config1")
+def test_batched_prefill_bf16():
+    w = workloads.CONFIGS[workloads.BATCHED_PREFILL]
+    inp = workloads.config_inputs(workloads.BATCHED_PREFILL)
+    check(inp, w.chunk, TOL[w.dtype], label=w.name)
     check_bf16_output(inp, w.chunk)
 
 
 @pytest.mark.timeout(900)
-def test_config2_long_context_sampled_heads():
+def test_long_context_prefill_sampled_heads():
     """Full-size launch (B1 H32 T65536); the oracle recomputes heads 0, 17 and 31."""
-    w = workloads.CONFIGS[2]
-    say("[case] config2 generating inputs")
-    inp = workloads.config_inputs(2)
-    say("[case] config2 GPU prefill")
+    w = workloads.CONFIGS[workloads.LONG_CONTEXT_PREFILL]
+    say("[case] long-context-prefill generating inputs")
+    inp = workloads.config_inputs(workloads.LONG_CONTEXT_PREFILL)
+    say("[case] long-context-prefill GPU prefill")
     og, Sg = gpu_prefill(inp, w.chunk)
     for h in (0, 17, 31):
-        say(f"[case] config2 oracle head {h}")
+        say(f"[case] long-context-prefill oracle head {h}")
         oo, So = oracle_prefill(inp, heads=(h, h + 1))
         eo, es = rel_err(og[:, :, h:h + 1], oo), rel_err(Sg[:, h:h + 1], So)
         say(f"    head {h}: err o={eo:.3e} S={es:.3e}")
@@ -105,15 +105,15 @@ def test_config2_long_context_sampled_heads():
 
 
 @pytest.mark.timeout(1200)
-def test_config4_packed_varlen_resume_sampled_heads():
+def test_packed_varlen_resume_sampled_heads():
     """64 packed sequences (lengths U[1, 32768]), S0 != 0; the oracle recomputes heads 3 and 12."""
-    w = workloads.CONFIGS[4]
-    say("[case] config4 generating inputs")
-    inp = workloads.config_inputs(4)
-    say(f"[case] config4 GPU prefill, T={inp['q'].shape[1]}")
+    w = workloads.CONFIGS[workloads.PACKED_VARLEN_RESUME]
+    say("[case] packed-varlen-resume generating inputs")
+    inp = workloads.config_inputs(workloads.PACKED_VARLEN_RESUME)
+    say(f"[case] packed-varlen-resume GPU prefill, T={inp['q'].shape[1]}")
     og, Sg = gpu_prefill(inp, w.chunk)
     for h in (3, 12):
-        say(f"[case] config4 oracle head {h}")
+        say(f"[case] packed-varlen-resume oracle head {h}")
         oo, So = oracle_prefill(inp, heads=(h, h + 1))
         eo, es = rel_err(og[:, :, h:h + 1], oo), rel_err(Sg[:, h:h + 1], So)
         say(f"    head {h}: err o={eo:.3e} S={es:.3e}")
@@ -132,12 +132,12 @@ def _decode_run(inp, steps, scale=1.0, o_dtype=torch.float32):
 
 
 @pytest.mark.timeout(600)
-def test_config3_decode_128_steps_sampled_sequences():
+def test_decode_128_steps_sampled_sequences():
     """256 sequences x H32, 128 in-place steps; the oracle recomputes sequences 0, 101 and 255."""
-    w = workloads.CONFIGS[3]
-    say("[case] config3 generating inputs")
+    w = workloads.CONFIGS[workloads.DECODE]
+    say("[case] decode generating inputs")
     inp = workloads.decode_inputs(3)
-    say("[case] config3 GPU decode x128")
+    say("[case] decode GPU decode x128")
     og, Sg = _decode_run(inp, w.decode_steps)
     for n in (0, 101, 255):
         sub = {k: (v[:, n:n + 1] if k != "S0" else v[n:n + 1]) for k, v in inp.items()}

@@ -15,7 +15,7 @@ from oracle import kda_oracle
 
 
 def test_bf16_rounding_of_exact_output_exceeds_bound():
-    inp = workloads.config_inputs(1)
+    inp = workloads.config_inputs(workloads.BATCHED_PREFILL)
     o, _ = kda_oracle.forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
                               heads=(0, 2))
     ob = torch.from_numpy(o).to(torch.bfloat16).double().numpy()

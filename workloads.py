@@ -55,6 +55,9 @@ class Workload:
     decode_seqs: int = 0       # N sequences of the decode workload
 
 
+# The workloads by name (the value is also the seed offset of each).
+TINY_FP32, BATCHED_PREFILL, LONG_CONTEXT_PREFILL, DECODE, PACKED_VARLEN_RESUME = 0, 1, 2, 3, 4
+
 CONFIGS = {
     0: Workload("tiny-fp32", 0, batch=1, seqlen=64, heads=1, dk=16, dv=16, chunk=16,
                 dtype=torch.float32, alpha_mu=3.0, s0_std=0.0),
