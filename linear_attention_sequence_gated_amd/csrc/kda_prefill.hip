@@ -480,23 +480,50 @@ void kda_intra_kernel(const PrefillArgs a) {
         // backward pass: Kbar = k 2^{g_C - g_r} (suffix products), straight to the workspace
         {
             const int ut = sgi >> 2, gq = sgi & 3;
+            f32x4 kbq[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int c = 8 * cg + e;
-                float kb4[4];
                 if (fast) {
                     float sf = tail[e];
 #pragma unroll
                     for (int u = 3; u >= 0; --u) {
-                        kb4[u] = kr[u][e] * sf;
+                        kbq[e][u] = kr[u][e] * sf;
                         sf *= al[u][e];
                     }
                 } else {
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        kb4[u] = kr[u][e] * __builtin_amdgcn_exp2f(fminf(tot[e] - (off[e] + lg[u][e]), 0.f));
+                        kbq[e][u] = kr[u][e] * __builtin_amdgcn_exp2f(fminf(tot[e] - (off[e] + lg[u][e]), 0.f));
                 }
-                store_q<T>(Kbf + Frag<T>::off(c >> 4, ut, 16 * gq + (c & 15), C), f32x4{kb4[0], kb4[1], kb4[2], kb4[3]});
+            }
+            if constexpr (sizeof(T) == 2 && I::NSEG == 16) {
+                // a fragment lane's 16 bytes hold the token quads ut and ut ^ 1 of one
+                // channel, which lie with this thread and the one 4 lanes away (same DPP
+                // row).  Per channel pair the even-ut thread writes channel e0 and the
+                // odd-ut thread channel e1, each fetching the partner's quad by DPP
+                // (moves unconditional, the choice by select).
+                const bool odd = (ut & 1) != 0;
+#pragma unroll
+                for (int e0 = 0; e0 < 8; e0 += 2) {
+                    const Q q0 = make_quad<T>(kbq[e0]), q1 = make_quad<T>(kbq[e0 + 1]);
+                    typedef int i32x2 __attribute__((ext_vector_type(2)));
+                    const i32x2 w0 = __builtin_bit_cast(i32x2, q0), w1 = __builtin_bit_cast(i32x2, q1);
+                    i32x2 up, dn;   // partner's e0 quad (from 4 lanes above), e1 quad (from 4 below)
+                    up[0] = __builtin_amdgcn_update_dpp(0, w0[0], 0x104, 0xf, 0xf, true);
+                    up[1] = __builtin_amdgcn_update_dpp(0, w0[1], 0x104, 0xf, 0xf, true);
+                    dn[0] = __builtin_amdgcn_update_dpp(0, w1[0], 0x114, 0xf, 0xf, true);
+                    dn[1] = __builtin_amdgcn_update_dpp(0, w1[1], 0x114, 0xf, 0xf, true);
+                    typedef int i32x4 __attribute__((ext_vector_type(4)));
+                    const i32x4 v = odd ? i32x4{dn[0], dn[1], w1[0], w1[1]} : i32x4{w0[0], w0[1], up[0], up[1]};
+                    const int c = 8 * cg + e0 + (odd ? 1 : 0);
+                    *reinterpret_cast<i32x4*>(Kbf + Frag<T>::off(c >> 4, ut & ~1, 16 * gq + (c & 15), C)) = v;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int c = 8 * cg + e;
+                    store_q<T>(Kbf + Frag<T>::off(c >> 4, ut, 16 * gq + (c & 15), C), kbq[e]);
+                }
             }
         }
         // forward pass: prefix products give the row / column factors and 2^{g_r}
