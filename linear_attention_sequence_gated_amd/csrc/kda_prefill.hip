@@ -557,11 +557,33 @@ void kda_intra_kernel(const PrefillArgs a) {
                 store8(Aq + r * LD_ROW + 8 * cg, aq);
                 store8(Bd + r * LD_ROW + 8 * cg, bd);
             }
+            if constexpr (sizeof(T) == 2 && I::NSEG == 16 && I::NCG % 4 == 0) {
+                // (four channel groups per wave, so every lane has its partner)
+                // Qtilde quads of token r, channel groups 2cg and 2cg + 1.  A fragment
+                // lane's 16 bytes hold the quads of groups a4 and a4 + 4, i.e. of this
+                // thread and the one 32 lanes away (channel group cg +- 2): the lower
+                // lane writes the slot of its group 2cg, the upper lane that of 2cg + 1,
+                // each taking the partner's quad from one permlane32 swap per dword.
+                typedef int i32x2 __attribute__((ext_vector_type(2)));
+                typedef int i32x4 __attribute__((ext_vector_type(4)));
+                const bool upper = (cg & 2) != 0;
+                const i32x2 h0 = __builtin_bit_cast(i32x2, make_quad<T>(f32x4{qt[0], qt[1], qt[2], qt[3]}));
+                const i32x2 h1 = __builtin_bit_cast(i32x2, make_quad<T>(f32x4{qt[4], qt[5], qt[6], qt[7]}));
+                const auto s0 = __builtin_amdgcn_permlane32_swap(h0[0], h1[0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(h0[1], h1[1], false, false);
+                // lower lanes: s*[1] is the upper partner's group-2cg quad; upper lanes:
+                // s*[0] is the lower partner's group-(2cg + 1) quad
+                const i32x4 v = upper ? i32x4{(int)s0[0], (int)s1[0], h1[0], h1[1]}
+                                      : i32x4{h0[0], h0[1], (int)s0[1], (int)s1[1]};
+                const int a4 = 2 * (upper ? cg - 2 : cg) + (upper ? 1 : 0);   // the slot's even group
+                *reinterpret_cast<i32x4*>(Qf + Frag<T>::off(r >> 4, a4 >> 2, 16 * (a4 & 3) + (r & 15), DK)) = v;
+            } else {
 #pragma unroll
-            for (int hq = 0; hq < 2; ++hq) {  // Qtilde quads: token r, channel groups 2cg, 2cg+1
-                const int a4 = 2 * cg + hq, ut = a4 >> 2, gq = a4 & 3;
-                store_q<T>(Qf + Frag<T>::off(r >> 4, ut, 16 * gq + (r & 15), DK),
-                           f32x4{qt[4 * hq], qt[4 * hq + 1], qt[4 * hq + 2], qt[4 * hq + 3]});
+                for (int hq = 0; hq < 2; ++hq) {  // Qtilde quads: token r, channel groups 2cg, 2cg+1
+                    const int a4 = 2 * cg + hq, ut = a4 >> 2, gq = a4 & 3;
+                    store_q<T>(Qf + Frag<T>::off(r >> 4, ut, 16 * gq + (r & 15), DK),
+                               f32x4{qt[4 * hq], qt[4 * hq + 1], qt[4 * hq + 2], qt[4 * hq + 3]});
+                }
             }
         }
 #pragma unroll

@@ -164,6 +164,9 @@ SHAPES = [
     (1, 80, 2, 64, 128, 16, torch.bfloat16, True),
     (1, 90, 2, 16, 64, 32, torch.bfloat16, True),
     (1, 150, 1, 16, 32, 64, torch.bfloat16, False),
+    # bf16, chunk 64, four channel groups in one wave: the paired 16-byte
+    # workspace stores of the intra-chunk kernel with the fewest groups
+    (1, 100, 2, 32, 64, 64, torch.bfloat16, True),
 ]
 
 
