@@ -53,6 +53,15 @@ __device__ __forceinline__ float row_scan16(float x) {
 
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 
+// Two fp16 quads that are adjacent in memory (the halves of one 16-byte
+// fragment slot) stored with one 16-byte write.
+__device__ __forceinline__ void store_pair(_Float16* p, const f32x4& lo, const f32x4& hi) {
+    const f16x4 a = make_quad<_Float16>(lo), b = make_quad<_Float16>(hi);
+    *reinterpret_cast<f16x8*>(p) = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+
+
 // log2(alpha) is floored here: alpha below 2^-40 is treated as 2^-40, a
 // relative change of the decayed terms far below fp32 resolution.
 constexpr float kLog2Floor = -40.f;
@@ -789,11 +798,21 @@ void kda_intra_kernel(const PrefillArgs a) {
         for (int e = 0; e < 8; ++e)
             store_q<T>(VT + (8 * cgv + e) * LD_CT + 4 * sgv, f32x4{vr[0][e], vr[1][e], vr[2][e], vr[3][e]});
     }
-    for (int e = tid; e < NB * NB * 64; e += I::kThreads) {
-        const int ct = e / (NB * 64), ut = (e / 64) % NB, ln = e & 63;
-        const int r = 16 * ct + (ln & 15), i0 = 16 * ut + 4 * (ln >> 4);
-        const f32x4 v4 = ut <= ct ? *reinterpret_cast<const f32x4*>(Pm + r * LD_F + i0) : zero4();
-        *reinterpret_cast<Q*>(Pf + Frag<T>::off(ct, ut, ln, C)) = make_quad<T>(v4);
+    if constexpr (sizeof(T) == 2 && NB % 2 == 0) {   // both quads of a 16-byte slot per thread
+        for (int e = tid; e < NB * (NB / 2) * 64; e += I::kThreads) {
+            const int ct = e / (NB / 2 * 64), ut = 2 * ((e / 64) % (NB / 2)), ln = e & 63;
+            const int r = 16 * ct + (ln & 15), i0 = 16 * ut + 4 * (ln >> 4);
+            const f32x4 va = ut <= ct ? *reinterpret_cast<const f32x4*>(Pm + r * LD_F + i0) : zero4();
+            const f32x4 vb = ut + 1 <= ct ? *reinterpret_cast<const f32x4*>(Pm + r * LD_F + i0 + 16) : zero4();
+            store_pair(reinterpret_cast<_Float16*>(Pf) + Frag<T>::off(ct, ut, ln, C), va, vb);
+        }
+    } else {
+        for (int e = tid; e < NB * NB * 64; e += I::kThreads) {
+            const int ct = e / (NB * 64), ut = (e / 64) % NB, ln = e & 63;
+            const int r = 16 * ct + (ln & 15), i0 = 16 * ut + 4 * (ln >> 4);
+            const f32x4 v4 = ut <= ct ? *reinterpret_cast<const f32x4*>(Pm + r * LD_F + i0) : zero4();
+            *reinterpret_cast<Q*>(Pf + Frag<T>::off(ct, ut, ln, C)) = make_quad<T>(v4);
+        }
     }
     lds_barrier();
     // W^T(channel tile t, token tile tb) = Ktilde^T Tm^T: lane holds W[16tb+cl][16t+4g+j].
