@@ -60,9 +60,9 @@ KERNEL_SOURCES = {
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {  # kernel: (sources, sha256[:16] of the sources, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "kda_intra_kernel": ("prefill", "fbb523508f9c646f", 1343681.0, 2376360.0),
-    "kda_inter_kernel": ("prefill", "fbb523508f9c646f", 1196124.0, 527664.0),
-    "kda_decode_kernel": ("decode", "8169c036a2227051", 267576.0, 526425.0),
+    "kda_intra_kernel": ("prefill", "23d7f8f1dde524fd", 1343688.0, 2376261.0),
+    "kda_inter_kernel": ("prefill", "23d7f8f1dde524fd", 1196130.0, 527770.0),
+    "kda_decode_kernel": ("decode", "8169c036a2227051", 267576.0, 526455.0),
 }
 
 
