@@ -60,9 +60,9 @@ KERNEL_SOURCES = {
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {  # kernel: (sources, sha256[:16] of the sources, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "kda_intra_kernel": ("prefill", "23d7f8f1dde524fd", 1343688.0, 2376261.0),
-    "kda_inter_kernel": ("prefill", "23d7f8f1dde524fd", 1196130.0, 527770.0),
-    "kda_decode_kernel": ("decode", "8169c036a2227051", 267576.0, 526455.0),
+    "kda_intra_kernel": ("prefill", "91efdf7be86212ad", 1343686.0, 2376222.0),
+    "kda_inter_kernel": ("prefill", "91efdf7be86212ad", 1196130.0, 526336.0),
+    "kda_decode_kernel": ("decode", "8169c036a2227051", 267576.0, 526420.0),
 }
 
 

@@ -979,9 +979,10 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 // d > 0: the I/O waves also pull the block d chunks ahead of the copy into L2
-// (measured on the long-context workload: d = 2 best, 0 slowest).
+// (long-context workload, current kernel: d = 1 1.047 ms, 2 1.056, 3 1.077;
+// without any prefetch the copies are exposed).
 #ifndef KDA_L2_PREFETCH
-#define KDA_L2_PREFETCH 2
+#define KDA_L2_PREFETCH 1
 #endif
 
 // Copy the 1 KiB units first, first + step, ... of `bytes` (a multiple of
