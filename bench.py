@@ -91,6 +91,18 @@ def roof(bound, amount, seconds, unit, kernel, traffic=None):
             "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel}
 
 
+def cpu_model():
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(inp, heads, target_s=12.0):
     """Oracle tokens/s on a leading slice of the prefill workload, all heads."""
     from oracle import kda_oracle
@@ -108,7 +120,7 @@ def cpu_baseline(inp, heads, target_s=12.0):
     tokens = max(64, tokens // 64 * 64)
     dt = run(tokens)
     return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": kda_oracle.threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"first {tokens} tokens of the prefill workload, all {heads} heads "
                       f"({tokens * heads} token-heads), fp64 token-by-token, {dt:.1f} s"}
 
@@ -237,6 +249,24 @@ def main():
         del ck, gate, al, bl, a_s
     del pre, d
     torch.cuda.empty_cache()
+    if not args.no_variants:
+        # packed variable-length prefill with prefix-cache resume: 64 sequences
+        # (the workload's seeded lengths), H16, nonzero initial states; inputs
+        # drawn on the device with the workload's recipe, o in bf16
+        wp = workloads.CONFIGS[workloads.PACKED_VARLEN_RESUME]
+        log(f"generating {wp.name} inputs on the device")
+        dp = workloads.device_inputs(workloads.PACKED_VARLEN_RESUME, dev)
+        ptok = int(dp["q"].shape[1])
+        pp = kda.Prefill(dp["q"], dp["k"], dp["v"], dp["alpha"], dp["beta"], dp["S0"], dp["cu_seqlens"],
+                         chunk_size=wp.chunk, o_dtype=torch.bfloat16)
+        ms = time_call(pp.run, reps=3)
+        variants["prefill_packed_varlen_resume"] = {
+            "ms": round(ms, 4), "tokens": ptok, "sequences": wp.packed_seqs, "heads": wp.heads,
+            "tokens_per_s": round(ptok / (ms / 1e3), 1),
+            "token_heads_per_s": round(ptok * wp.heads / (ms / 1e3), 1),
+            "workspace_bytes": int(pp.workspace.numel())}
+        del pp, dp
+        torch.cuda.empty_cache()
 
     # ---- decode --------------------------------------------------------------
     wd = workloads.CONFIGS[DECODE_CFG]

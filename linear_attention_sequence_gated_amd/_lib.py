@@ -127,6 +127,20 @@ def _need(cond: bool, what: str) -> None:
         raise ValueError(what)
 
 
+def _on_device(t: torch.Tensor) -> bool:
+    """Whether `t` lives in device memory (the kernels dereference every pointer on the GPU)."""
+    return t.is_cuda
+
+
+def _dense(t: Optional[torch.Tensor], shape, dtype, what: str) -> None:
+    """`t` is None or a contiguous device tensor of exactly `shape` and `dtype`."""
+    if t is None:
+        return
+    _need(tuple(t.shape) == tuple(shape) and t.dtype == dtype and _on_device(t) and t.is_contiguous(),
+          f"{what} must be a contiguous {dtype} device tensor of shape {tuple(shape)}, got "
+          f"{tuple(t.shape)} {t.dtype} on {t.device}{'' if t.is_contiguous() else ' (strided)'}")
+
+
 def chunk_params(q: torch.Tensor, v: torch.Tensor, cu_seqlens: Optional[torch.Tensor],
                  chunk_size: int, scale: float, o_dtype: Optional[torch.dtype] = None) -> ChunkParams:
     B, T, H, dk = q.shape
@@ -167,34 +181,32 @@ class Prefill:
         _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
         _need(alpha.dtype == torch.float32 and beta.dtype == torch.float32, "alpha, beta must be fp32")
         for t in (q, k, v, alpha, beta):
-            _need(t.is_cuda and t.is_contiguous(), "inputs must be contiguous device tensors")
-        n = B if cu_seqlens is None else cu_seqlens.numel() - 1
+            _need(_on_device(t) and t.is_contiguous(), "inputs must be contiguous device tensors")
         if cu_seqlens is not None:
-            _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda, "cu_seqlens: int32 device")
-        if initial_state is not None:
-            _need(initial_state.shape == (n, H, dk, dv) and initial_state.dtype == torch.float32
-                  and initial_state.is_contiguous(), "initial_state must be fp32 [N,H,dk,dv]")
+            _need(cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 2,
+                  "cu_seqlens must be int32 [N+1] with N >= 1")
+            _dense(cu_seqlens, (cu_seqlens.numel(),), torch.int32, "cu_seqlens")
+        n = B if cu_seqlens is None else cu_seqlens.numel() - 1
+        _dense(initial_state, (n, H, dk, dv), torch.float32, "initial_state")
+        _dense(final_state, (n, H, dk, dv), torch.float32, "final_state")
         o_dtype = q.dtype if o_dtype is None else o_dtype
+        _dense(o, v.shape, o_dtype, "o")
+        if ckpt_every:
+            _need(checkpoints is not None and checkpoints.dim() == 5 and checkpoints.shape[0] == n
+                  and checkpoints.shape[2:] == (H, dk, dv) and checkpoints.dtype == torch.float32
+                  and _on_device(checkpoints) and checkpoints.is_contiguous(),
+                  "checkpoints must be fp32 [N, max_ckpts, H, dk, dv]")
+        _dense(gate, v.shape, q.dtype, "gate")
+        _dense(norm_weight, (dv,), torch.float32, "norm_weight")
+        # every check above precedes the first allocation
         if o is None:
             o = torch.empty(v.shape, dtype=o_dtype, device=v.device)
-        _need(o.shape == v.shape and o.dtype == o_dtype and o.is_contiguous(), "o shape/dtype")
         if final_state is None and output_final_state:
             final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
         self.params = chunk_params(q, v, cu_seqlens, chunk_size, scale, o_dtype)
         self.o, self.final_state = o, final_state
         self.options = None
         self.checkpoints = checkpoints
-        if ckpt_every:
-            _need(checkpoints is not None and checkpoints.dim() == 5 and checkpoints.shape[0] == n
-                  and checkpoints.shape[2:] == (H, dk, dv) and checkpoints.dtype == torch.float32
-                  and checkpoints.is_cuda and checkpoints.is_contiguous(),
-                  "checkpoints must be fp32 [N, max_ckpts, H, dk, dv]")
-        if gate is not None:
-            _need(gate.shape == v.shape and gate.dtype == q.dtype and gate.is_cuda and gate.is_contiguous(),
-                  "gate must be [B,T,H,dv] in the dtype of q")
-        if norm_weight is not None:
-            _need(norm_weight.shape == (dv,) and norm_weight.dtype == torch.float32 and norm_weight.is_cuda,
-                  "norm_weight must be fp32 [dv]")
         if ckpt_every or decay_floor or alpha_scalar or fuse_inputs or gate is not None or norm_weight is not None:
             self.options = ChunkOptions(checkpoints=checkpoints.data_ptr() if ckpt_every else None,
                                         ckpt_every=int(ckpt_every),
@@ -279,23 +291,19 @@ def decode_step(q, k, v, alpha, beta, state, scale: float = 1.0, o=None, stream=
         _need(state.shape == (N, H, dk, dv), "state must be [N,H,dk,dv]")
     else:
         _need(state.dim() == 4 and state.shape[1:] == (H, dk, dv), "state pool must be [P,H,dk,dv]")
-        _need(state_slots.shape == (N,) and state_slots.dtype == torch.int32 and state_slots.is_cuda,
-              "state_slots must be int32 [N] on the device")
+        _dense(state_slots, (N,), torch.int32, "state_slots")
     _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
     _need(alpha.dtype == torch.float32 and beta.dtype == torch.float32
           and state.dtype == torch.float32, "alpha, beta, state must be fp32")
-    for t in (q, k, v, alpha, beta, state):
-        _need(t.is_cuda and t.is_contiguous(), "inputs must be contiguous device tensors")
-    if gate is not None:
-        _need(gate.shape == v.shape and gate.dtype == q.dtype and gate.is_cuda and gate.is_contiguous(),
-              "gate must be [N,H,dv] in the dtype of q")
-    if norm_weight is not None:
-        _need(norm_weight.shape == (dv,) and norm_weight.dtype == torch.float32 and norm_weight.is_cuda,
-              "norm_weight must be fp32 [dv]")
+    for t in (q, k, v, alpha, beta):
+        _need(_on_device(t) and t.is_contiguous(), "inputs must be contiguous device tensors")
+    _dense(state, state.shape, torch.float32, "state")
+    _dense(gate, v.shape, q.dtype, "gate")
+    _dense(norm_weight, (dv,), torch.float32, "norm_weight")
     o_dtype = q.dtype if o_dtype is None else o_dtype
+    _dense(o, v.shape, o_dtype, "o")
     if o is None:
         o = torch.empty(v.shape, dtype=o_dtype, device=v.device)
-    _need(o.shape == v.shape and o.dtype == o_dtype and o.is_contiguous(), "o shape/dtype")
     lib = load()
     head = (N, H, dk, dv, float(scale), _code(q.dtype), _code(o_dtype))
     tail = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o), _stream(stream))

@@ -28,24 +28,15 @@
 
 namespace kda {
 
-#ifndef KDA_DECODE_COLS
-#define KDA_DECODE_COLS 128
-#endif
-#ifndef KDA_DECODE_THREADS
-#define KDA_DECODE_THREADS 256
-#endif
-#ifndef KDA_DECODE_NT_LOAD
-#define KDA_DECODE_NT_LOAD 0
-#endif
-#ifndef KDA_DECODE_NT_STORE
-#define KDA_DECODE_NT_STORE 1
-#endif
+// Columns per workgroup (a whole 128-column row) and threads per workgroup.
+constexpr int kDecodeCols = 128;
+constexpr int kDecodeThreads = 256;
 
 template <int DK, int DV> struct DecodeShape {
-    static constexpr int DVW = DV < KDA_DECODE_COLS ? DV : KDA_DECODE_COLS;  // columns per workgroup
+    static constexpr int DVW = DV < kDecodeCols ? DV : kDecodeCols;  // columns per workgroup
     static constexpr int CB = DV / DVW;                                     // column blocks per state
     static constexpr int CG = DVW / 4;                                      // threads per state row
-    static constexpr int NT = (DK * DVW / 4) < KDA_DECODE_THREADS ? (DK * DVW / 4) : KDA_DECODE_THREADS;
+    static constexpr int NT = (DK * DVW / 4) < kDecodeThreads ? (DK * DVW / 4) : kDecodeThreads;
     static constexpr int RPP = NT / CG;                                     // rows per pass
     static constexpr int PASSES = DK / RPP;
     static constexpr int NW = (NT + 63) / 64;
@@ -74,8 +65,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void kda_decode_kernel(c
     f32x4 s[PASSES];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p)
-        s[p] = KDA_DECODE_NT_LOAD ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (r0 + p * RPP) * DV + 4 * cg))
-                                  : *reinterpret_cast<const f32x4*>(S + (r0 + p * RPP) * DV + 4 * cg);
+        s[p] = *reinterpret_cast<const f32x4*>(S + (r0 + p * RPP) * DV + 4 * cg);
 
     const T* __restrict__ q = reinterpret_cast<const T*>(a.q) + (int64_t)unit * DK;
     const T* __restrict__ k = reinterpret_cast<const T*>(a.k) + (int64_t)unit * DK;
@@ -154,8 +144,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void kda_decode_kernel(c
     for (int p = 0; p < PASSES; ++p) {
         const int c = r0 + p * RPP;
         const f32x4 ns = s[p] + (bk * sk[c]) * e;
-        if (KDA_DECODE_NT_STORE) __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(S + c * DV + 4 * cg));
-        else *reinterpret_cast<f32x4*>(S + c * DV + 4 * cg) = ns;
+        __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(S + c * DV + 4 * cg));
     }
     if (r0 == 0) {  // the CG threads of the first row group: lanes 0 .. CG-1 of wave 0
         f32x4 o4 = (y + (beta * sqk) * e) * a.scale;
@@ -206,7 +195,7 @@ static hipError_t launch_decode_k(const DecodeArgs& a, int DK, int DV, hipStream
     return hipErrorInvalidValue;
 }
 
-int decode_columns(int DV) { return DV < KDA_DECODE_COLS ? DV : KDA_DECODE_COLS; }
+int decode_columns(int DV) { return DV < kDecodeCols ? DV : kDecodeCols; }
 
 hipError_t launch_decode(const DecodeArgs& a, int DK, int DV, bool bf16, hipStream_t s) {
     return bf16 ? launch_decode_k<__bf16>(a, DK, DV, s) : launch_decode_k<float>(a, DK, DV, s);

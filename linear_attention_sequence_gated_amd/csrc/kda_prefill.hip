@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kda_kernels.h"
 #include "kda_quads.h"
 
@@ -68,18 +70,6 @@ constexpr float kLog2Floor = -40.f;
 // Largest decay (log2 units) a 16-token block may show in any channel for the
 // factored Gram path; see the intra-chunk kernel.
 constexpr float kFastRange = 12.f;
-// 1: the intra-chunk grid runs over heads fastest (one dimension); 0: over
-// chunks fastest (chunks x heads).  Heads fastest measured 1.365 ms against
-// 1.448 ms per launch on the long-context workload.
-#ifndef KDA_INTRA_HEADS_FASTEST
-#define KDA_INTRA_HEADS_FASTEST 1
-#endif
-#ifndef KDA_LATE_V
-#define KDA_LATE_V 1
-#endif
-#ifndef KDA_WU_UNROLL
-#define KDA_WU_UNROLL 1
-#endif
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
 
@@ -242,13 +232,11 @@ void kda_intra_kernel(const PrefillArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, g = lane >> 4, cl = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-#if KDA_INTRA_HEADS_FASTEST
     // one-dimensional grid, heads fastest: the workgroups in flight read
     // neighbouring rows of q, k, v, alpha and write neighbouring blocks
+    // (1.365 ms against 1.448 ms per launch with chunks fastest on the
+    // long-context workload)
     const int x = (int)(blockIdx.x / (unsigned)a.H), h = (int)(blockIdx.x % (unsigned)a.H);
-#else
-    const int x = blockIdx.x, h = blockIdx.y;
-#endif
     ChunkPos pos;
     if (!locate_chunk(a, C, x, pos)) return;  // uniform over the workgroup
     const int valid = pos.valid;
@@ -327,7 +315,7 @@ void kda_intra_kernel(const PrefillArgs a) {
         }
     }
     // v is needed only once the solve is done: its loads go out after the Gram
-    // phase (KDA_LATE_V) so that they do not queue behind the factor inputs
+    // phase so that they do not queue behind the factor inputs
     auto load_v = [&]() {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {   // masked where V^T is staged
@@ -335,7 +323,6 @@ void kda_intra_kernel(const PrefillArgs a) {
             vraw[u].load(vg + ((pos.tok0 + (ok ? 4 * sgv + u : 0)) * H + h) * DV + 8 * (pv ? cgv : 0));
         }
     };
-    if (!KDA_LATE_V) load_v();
     if (kOpts && a.fuse_inputs) {
         // L2 norm of q and k per token.  The channel groups of a token are the
         // lanes sgi + NSEG * cg, spread over up to four waves: reduce inside
@@ -708,7 +695,7 @@ void kda_intra_kernel(const PrefillArgs a) {
     }
     lds_barrier();
 
-    if (KDA_LATE_V) load_v();
+    load_v();
 
     // ---- phase 3: X = (I + M)^{-1}; X^T kept in the strictly upper part of MX
     if (tid < C) {  // diagonal blocks by forward substitution, one column each
@@ -823,7 +810,7 @@ void kda_intra_kernel(const PrefillArgs a) {
         Q bq[NB];
 #pragma unroll
         for (int u = 0; u < NB; ++u) bq[u] = *reinterpret_cast<const Q*>(Tb + (16 * tb + cl) * LD_CT + 16 * u + 4 * g);
-#pragma unroll KDA_WU_UNROLL
+#pragma unroll 1
         for (int t = wave / NB; t < NQK; t += 4 / NB) {
             Q aq[NB];
 #pragma unroll
@@ -845,7 +832,7 @@ void kda_intra_kernel(const PrefillArgs a) {
 #pragma unroll
             for (int u = 0; u < NB; ++u) vq[j][u] = *reinterpret_cast<const Q*>(VT + (16 * sv + cl) * LD_CT + 16 * u + 4 * g);
         }
-#pragma unroll KDA_WU_UNROLL
+#pragma unroll 1
         for (int tb = 0; tb < NB; ++tb) {
             Q aq[NB];
 #pragma unroll
@@ -906,44 +893,21 @@ __device__ __forceinline__ void load_frag(f32x4 (&q)[N], const char* base, int r
     for (int u = 0; u < N; ++u) q[u] = *reinterpret_cast<const f32x4*>(p + u * 64 * 4);
 }
 
-// Value slices (16 columns each) per compute wave of a plain call: the A
-// fragments loaded from LDS feed that many MFMA column tiles.
-#ifndef KDA_SLICES_PER_WAVE
-#define KDA_SLICES_PER_WAVE 1
-#endif
-#define KDA_SLICES_PER_WAVE_VALUE KDA_SLICES_PER_WAVE
-// 1: ring B copies of the two-compute-wave path complete an interval after
-// they are issued (waited for one barrier later); 0: at the next barrier.
-#ifndef KDA_DEFER_B
-#define KDA_DEFER_B 1
-#endif
-// 1: plain one-slice workgroups split the chain over two compute waves (the
-// state wave and an output wave one chunk behind it); 0: one compute wave.
-#ifndef KDA_O_WAVE
-#define KDA_O_WAVE 1
-#endif
-
 // Gated calls keep all dv / 16 slices (8 at dv = 128) in one workgroup, two per
 // compute wave, so that a workgroup still has two waves per SIMD (8 waves).
 constexpr int kGateSlices = 8;
 constexpr int kGateSlicesPerWave = 2;
 
 // Waves per workgroup that copy chunk blocks into LDS (they split the 1 KiB
-// units): KDA_IO_WAVES with one compute wave per slice group, KDA_IO_WAVES_OW
-// beside the state and output waves.  Long-context inter-chunk pass with the
-// ring B wait deferred: 4 waves 1.036 ms, 6: 1.039, 8: 1.059 (before the
-// deferral 8 waves were best: 1.26 against 1.33 ms with 4).
-#ifndef KDA_IO_WAVES
-#define KDA_IO_WAVES 4
-#endif
-#ifndef KDA_IO_WAVES_OW
-#define KDA_IO_WAVES_OW 4
-#endif
-constexpr int kIoWaves = KDA_IO_WAVES;
+// units), both beside one compute wave per slice group and beside the state
+// and output waves.  Long-context inter-chunk pass with the ring B wait
+// deferred: 4 waves 1.036 ms, 6: 1.039, 8: 1.059 (before the deferral 8
+// waves were best: 1.26 against 1.33 ms with 4).
+constexpr int kIoWaves = 4;
 
 template <int DK, int C, typename T, bool kGate = false> struct Inter {
     static constexpr int G = kGate ? kGateSlices : kGroupSlices;   // most slices per workgroup
-    static constexpr int SPW = kGate ? kGateSlicesPerWave : KDA_SLICES_PER_WAVE_VALUE;
+    static constexpr int SPW = kGate ? kGateSlicesPerWave : 1;
     static constexpr int kMaxCompute = (G + SPW - 1) / SPW;
     static constexpr int64_t kShared = (2 * Frag<T>::elems(C, DK) + Frag<T>::elems(DK, C) + Frag<T>::elems(C, C)) *
                                            (int64_t)sizeof(T) + round_kib(DK * 4);
@@ -962,10 +926,10 @@ template <int DK, int C, typename T, bool kGate = false> struct Inter {
     static constexpr int64_t kBufB = kSzW + kSzP;
     static constexpr int64_t kHand = (int64_t)(DK / 16 + C / 16) * 64 * sizeof(quad_t<T>);
     static constexpr int64_t kOWaveLds = 2 * kBufA + 3 * kBufB + 2 * kHand;
-    static constexpr bool kOWave = KDA_O_WAVE && !kGate && G == 1 && SPW == 1 && kSzW % 1024 == 0 &&
+    static constexpr bool kOWave = !kGate && G == 1 && SPW == 1 && kSzW % 1024 == 0 &&
                                    kSzP % 1024 == 0 && kSzK == kSzW && kOWaveLds <= 163840;
     static constexpr int kComputeWaves = kOWave ? 2 : kMaxCompute;
-    static constexpr int kIo = kOWave ? KDA_IO_WAVES_OW : KDA_IO_WAVES;
+    static constexpr int kIo = kIoWaves;
     // 1 KiB copies of ring B issued by each I/O wave per chunk (they are dealt
     // evenly only when the I/O waves divide them)
     static constexpr int kDeferB = (int)((kSzW + kSzP) / 1024 / kIo);
@@ -978,12 +942,10 @@ template <int DK, int C, typename T, bool kGate = false> struct Inter {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-// d > 0: the I/O waves also pull the block d chunks ahead of the copy into L2
-// (long-context workload, current kernel: d = 1 1.047 ms, 2 1.056, 3 1.077;
+// The I/O waves also pull the block kL2Ahead chunks past the one they copy
+// into L2 (long-context workload: 1 chunk 1.047 ms, 2: 1.056, 3: 1.077;
 // without any prefetch the copies are exposed).
-#ifndef KDA_L2_PREFETCH
-#define KDA_L2_PREFETCH 1
-#endif
+constexpr int kL2Ahead = 1;
 
 // Copy the 1 KiB units first, first + step, ... of `bytes` (a multiple of
 // 1 KiB) from global to LDS, 16 bytes per lane per instruction.
@@ -1009,7 +971,7 @@ void kda_inter_kernel(const PrefillArgs a) {
     constexpr int NB = C / 16, NQK = DK / 16, SPW = X::SPW;
     __shared__ __attribute__((aligned(1024))) char ring[X::kLds];
     // target of the I/O waves' one-dword L2 prefetch loads (never read)
-    __shared__ __attribute__((aligned(256))) int pf_sink[X::kOWave && KDA_L2_PREFETCH && KDA_DEFER_B ? 64 : 1];
+    __shared__ __attribute__((aligned(256))) int pf_sink[X::kOWave ? 64 : 1];
     // per-token sums of squares of each compute wave's outputs (double-buffered
     // by chunk parity) for the output norm of gated calls
     __shared__ float part[kGate ? 2 : 1][kGate ? X::kMaxCompute : 1][kGate ? C : 1];
@@ -1073,23 +1035,20 @@ void kda_inter_kernel(const PrefillArgs a) {
             };
             if (nch > 0) fetch(0);
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-#if KDA_L2_PREFETCH
-            // one dword per 128-byte line of a chunk KDA_L2_PREFETCH ahead of the
-            // copy (see the one-wave path below)
+            // one dword per 128-byte line of a chunk kL2Ahead past the copy (see
+            // the one-wave path below)
             const int64_t shared_lines = cb.shared / 128, group_lines = cb.group / 128;
             const int64_t my_shared = (shared_lines - grp + ngroups - 1) / ngroups;
             const int64_t pl = (int64_t)io * 64 + lane;
             const int64_t pf_off = pl < my_shared ? (grp + pl * ngroups) * 128
                                    : pl < my_shared + group_lines ? cb.u + grp * cb.group + (pl - my_shared) * 128
                                    : 0;
-#endif
             for (int jn = 0; jn < nint; ++jn) {
                 const bool more = jn + 1 < nch;
                 if (more) fetch(jn + 1);
-#if KDA_L2_PREFETCH
                 asm volatile("" ::: "memory");   // the line load stays after the copies
-                const int xp = c_begin + min(jn + 1 + KDA_L2_PREFETCH, nch - 1);
-                if constexpr (KDA_DEFER_B && X::kDeferOk) {
+                const int xp = c_begin + min(jn + 1 + kL2Ahead, nch - 1);
+                if constexpr (X::kDeferOk) {
                 // the line load lands in a scratch LDS word (no register, so no
                 // compiler wait); ring B of the chunk just issued is first read
                 // an interval later, so the wait leaves its copies (kDeferB per
@@ -1105,9 +1064,6 @@ void kda_inter_kernel(const PrefillArgs a) {
                 asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
                 asm volatile("" ::"v"(pv));
                 }
-#else
-                asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-#endif
             }
             return;
         }
@@ -1232,10 +1188,9 @@ void kda_inter_kernel(const PrefillArgs a) {
             };
             if (c_begin < c_end) fetch(c_begin, 0);
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-#if KDA_L2_PREFETCH
             // The ring holds two chunks, so the copy of chunk x + 1 is issued only
             // one chunk ahead and would pay the full HBM latency.  One dword per
-            // 128-byte line of chunk x + 1 + KDA_L2_PREFETCH is loaded into a register
+            // 128-byte line of chunk x + 1 + kL2Ahead is loaded into a register
             // as well, which brings that block into this XCD's L2 early: the shared part is split
             // over the slice groups of the (sequence, head), each group touches its
             // own value slice.  Exactly one load per lane (a lane without a line
@@ -1251,20 +1206,13 @@ void kda_inter_kernel(const PrefillArgs a) {
             for (int x = c_begin; x < c_end; ++x) {
                 if (x + 1 < c_end) fetch(x + 1, (x + 1 - c_begin) & 1);
                 asm volatile("" ::: "memory");   // the line load stays after the copies
-                const int xp = min(x + 1 + KDA_L2_PREFETCH, c_end - 1);
+                const int xp = min(x + 1 + kL2Ahead, c_end - 1);
                 typedef __attribute__((address_space(1))) const int gbl_int_t;
                 const int pv = *(gbl_int_t*)(a.ws_chunks + ((int64_t)xp * H + h) * cb.bytes + pf_off);
                 asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
                 asm volatile("" ::"v"(pv));
             }
             return;
-#else
-            for (int x = c_begin; x < c_end; ++x) {
-                if (x + 1 < c_end) fetch(x + 1, (x + 1 - c_begin) & 1);
-                asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-            }
-            return;
-#endif
         }
 
         // ---- compute waves: SPW value slices (16 columns each) per wave ----------------
@@ -1446,11 +1394,7 @@ static hipError_t launch_phase_t(const PrefillArgs& a, int max_chunks, bool intr
     } else {
         if (intra) {
             if (max_chunks > 0) {
-#if KDA_INTRA_HEADS_FASTEST
                 const dim3 grid((unsigned)max_chunks * (unsigned)a.H);
-#else
-                const dim3 grid(max_chunks, a.H);
-#endif
                 if (a.alpha_scalar || a.fuse_inputs || a.alpha_floor != 0.f)
                     hipLaunchKernelGGL((kda_intra_kernel<DK, C, In, true>), grid, dim3(256), 0, stream, a);
                 else
@@ -1595,11 +1539,20 @@ hipError_t launch_gate_epilogue(const PrefillArgs& a, int64_t rows, bool bf16, h
     return hipGetLastError();
 }
 
+// Compute units of each device, queried once per device (0: not yet).  A
+// racing first query stores the same value twice.
+constexpr int kMaxDevices = 64;
+static std::atomic<int> g_cu_count[kMaxDevices];
+
 bool gate_split(int64_t units) {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return units < 256;
+    int cus = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        g_cu_count[dev].store(cus, std::memory_order_relaxed);
+    }
     return units < cus;
 }
 

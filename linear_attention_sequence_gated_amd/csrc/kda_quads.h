@@ -141,12 +141,7 @@ template <typename T> struct Frag {
 // chain of a (sequence, head) is serial, so one slice per workgroup spreads a
 // few long sequences over every CU (32 heads x 8 slices fill 256 CUs); the
 // price is that each slice's workgroup reads the shared region from L2 itself.
-#ifndef KDA_GROUP_SLICES
-#define KDA_GROUP_SLICES 1
-#endif
-constexpr int kGroupSlices = KDA_GROUP_SLICES;
-static_assert(kGroupSlices == 1 || kGroupSlices == 2 || kGroupSlices == 4 || kGroupSlices == 8,
-              "slice groups must divide every supported dv / 16");
+constexpr int kGroupSlices = 1;
 __host__ __device__ constexpr int64_t round_kib(int64_t x) { return (x + 1023) / 1024 * 1024; }
 __host__ __device__ constexpr int group_slices(int DV) { return DV / 16 < kGroupSlices ? DV / 16 : kGroupSlices; }
 

@@ -15,6 +15,7 @@ import torch
 import linear_attention_sequence_gated_amd as kda
 import workloads
 from oracle import kda_oracle
+from parity_measure import WholeTensorError, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -23,16 +24,6 @@ TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
 
 def say(*a):
     print(*a, flush=True)
-
-
-def rel_err(gpu, ref):
-    gpu = np.asarray(gpu, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
-    assert np.all(np.isfinite(gpu)), "non-finite GPU output"
-    rms = float(np.sqrt(np.mean(ref ** 2)))
-    diff = float(np.max(np.abs(gpu - ref))) if gpu.size else 0.0
-    return diff / rms if rms > 0 else diff
 
 
 def to_dev(inp):
@@ -88,36 +79,45 @@ def test_batched_prefill_bf16():
     check_bf16_output(inp, w.chunk)
 
 
+def whole_prefill_parity(inp, chunk, heads_per_group, label):
+    """Every head of a full-size launch against the oracle, one group of heads at a time."""
+    H = inp["q"].shape[2]
+    say(f"[case] {label} GPU prefill, T={inp['q'].shape[1]} H={H}")
+    d = to_dev(inp)
+    o, S = kda.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"],
+                         chunk_size=chunk, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    del d
+    eo, es = WholeTensorError(), WholeTensorError()
+    for h0 in range(0, H, heads_per_group):
+        h1 = min(H, h0 + heads_per_group)
+        say(f"[case] {label} oracle heads {h0}..{h1 - 1}")
+        oo, So = oracle_prefill(inp, heads=(h0, h1))
+        eo.add(o[:, :, h0:h1].contiguous().cpu().numpy(), oo)
+        es.add(S[:, h0:h1].contiguous().cpu().numpy(), So)
+        del oo, So
+    say(f"    all {H} heads: err o={eo.value():.3e} S={es.value():.3e}")
+    return eo.value(), es.value()
+
+
 @pytest.mark.timeout(900)
-def test_long_context_prefill_sampled_heads():
-    """Full-size launch (B1 H32 T65536); the oracle recomputes heads 0, 17 and 31."""
+def test_long_context_prefill_every_head():
+    """Full-size launch (B1 H32 T65536): o and the final states of all 32 heads against the oracle."""
     w = workloads.CONFIGS[workloads.LONG_CONTEXT_PREFILL]
     say("[case] long-context-prefill generating inputs")
     inp = workloads.config_inputs(workloads.LONG_CONTEXT_PREFILL)
-    say("[case] long-context-prefill GPU prefill")
-    og, Sg = gpu_prefill(inp, w.chunk)
-    for h in (0, 17, 31):
-        say(f"[case] long-context-prefill oracle head {h}")
-        oo, So = oracle_prefill(inp, heads=(h, h + 1))
-        eo, es = rel_err(og[:, :, h:h + 1], oo), rel_err(Sg[:, h:h + 1], So)
-        say(f"    head {h}: err o={eo:.3e} S={es:.3e}")
-        assert eo < TOL[w.dtype] and es < TOL[w.dtype], (h, eo, es)
+    eo, es = whole_prefill_parity(inp, w.chunk, 16, "long-context-prefill")
+    assert eo < TOL[w.dtype] and es < TOL[w.dtype], (eo, es)
 
 
 @pytest.mark.timeout(1200)
-def test_packed_varlen_resume_sampled_heads():
-    """64 packed sequences (lengths U[1, 32768]), S0 != 0; the oracle recomputes heads 3 and 12."""
+def test_packed_varlen_resume_every_head():
+    """64 packed sequences (lengths U[1, 32768]), S0 != 0: all 16 heads against the oracle."""
     w = workloads.CONFIGS[workloads.PACKED_VARLEN_RESUME]
     say("[case] packed-varlen-resume generating inputs")
     inp = workloads.config_inputs(workloads.PACKED_VARLEN_RESUME)
-    say(f"[case] packed-varlen-resume GPU prefill, T={inp['q'].shape[1]}")
-    og, Sg = gpu_prefill(inp, w.chunk)
-    for h in (3, 12):
-        say(f"[case] packed-varlen-resume oracle head {h}")
-        oo, So = oracle_prefill(inp, heads=(h, h + 1))
-        eo, es = rel_err(og[:, :, h:h + 1], oo), rel_err(Sg[:, h:h + 1], So)
-        say(f"    head {h}: err o={eo:.3e} S={es:.3e}")
-        assert eo < TOL[w.dtype] and es < TOL[w.dtype], (h, eo, es)
+    eo, es = whole_prefill_parity(inp, w.chunk, 4, "packed-varlen-resume")
+    assert eo < TOL[w.dtype] and es < TOL[w.dtype], (eo, es)
 
 
 def _decode_run(inp, steps, scale=1.0, o_dtype=torch.float32):
@@ -132,19 +132,20 @@ def _decode_run(inp, steps, scale=1.0, o_dtype=torch.float32):
 
 
 @pytest.mark.timeout(600)
-def test_decode_128_steps_sampled_sequences():
-    """256 sequences x H32, 128 in-place steps; the oracle recomputes sequences 0, 101 and 255."""
+def test_decode_128_steps_every_sequence():
+    """256 sequences x H32, 128 in-place steps: o of every step and every final state against the oracle."""
     w = workloads.CONFIGS[workloads.DECODE]
     say("[case] decode generating inputs")
     inp = workloads.decode_inputs(3)
     say("[case] decode GPU decode x128")
     og, Sg = _decode_run(inp, w.decode_steps)
-    for n in (0, 101, 255):
-        sub = {k: (v[:, n:n + 1] if k != "S0" else v[n:n + 1]) for k, v in inp.items()}
-        oo, So = kda_oracle.decode(sub["S0"], sub["q"], sub["k"], sub["v"], sub["alpha"], sub["beta"])
-        eo, es = rel_err(og[:, n:n + 1], oo), rel_err(Sg[n:n + 1], So)
-        say(f"    seq {n}: err o={eo:.3e} S={es:.3e}")
-        assert eo < TOL[w.dtype] and es < TOL[w.dtype], (n, eo, es)
+    say("[case] decode oracle, all 256 sequences")
+    oo, So = kda_oracle.decode(inp["S0"], inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"])
+    eo, es = WholeTensorError(), WholeTensorError()
+    eo.add(og, oo)
+    es.add(Sg, So)
+    say(f"    all sequences: err o={eo.value():.3e} S={es.value():.3e}")
+    assert eo.value() < TOL[w.dtype] and es.value() < TOL[w.dtype], (eo.value(), es.value())
 
 
 # --- shapes, ragged tails, packing --------------------------------------------

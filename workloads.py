@@ -196,3 +196,44 @@ def decode_inputs(index: int = 3, steps: Optional[int] = None, seqs: Optional[in
     # make_inputs draws [batch=steps, seqlen=n, ...]: axis 0 is the step.
     return {"q": d["q"], "k": d["k"], "v": d["v"], "alpha": d["alpha"], "beta": d["beta"],
             "S0": s0}
+
+
+def device_inputs(index: int, device, seed_offset: int = 7000):
+    """Inputs shaped like prefill workload ``index``, drawn directly on ``device``.
+
+    Same shapes, dtypes and distributions as ``config_inputs(index)`` (and, for
+    the packed workload, the very same sequence lengths, drawn on the CPU from
+    the workload's seed), but the tensor values come from a device generator,
+    so they differ from the CPU draw.  For timing runs, where drawing a
+    million-token workload on the host would dominate the run.
+    """
+    w = CONFIGS[index]
+    assert w.decode_steps == 0
+    cu = None
+    if w.packed_seqs:
+        gen = torch.Generator(device="cpu")
+        gen.manual_seed(SEED_BASE + index)
+        lens = packed_lengths(gen, w.packed_seqs, w.max_len)
+        cu = torch.zeros(len(lens) + 1, dtype=torch.int64)
+        cu[1:] = torch.cumsum(lens, 0)
+        batch, seqlen, n_seq = 1, int(cu[-1]), len(lens)
+    else:
+        batch, seqlen, n_seq = w.batch, w.seqlen, w.batch
+    g = torch.Generator(device=device)
+    g.manual_seed(SEED_BASE + index + seed_offset)
+    shp = (batch, seqlen, w.heads)
+
+    def unit(d):
+        x = torch.randn(*shp, d, generator=g, device=device)
+        return (x / x.norm(dim=-1, keepdim=True).clamp_min(1e-12)).to(w.dtype)
+
+    q, k = unit(w.dk), unit(w.dk)
+    v = torch.nn.functional.silu(torch.randn(*shp, w.dv, generator=g, device=device)).to(w.dtype)
+    alpha = torch.sigmoid(torch.randn(*shp, w.dk, generator=g, device=device) + w.alpha_mu)
+    beta = torch.sigmoid(torch.randn(*shp, generator=g, device=device))
+    s0 = None
+    if w.s0_std > 0.0:
+        s0 = torch.randn(n_seq, w.heads, w.dk, w.dv, generator=g, device=device) * w.s0_std
+    return {"q": q, "k": k, "v": v, "alpha": alpha, "beta": beta, "S0": s0,
+            "cu_seqlens": None if cu is None else cu.to(torch.int32).to(device)}
+
