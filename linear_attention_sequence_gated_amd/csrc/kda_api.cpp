@@ -44,7 +44,7 @@ int chunk_of(const kda_chunk_params_t* p) {
     return kda::effective_chunk(p->head_dim_k, p->chunk_size, p->qkv_dtype == KDA_DTYPE_BF16);
 }
 
-PrefillPlan plan_prefill(const kda_chunk_params_t* p, bool packed, bool gate) {
+PrefillPlan plan_prefill(const kda_chunk_params_t* p, bool packed, bool whole) {
     PrefillPlan pl{};
     const int64_t C = chunk_of(p);
     if (packed)
@@ -52,7 +52,7 @@ PrefillPlan plan_prefill(const kda_chunk_params_t* p, bool packed, bool gate) {
     else
         pl.max_chunks = (int64_t)p->batch * ((p->seqlen + C - 1) / C);
     pl.block_bytes = kda::chunk_block_bytes(p->head_dim_k, (int)C, p->head_dim_v, p->qkv_dtype == KDA_DTYPE_BF16,
-                                            kda::slice_group(p->head_dim_v, gate));
+                                            kda::slice_group(p->head_dim_v, whole));
     pl.off_bytes = packed ? round_up(sizeof(int32_t) * ((size_t)p->num_seqs + 1), kWsAlign) : 0;
     pl.total = pl.off_bytes + (size_t)pl.max_chunks * (size_t)p->num_heads * (size_t)pl.block_bytes;
     return pl;
@@ -69,8 +69,8 @@ size_t gate_scratch_bytes(const kda_chunk_params_t* p) {
 size_t base_workspace(const kda_chunk_params_t* p) {
     size_t most = 0;
     for (int packed = 0; packed < 2; ++packed)
-        for (int gate = 0; gate < 2; ++gate) {
-            const PrefillPlan pl = plan_prefill(p, packed, gate);
+        for (int whole = 0; whole < 2; ++whole) {
+            const PrefillPlan pl = plan_prefill(p, packed, whole);
             most = pl.total > most ? pl.total : most;
         }
     return most;
@@ -175,8 +175,9 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
         if (overlaps(initial_state, sb, final_state, sb)) return KDA_ERR_INVALID_ARG;
     }
     const bool gate = op && op->gate;
-    const bool split = gate && kda::gate_split((int64_t)p->num_seqs * p->num_heads);
-    const PrefillPlan pl = plan_prefill(p, packed, gate && !split);
+    const bool whole = kda::whole_rows((int64_t)p->num_seqs * p->num_heads);
+    const bool split = gate && !whole;
+    const PrefillPlan pl = plan_prefill(p, packed, whole);
     const size_t need = round_up(pl.total, kWsAlign) + (split ? gate_scratch_bytes(p) : 0);
     if (need > 0) {
         if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_WORKSPACE;
@@ -217,7 +218,8 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
         a.norm_w = op->norm_weight;
         a.norm_eps = op->norm_eps;
     }
-    a.gsl = kda::slice_group(p->head_dim_v, gate && !split);
+    a.gsl = kda::slice_group(p->head_dim_v, whole);
+    a.whole_rows = whole;
     const int64_t rows = (int64_t)p->batch * p->seqlen * p->num_heads;
     if (split) {
         a.gate_split = 1;

@@ -35,6 +35,7 @@ struct PrefillArgs {
     float norm_eps;
     int32_t gsl;                 // value slices per slice group (slice_group())
     int32_t gate_split;          // gated output through o_scratch + part_scratch and an epilogue
+    int32_t whole_rows;          // plain output from whole-row inter-chunk workgroups
     float* o_scratch;            // [B*T*H, dv] un-normalised outputs (split gate)
     float* part_scratch;         // [B*T*H, dv/16] per-slice sums of squares (split gate)
 };
@@ -70,12 +71,13 @@ hipError_t launch_decode(const DecodeArgs& a, int DK, int DV, bool bf16, hipStre
 // Value columns one decode workgroup owns (the output gate needs the whole row).
 int decode_columns(int DV);
 // Value slices per inter-chunk workgroup (and per Utilde group of the
-// workspace): all dv / 16 when the output gate is fused (it needs a token's
-// whole row in one workgroup), else the plain grouping.
-int slice_group(int DV, bool gate);
-// Gated calls with fewer (sequence, head) units than the device has CUs keep
-// one slice per workgroup and finish the norm in an epilogue kernel.
-bool gate_split(int64_t units);
+// workspace): all dv / 16 for whole-row workgroups, else the plain grouping.
+int slice_group(int DV, bool whole);
+// Whether the inter-chunk pass runs whole-row workgroups: with at least as
+// many (sequence, head) units as the device has CUs (queried once per
+// device).  With fewer, one-slice workgroups spread the units over every CU,
+// and gated calls finish the norm in an epilogue kernel.
+bool whole_rows(int64_t units);
 hipError_t launch_gate_epilogue(const PrefillArgs& a, int64_t rows, bool bf16, hipStream_t s);
 int64_t chunk_block_bytes(int DK, int C, int DV, bool bf16, int gsl);
 

@@ -893,8 +893,14 @@ __device__ __forceinline__ void load_frag(f32x4 (&q)[N], const char* base, int r
     for (int u = 0; u < N; ++u) q[u] = *reinterpret_cast<const f32x4*>(p + u * 64 * 4);
 }
 
-// Gated calls keep all dv / 16 slices (8 at dv = 128) in one workgroup, two per
-// compute wave, so that a workgroup still has two waves per SIMD (8 waves).
+// Whole-row workgroups (gated calls, and plain calls with at least as many
+// (sequence, head) pairs as compute units) keep all dv / 16 slices (8 at
+// dv = 128) in one workgroup, two per compute wave, so that a workgroup still
+// has two waves per SIMD (8 waves).  Each chunk's shared operands (W, Q~,
+// Kbar^T, P) are then fetched once for the whole row instead of once per
+// slice: a compute unit takes in about 26 bytes per cycle from L2, and a
+// one-slice workgroup needs ~57 KiB of shared operands per chunk, which caps
+// it near 1 us per chunk whatever the number of workgroups in flight.
 constexpr int kGateSlices = 8;
 constexpr int kGateSlicesPerWave = 2;
 
@@ -935,6 +941,8 @@ template <int DK, int C, typename T, bool kGate = false> struct Inter {
     static constexpr int kDeferB = (int)((kSzW + kSzP) / 1024 / kIo);
     static constexpr bool kDeferOk = (kSzW + kSzP) / 1024 % kIo == 0 && kDeferB + 1 <= 63;
     static constexpr int kThreads = 64 * (kComputeWaves + kIo);
+    // one-dword L2 prefetch loads per I/O lane that cover a whole block
+    static constexpr int kPfLoads = (int)((kShared + kGroupMax) / 128 + kIo * 64 - 1) / (kIo * 64);
     static constexpr int64_t kLds = kOWave ? kOWaveLds : 2 * kBuf;
     static constexpr bool kFits = kOWave || 2 * kBuf + kPart <= 163840;
 };
@@ -955,23 +963,27 @@ __device__ __forceinline__ void dma_to_lds(const char* src, char* dst, int64_t b
 }
 
 // Output modes of the inter-chunk kernel.
-enum OutMode { kOutPlain = 0, kOutGate = 1, kOutSplit = 2 };
+enum OutMode { kOutPlain = 0, kOutGate = 1, kOutSplit = 2, kOutRow = 3 };
 
-// kMode kOutPlain: o stored per chunk; kOutGate: all slices of a row in this
-// workgroup, norm and gate applied here; kOutSplit: one-slice workgroups write
-// un-normalised fp32 outputs and per-slice sums of squares for the epilogue.
+// kMode kOutPlain: one-slice workgroups, o stored per chunk; kOutGate: all
+// slices of a row in this workgroup, norm and gate applied here; kOutSplit:
+// one-slice workgroups write un-normalised fp32 outputs and per-slice sums of
+// squares for the epilogue; kOutRow: all slices of a row in this workgroup, o
+// stored per chunk.
+template <int kMode> constexpr bool whole_row_mode() { return kMode == kOutGate || kMode == kOutRow; }
+
 template <int DK, int C, typename In, int kMode>
-__global__ __launch_bounds__((Inter<DK, C, typename OperandOf<In>::type, kMode == kOutGate>::kThreads))
+__global__ __launch_bounds__((Inter<DK, C, typename OperandOf<In>::type, whole_row_mode<kMode>()>::kThreads))
 void kda_inter_kernel(const PrefillArgs a) {
     constexpr bool kGate = kMode == kOutGate;
     using T = typename OperandOf<In>::type;
     using Q = quad_t<T>;
-    using X = Inter<DK, C, T, kGate>;
+    using X = Inter<DK, C, T, whole_row_mode<kMode>()>;
     static_assert(X::kFits, "LDS ring of the inter-chunk kernel exceeds one workgroup");
     constexpr int NB = C / 16, NQK = DK / 16, SPW = X::SPW;
     __shared__ __attribute__((aligned(1024))) char ring[X::kLds];
     // target of the I/O waves' one-dword L2 prefetch loads (never read)
-    __shared__ __attribute__((aligned(256))) int pf_sink[X::kOWave ? 64 : 1];
+    __shared__ __attribute__((aligned(256))) int pf_sink[64];
     // per-token sums of squares of each compute wave's outputs (double-buffered
     // by chunk parity) for the output norm of gated calls
     __shared__ float part[kGate ? 2 : 1][kGate ? X::kMaxCompute : 1][kGate ? C : 1];
@@ -1190,27 +1202,31 @@ void kda_inter_kernel(const PrefillArgs a) {
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
             // The ring holds two chunks, so the copy of chunk x + 1 is issued only
             // one chunk ahead and would pay the full HBM latency.  One dword per
-            // 128-byte line of chunk x + 1 + kL2Ahead is loaded into a register
-            // as well, which brings that block into this XCD's L2 early: the shared part is split
-            // over the slice groups of the (sequence, head), each group touches its
-            // own value slice.  Exactly one load per lane (a lane without a line
-            // re-reads the block's first line), so the wait below can leave that
-            // one outstanding; the register is read (by an empty asm statement)
-            // after the barrier, where only that load can still be in flight.
+            // 128-byte line of chunk x + 1 + kL2Ahead is loaded as well, into a
+            // scratch LDS word (no register the compiler would wait for), which
+            // brings that block into this XCD's L2 early: the shared part is
+            // split over the slice groups of the (sequence, head), each group
+            // touches its own value slices.  Every lane issues kPfLoads such
+            // loads (a lane without a line re-reads the block's first line), so
+            // the wait below leaves exactly those outstanding.
             const int64_t shared_lines = cb.shared / 128, group_lines = cb.group / 128;
             const int64_t my_shared = (shared_lines - grp + ngroups - 1) / ngroups;
-            const int64_t pl = (int64_t)io * 64 + lane;
-            const int64_t pf_off = pl < my_shared ? (grp + pl * ngroups) * 128
-                                   : pl < my_shared + group_lines ? cb.u + grp * cb.group + (pl - my_shared) * 128
-                                   : 0;
+            int64_t pf_off[X::kPfLoads];
+#pragma unroll
+            for (int i = 0; i < X::kPfLoads; ++i) {
+                const int64_t pl = ((int64_t)i * X::kIo + io) * 64 + lane;
+                pf_off[i] = pl < my_shared ? (grp + pl * ngroups) * 128
+                            : pl < my_shared + group_lines ? cb.u + grp * cb.group + (pl - my_shared) * 128
+                            : 0;
+            }
             for (int x = c_begin; x < c_end; ++x) {
                 if (x + 1 < c_end) fetch(x + 1, (x + 1 - c_begin) & 1);
-                asm volatile("" ::: "memory");   // the line load stays after the copies
-                const int xp = min(x + 1 + kL2Ahead, c_end - 1);
-                typedef __attribute__((address_space(1))) const int gbl_int_t;
-                const int pv = *(gbl_int_t*)(a.ws_chunks + ((int64_t)xp * H + h) * cb.bytes + pf_off);
-                asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
-                asm volatile("" ::"v"(pv));
+                asm volatile("" ::: "memory");   // the line loads stay after the copies
+                const char* pblk = a.ws_chunks + ((int64_t)min(x + 1 + kL2Ahead, c_end - 1) * H + h) * cb.bytes;
+#pragma unroll
+                for (int i = 0; i < X::kPfLoads; ++i)
+                    __builtin_amdgcn_global_load_lds((gbl_void_t*)(pblk + pf_off[i]), (lds_void_t*)pf_sink, 4, 0, 0);
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(X::kPfLoads) : "memory");
             }
             return;
         }
@@ -1407,6 +1423,10 @@ static hipError_t launch_phase_t(const PrefillArgs& a, int max_chunks, bool intr
                 constexpr int spw = Inter<DK, C, typename OperandOf<In>::type, true>::SPW;
                 hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutGate>), dim3(blocks),
                                    dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
+            } else if (a.whole_rows) {
+                constexpr int spw = Inter<DK, C, typename OperandOf<In>::type, true>::SPW;
+                hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutRow>), dim3(blocks),
+                                   dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
             } else {
                 using XP = Inter<DK, C, typename OperandOf<In>::type, false>;
                 const int threads = XP::kOWave ? XP::kThreads : 64 * ((a.gsl + XP::SPW - 1) / XP::SPW + kIoWaves);
@@ -1544,19 +1564,19 @@ hipError_t launch_gate_epilogue(const PrefillArgs& a, int64_t rows, bool bf16, h
 constexpr int kMaxDevices = 64;
 static std::atomic<int> g_cu_count[kMaxDevices];
 
-bool gate_split(int64_t units) {
+bool whole_rows(int64_t units) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return units < 256;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return units >= 256;
     int cus = g_cu_count[dev].load(std::memory_order_relaxed);
     if (cus == 0) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
         g_cu_count[dev].store(cus, std::memory_order_relaxed);
     }
-    return units < cus;
+    return units >= cus;
 }
 
-int slice_group(int DV, bool gate) { return gate ? DV / 16 : group_slices(DV); }
+int slice_group(int DV, bool whole) { return whole ? DV / 16 : group_slices(DV); }
 
 int64_t chunk_block_bytes(int DK, int C, int DV, bool bf16, int gsl) {
     return bf16 ? ChunkBlock<_Float16>(DK, C, DV, gsl).bytes : ChunkBlock<float>(DK, C, DV, gsl).bytes;

@@ -116,6 +116,22 @@ __device__ __forceinline__ f32x4 mma_quads_upto(const Q (&a)[N], const Q (&b)[N]
     return c;
 }
 
+// c[i] += sum over quads u in [0, N) of A_i,u * B_u for NT tiles that share
+// their B quads, issued K-step by K-step across the tiles: consecutive MFMAs
+// then write different accumulators, where the tile-by-tile order makes each
+// MFMA wait for the one before it.
+template <int NT, int N, typename Q>
+__device__ __forceinline__ void mma_tiles(const Q (&a)[NT][N], const Q (&b)[N], f32x4 (&c)[NT]) {
+#pragma unroll
+    for (int u = 0; u + 1 < N; u += 2)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) c[i] = mma_step2(a[i][u], a[i][u + 1], b[u], b[u + 1], c[i]);
+    if constexpr (N % 2 == 1) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) c[i] = mma_tail(a[i][N - 1], b[N - 1], c[i]);
+    }
+}
+
 // Fragment storage in global memory: a matrix of `rows` (multiple of 16) by
 // K (multiple of 16) stored so that lane l of the wave that consumes row tile
 // rt reads its quads of k-slices [kPerStep*gq, kPerStep*gq + kPerStep) as one

@@ -640,3 +640,25 @@ def test_prefill_gate_many_units_fused_in_inter_kernel():
     # apply the norm and gate inside the inter-chunk kernel
     inp = workloads.make_inputs(64, 70, 4, 64, 64, torch.bfloat16, s0_std=0.02, seed=505)
     _gate_case(inp, 32, TOL[torch.bfloat16], "B64 H4 (256 units)")
+
+
+# --- whole-row inter-chunk workgroups ---------------------------------------------
+# With at least as many (sequence, head) pairs as the device has CUs (256 on
+# MI355X), every value slice of a row shares one inter-chunk workgroup.
+
+@pytest.mark.parametrize("dk,dv,C,dtype", [(128, 128, 64, torch.bfloat16), (64, 32, 32, torch.bfloat16),
+                                           (32, 64, 16, torch.float32), (128, 16, 64, torch.bfloat16),
+                                           (128, 128, 32, torch.float32), (16, 128, 64, torch.bfloat16)])
+def test_whole_row_workgroups(dk, dv, C, dtype):
+    inp = workloads.make_inputs(64, 70, 4, dk, dv, dtype, s0_std=0.02, seed=600 + dk + dv + C)
+    check(inp, C, TOL[dtype], label=f"256 units dk{dk} dv{dv}")
+    check_bf16_output(inp, C)
+
+
+def test_whole_row_workgroups_packed_with_checkpoints():
+    g = torch.Generator().manual_seed(610)
+    lens = torch.randint(0, 200, (130,), generator=g).tolist()
+    lens[:4] = [0, 1, 64, 129]
+    inp = workloads.make_inputs(1, 0, 2, 128, 128, torch.bfloat16, s0_std=0.02, seed=611, lengths=lens)
+    check(inp, 64, TOL[torch.bfloat16], label="130 packed sequences x H2")
+    _ckpt_check(inp, 64, 64, 2, TOL[torch.bfloat16], "130 packed sequences x H2")
