@@ -201,11 +201,29 @@ template <int DK, int C, typename T> struct Intra {
     static constexpr int kMinBlocks = kLds <= 81920 ? 2 : 1;
 };
 
-// kOpts: the input options (decay floor, scalar gate, fused transforms) are
-// compiled in; plain calls run the instance without them.
-template <int DK, int C, typename In, bool kOpts>
+// Input modes of the intra-chunk kernel; each is its own instance, so a
+// plain call runs none of the option code (the first build with the options
+// compiled into every call cost 24 VGPRs and 6 %).
+enum InMode {
+    kInPlain = 0,    // alpha per key channel as given
+    kInOpts = 1,     // per-channel alpha; floor and fused transforms at run time
+    kInFloor = 2,    // per-channel alpha floored at >= 2^-0.75 (no other option)
+    kInScalar = 3,   // one alpha per (token, head); floor and fused transforms at run time
+};
+// A decay floor of at least 2^-0.75 bounds the decay of a 16-token block by
+// 2^-12 in every channel, which is the factored Gram path's range: the
+// floored instance needs neither the per-chunk range check nor the exact path.
+constexpr float kFloorFast = 0.59460356f;   // 2^-0.75
+
+template <int DK, int C, typename In, int kIn>
 __global__ __launch_bounds__(256, (Intra<DK, C, typename OperandOf<In>::type>::kMinBlocks))
 void kda_intra_kernel(const PrefillArgs a) {
+    // kOpts: floor and fused transforms applied at run time; kScalar: one decay
+    // per token (the Gram is plain Q K^T and K K^T with a rank-1 decay mask);
+    // kSureFast: every chunk takes the factored / masked Gram
+    constexpr bool kOpts = kIn == kInOpts || kIn == kInScalar;
+    constexpr bool kScalar = kIn == kInScalar;
+    constexpr bool kSureFast = kIn == kInFloor || kIn == kInScalar;
     using T = typename OperandOf<In>::type;
     using I = Intra<DK, C, T>;
     static_assert(I::kFits, "LDS budget of one gfx950 workgroup exceeded");
@@ -284,7 +302,7 @@ void kda_intra_kernel(const PrefillArgs a) {
             const int64_t base = row * DK + 8 * (p1 ? cg : 0);
             kraw[u].load(kg + base);
             qraw[u].load(qg + base);
-            if (kOpts && a.alpha_scalar) ascal[u] = a.alpha[row];
+            if constexpr (kScalar) ascal[u] = a.alpha[row];
             else araw[u].load(a.alpha + base);
         }
 #pragma unroll
@@ -292,19 +310,23 @@ void kda_intra_kernel(const PrefillArgs a) {
             const bool ok = p1 && 4 * sgi + u < valid;
             kraw[u].unpack(kr[u]);
             qraw[u].unpack(qr[u]);
-            if (kOpts && a.alpha_scalar) {
+            if constexpr (kScalar) {
+                // one decay for the token, formed once and shared by the channels
+                float as = ascal[u];
+                if (a.fuse_inputs) as = sigmoid(as);
+                as = fmaxf(as, a.alpha_floor);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) al[u][e] = ascal[u];
+                for (int e = 0; e < 8; ++e) al[u][e] = as;
             } else {
                 araw[u].unpack(al[u]);
-            }
-            if (kOpts && a.fuse_inputs) {
+                if (kOpts && a.fuse_inputs) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) al[u][e] = sigmoid(al[u][e]);
-            }
-            if (kOpts) {
+                    for (int e = 0; e < 8; ++e) al[u][e] = sigmoid(al[u][e]);
+                }
+                if (kIn != kInPlain) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) al[u][e] = fmaxf(al[u][e], a.alpha_floor);
+                    for (int e = 0; e < 8; ++e) al[u][e] = fmaxf(al[u][e], a.alpha_floor);
+                }
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -384,7 +406,39 @@ void kda_intra_kernel(const PrefillArgs a) {
     // segments of the channel group (a shuffle scan over NSEG adjacent lanes)
     float lg[4][8];  // inclusive running sum inside the segment
     float off[8], tot[8];
-    {
+    if constexpr (kScalar) {
+        // one exponent per token: a single scan, shared by the 8 channels
+        float run = 0.f, lgs[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            run += fmaxf(__builtin_amdgcn_logf(al[u][0]), kLog2Floor);
+            lgs[u] = run;
+        }
+        float incl = run;
+        if constexpr (I::NSEG == 16) {
+            incl = row_scan16(incl);
+        } else {
+#pragma unroll
+            for (int d = 1; d < I::NSEG; d <<= 1) {
+                const float t = __shfl_up(incl, d, I::NSEG);
+                if (sgi >= d) incl += t;
+            }
+        }
+        const float offs = incl - run, tots = __shfl(incl, I::NSEG - 1, I::NSEG);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            off[e] = offs;
+            tot[e] = tots;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) lg[u][e] = lgs[u];
+        }
+        // the token exponents g_r, for the decay mask of the Gram (the block
+        // exponent region is not used by this instance)
+        if (p1 && cg == 0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) Gs[4 * sgi + u] = offs + lgs[u];
+        }
+    } else {
         float run[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) run[e] = 0.f;
@@ -411,15 +465,15 @@ void kda_intra_kernel(const PrefillArgs a) {
             tot[e] = __shfl(incl, I::NSEG - 1, I::NSEG);
         }
     }
-    if (p1 && sp == 0) {
+    if (!kScalar && p1 && sp == 0) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) Gs[Rb * DK + 8 * cg + e] = off[e] + lg[0][e];
     }
-    if (p1 && sp == 3) {
+    if (!kScalar && p1 && sp == 3) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) Ge[Rb * DK + 8 * cg + e] = off[e] + lg[3][e];
     }
-    {
+    if constexpr (!kSureFast) {
         // decay range of each 16-token block (exponent at its first token minus
         // at its last), maximised over the wave's blocks and channels; the last
         // segment of a block is 3 lanes above its first
@@ -442,10 +496,10 @@ void kda_intra_kernel(const PrefillArgs a) {
         if (lane == 0) swmax[wave] = mx;
     }
     lds_barrier();
-    const bool fast = fmaxf(fmaxf(swmax[0], swmax[1]), fmaxf(swmax[2], swmax[3])) <= kFastRange;
+    const bool fast = kSureFast || fmaxf(fmaxf(swmax[0], swmax[1]), fmaxf(swmax[2], swmax[3])) <= kFastRange;
 
     // ---- phase 1 (cont.): operand factors, tiles and the workspace quads ----
-    if (fast && p1 && sp < Rb) {
+    if (!kScalar && fast && p1 && sp < Rb) {
         // pair factors 2^{G_R - G_I + h_I - h_R} (<= 1) of the off-diagonal tiles (R = Rb, I = sp)
         const int Ib = sp;
         float* dst = sIR + (Rb * (Rb - 1) / 2 + Ib) * DK + 8 * cg;
@@ -552,6 +606,11 @@ void kda_intra_kernel(const PrefillArgs a) {
                 store8(Ak + r * LD_ROW + 8 * cg, ak);
                 store8(Aq + r * LD_ROW + 8 * cg, aq);
                 store8(Bd + r * LD_ROW + 8 * cg, bd);
+            } else if (kScalar) {
+                // one decay per token: the Gram operands are k and q as they are
+                // (the decay enters as a mask on the fp32 products)
+                store8(Ak + r * LD_ROW + 8 * cg, kr[u]);
+                store8(Aq + r * LD_ROW + 8 * cg, qr[u]);
             }
             if constexpr (sizeof(T) == 2 && I::NSEG == 16 && I::NCG % 4 == 0) {
                 // (four channel groups per wave, so every lane has its partner)
@@ -595,7 +654,11 @@ void kda_intra_kernel(const PrefillArgs a) {
         }
     };
     if (p1) {
-        if (fast) factor_phase(BoolTag<true>{});
+        // the scalar gate takes the per-token exponents of the exact path's
+        // formulas (one exp2 per token: the channels share them) and the
+        // plain operands
+        if (kScalar) factor_phase(BoolTag<false>{});
+        else if (fast) factor_phase(BoolTag<true>{});
         else factor_phase(BoolTag<false>{});
     }
     lds_barrier();
@@ -619,7 +682,11 @@ void kda_intra_kernel(const PrefillArgs a) {
             pres[pi] = zero4();
             if (p < NP) {
                 Q aq[NQK], bk[NQK], bq[NQK];
-                if (Ib == R) {
+                if (kScalar) {   // plain k rows of block Ib
+#pragma unroll
+                    for (int u = 0; u < NQK; ++u)
+                        aq[u] = *reinterpret_cast<const Q*>(Ak + (16 * Ib + cl) * LD_ROW + 16 * u + 4 * g);
+                } else if (Ib == R) {
 #pragma unroll
                     for (int u = 0; u < NQK; ++u)
                         aq[u] = *reinterpret_cast<const Q*>(Bd + (16 * Ib + cl) * LD_ROW + 16 * u + 4 * g);
@@ -637,8 +704,8 @@ void kda_intra_kernel(const PrefillArgs a) {
                     bk[u] = *reinterpret_cast<const Q*>(Ak + (16 * R + cl) * LD_ROW + 16 * u + 4 * g);
                     bq[u] = *reinterpret_cast<const Q*>(Aq + (16 * R + cl) * LD_ROW + 16 * u + 4 * g);
                 }
-                mres[pi] = mma_quads(aq, bk, zero4());
-                pres[pi] = mma_quads(aq, bq, zero4());
+                // the M and P chains share A and are issued alternately
+                mma_quads_pair(aq, bk, bq, mres[pi], pres[pi]);
             }
         }
         lds_barrier();  // the operand tiles are dead from here on
@@ -649,6 +716,17 @@ void kda_intra_kernel(const PrefillArgs a) {
                 // lane holds M'^T[i = 16Ib + 4g + j][r = 16R + cl] for j = 0..3
                 const int r = 16 * pR[pi] + cl, i0 = 16 * pI[pi] + 4 * g;
                 const float br = sbeta[r];
+                if constexpr (kScalar) {
+                    // rank-1 decay mask 2^{g_r - g_i} (<= 1 where i <= r); Gs holds
+                    // the token exponents in this instance
+                    const float gr = Gs[r];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float dm = __builtin_amdgcn_exp2f(fminf(gr - Gs[i0 + j], 0.f));
+                        mres[pi][j] *= dm;
+                        pres[pi][j] *= dm;
+                    }
+                }
                 if (pI[pi] < pR[pi]) {
                     *reinterpret_cast<f32x4*>(MX + r * LD_F + i0) = br * mres[pi];
                     *reinterpret_cast<f32x4*>(Pm + r * LD_F + i0) = pres[pi];
@@ -1411,10 +1489,14 @@ static hipError_t launch_phase_t(const PrefillArgs& a, int max_chunks, bool intr
         if (intra) {
             if (max_chunks > 0) {
                 const dim3 grid((unsigned)max_chunks * (unsigned)a.H);
-                if (a.alpha_scalar || a.fuse_inputs || a.alpha_floor != 0.f)
-                    hipLaunchKernelGGL((kda_intra_kernel<DK, C, In, true>), grid, dim3(256), 0, stream, a);
+                if (a.alpha_scalar)
+                    hipLaunchKernelGGL((kda_intra_kernel<DK, C, In, kInScalar>), grid, dim3(256), 0, stream, a);
+                else if (!a.fuse_inputs && a.alpha_floor >= kFloorFast)
+                    hipLaunchKernelGGL((kda_intra_kernel<DK, C, In, kInFloor>), grid, dim3(256), 0, stream, a);
+                else if (a.fuse_inputs || a.alpha_floor != 0.f)
+                    hipLaunchKernelGGL((kda_intra_kernel<DK, C, In, kInOpts>), grid, dim3(256), 0, stream, a);
                 else
-                    hipLaunchKernelGGL((kda_intra_kernel<DK, C, In, false>), grid, dim3(256), 0, stream, a);
+                    hipLaunchKernelGGL((kda_intra_kernel<DK, C, In, kInPlain>), grid, dim3(256), 0, stream, a);
             }
         } else {
             const int units = a.N * a.H;

@@ -116,6 +116,21 @@ __device__ __forceinline__ f32x4 mma_quads_upto(const Q (&a)[N], const Q (&b)[N]
     return c;
 }
 
+// c0 += A B0 and c1 += A B1 over N quads, the two chains issued alternately.
+template <int N, typename Q>
+__device__ __forceinline__ void mma_quads_pair(const Q (&a)[N], const Q (&b0)[N], const Q (&b1)[N], f32x4& c0,
+                                               f32x4& c1) {
+#pragma unroll
+    for (int u = 0; u + 1 < N; u += 2) {
+        c0 = mma_step2(a[u], a[u + 1], b0[u], b0[u + 1], c0);
+        c1 = mma_step2(a[u], a[u + 1], b1[u], b1[u + 1], c1);
+    }
+    if constexpr (N % 2 == 1) {
+        c0 = mma_tail(a[N - 1], b0[N - 1], c0);
+        c1 = mma_tail(a[N - 1], b1[N - 1], c1);
+    }
+}
+
 // c[i] += sum over quads u in [0, N) of A_i,u * B_u for NT tiles that share
 // their B quads, issued K-step by K-step across the tiles: consecutive MFMAs
 // then write different accumulators, where the tile-by-tile order makes each

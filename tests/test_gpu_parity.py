@@ -662,3 +662,50 @@ def test_whole_row_workgroups_packed_with_checkpoints():
     inp = workloads.make_inputs(1, 0, 2, 128, 128, torch.bfloat16, s0_std=0.02, seed=611, lengths=lens)
     check(inp, 64, TOL[torch.bfloat16], label="130 packed sequences x H2")
     _ckpt_check(inp, 64, 64, 2, TOL[torch.bfloat16], "130 packed sequences x H2")
+
+
+# --- scalar-gate and floored-decay instances of the intra-chunk kernel --------------
+
+@pytest.mark.timeout(900)
+def test_scalar_gate_long_context_every_head():
+    """One decay per (token, head) at the long-context shape (B1 H32 T65536): every head against the oracle."""
+    w = workloads.CONFIGS[workloads.LONG_CONTEXT_PREFILL]
+    say("[case] scalar gate, long-context shape: generating inputs")
+    inp = workloads.config_inputs(workloads.LONG_CONTEXT_PREFILL)
+    inp["alpha"] = inp["alpha"][..., 0].contiguous()   # one sigmoid(N(4, 1)) draw per (token, head)
+    d = to_dev(inp)
+    o, S = kda.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], None, None, chunk_size=w.chunk,
+                         o_dtype=torch.float32, alpha_scalar=True)
+    torch.cuda.synchronize()
+    del d
+    eo, es = WholeTensorError(), WholeTensorError()
+    for h0 in range(0, 32, 16):
+        say(f"[case] scalar gate oracle heads {h0}..{h0 + 15}")
+        oo, So = kda_oracle.forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], heads=(h0, h0 + 16),
+                                    alpha_scalar=True)
+        eo.add(o[:, :, h0:h0 + 16].contiguous().cpu().numpy(), oo)
+        es.add(S[:, h0:h0 + 16].contiguous().cpu().numpy(), So)
+        del oo, So
+    say(f"    all 32 heads: err o={eo.value():.3e} S={es.value():.3e}")
+    assert eo.value() < TOL[w.dtype] and es.value() < TOL[w.dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("alpha_mu", [3.0, -3.0])
+def test_scalar_gate_shapes(dtype, alpha_mu):
+    # alpha_mu = -3: the decay over a chunk spans far more than any fp16 factor
+    # could hold; the scalar path's mask is formed in fp32 and needs no fallback
+    for (B, T, H, dk, dv, C) in ((2, 150, 3, 128, 64, 64), (1, 97, 2, 64, 128, 32), (2, 70, 2, 32, 32, 16)):
+        inp = _prefill_opts_inputs(B, T, H, dk, dv, dtype, seed=700 + T, alpha_mu=alpha_mu, alpha_scalar=True)
+        _prefill_opts_check(inp, C, TOL[dtype], f"B{B} T{T} dk{dk} dv{dv}", alpha_scalar=True)
+
+
+@pytest.mark.parametrize("floor", [0.59460356, 0.6, 0.95])
+def test_decay_floor_fast_instance(floor):
+    # floors at or above 2^-0.75 run the instance without the range check and
+    # the exact path; with alpha ~ sigmoid(N(-3, 1)) nearly every value is floored
+    for alpha_mu in (4.0, -3.0):
+        lens = [1, 63, 64, 65, 300, 7, 128]
+        inp = _prefill_opts_inputs(1, 0, 3, 128, 128, torch.bfloat16, seed=720, lengths=lens, alpha_mu=alpha_mu,
+                                   decay_floor=floor)
+        _prefill_opts_check(inp, 64, TOL[torch.bfloat16], f"packed {lens} mu {alpha_mu}", decay_floor=floor)
