@@ -22,7 +22,9 @@
  * Conventions shared by every entry point:
  *  - Every tensor argument is a DEVICE pointer owned by the caller.  The
  *    library allocates no device memory, keeps no pointer after returning and
- *    takes scratch only through the caller's workspace.
+ *    takes scratch only through the caller's workspace; the one exception is
+ *    kda_chunk_fwd_noalloc, whose scratch is a fixed device array the
+ *    library holds (see there).
  *  - Tensors are dense, row-major, last index fastest, with the shapes given
  *    below.  q, k, v, o, alpha and states must be 16-byte aligned; beta and
  *    cu_seqlens 4-byte aligned; workspace 256-byte aligned.
@@ -31,9 +33,11 @@
  *  - Arguments are validated before anything is launched: a call that
  *    returns an error has touched no output.  KDA_ERR_HIP reports a launch
  *    failure (the HIP error is consumed).  No C++ exception crosses the ABI.
- *  - Inputs must be finite.  The library holds no mutable global state;
- *    calls on different streams may run concurrently if their outputs and
- *    workspaces do not overlap.
+ *  - Inputs must be finite.  The only mutable global state is a per-device
+ *    cache of the compute-unit count and of kda_chunk_fwd_noalloc's scratch
+ *    address, each filled once; calls on different streams may run
+ *    concurrently if their outputs and workspaces do not overlap (never two
+ *    kda_chunk_fwd_noalloc calls on one device).
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -117,6 +121,31 @@ kda_status_t kda_chunk_fwd(const kda_chunk_params_t* params,
                            void* o, float* final_state,
                            void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* kda_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code running under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It allocates nothing and calls no
+ * allocating routine; its scratch is a device array of
+ * KDA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on every device it
+ * runs on until the process ends.
+ *  - Limit: a call whose workspace (kda_chunk_fwd_workspace_size) exceeds
+ *    KDA_NOALLOC_SCRATCH_BYTES returns KDA_ERR_WORKSPACE before anything is
+ *    launched; at dk = dv = 128, chunk 64, bf16 that is about 900 (chunk,
+ *    head) pairs, e.g. 57,000 token-heads of one sequence.
+ *  - Every call on a device shares that device's array: calls that may
+ *    overlap on one device (on different streams, or from host threads that
+ *    do not order them) race and must not be issued.  Calls ordered on one
+ *    stream are safe; no part of the array needs to start at zero.
+ *  - The first call on a device looks up the array's device address
+ *    (hipGetSymbolAddress) with that device current; KDA_ERR_HIP if it fails.
+ * Otherwise arguments, validation and results are those of kda_chunk_fwd:
+ * the same kernels run on the same layout, so the outputs are identical. */
+#define KDA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+kda_status_t kda_chunk_fwd_noalloc(const kda_chunk_params_t* params,
+                                   const void* q, const void* k, const void* v,
+                                   const float* alpha, const float* beta,
+                                   const float* initial_state, const int32_t* cu_seqlens,
+                                   void* o, float* final_state, void* stream);
 
 /* The two halves of kda_chunk_fwd, for callers that schedule them separately
  * (for example to time them, or to overlap the intra-chunk half of one call

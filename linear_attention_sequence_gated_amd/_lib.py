@@ -24,7 +24,9 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "
 # Every symbol include/kda.h declares.
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
             "kda_chunk_fwd_inter", "kda_chunk_fwd_ex", "kda_chunk_fwd_ex_workspace_size", "kda_decode_step",
-            "kda_decode_step_ex")
+            "kda_decode_step_ex", "kda_chunk_fwd_noalloc")
+# Bytes of the library-held scratch of kda_chunk_fwd_noalloc (KDA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class KdaError(RuntimeError):
@@ -86,6 +88,8 @@ def load() -> ctypes.CDLL:
     lib.kda_chunk_fwd_ex.restype = ctypes.c_int
     lib.kda_chunk_fwd_ex.argtypes = [ctypes.POINTER(ChunkParams), ctypes.POINTER(ChunkOptions),
                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(ChunkParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_step_ex.restype = ctypes.c_int
@@ -267,6 +271,43 @@ def chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_s
                    output_final_state, o, final_state, workspace, stream, o_dtype,
                    checkpoints, ckpt_every, decay_floor, alpha_scalar, fuse_inputs, gate, norm_weight,
                    norm_eps).run()
+
+
+def chunk_fwd_noalloc(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, o=None, final_state=None,
+                      chunk_size: int = 64, scale: float = 1.0, o_dtype: Optional[torch.dtype] = None,
+                      stream=None):
+    """kda_chunk_fwd_noalloc: kda_chunk_fwd on the library-held scratch, with no workspace.
+
+    The library allocates nothing for the call; ``o`` and ``final_state`` are
+    allocated here only when not given (pass both to allocate nothing at all).
+    Shapes and dtypes as chunk_fwd.  Returns (o, final_state).
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(k.shape == q.shape and alpha.shape == q.shape, "q, k, alpha must share [B,T,H,dk]")
+    _need(v.shape == (B, T, H, dv) and beta.shape == (B, T, H), "v/beta shapes")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
+    _need(alpha.dtype == torch.float32 and beta.dtype == torch.float32, "alpha, beta must be fp32")
+    for t in (q, k, v, alpha, beta):
+        _need(_on_device(t) and t.is_contiguous(), "inputs must be contiguous device tensors")
+    if cu_seqlens is not None:
+        _need(cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 2, "cu_seqlens must be int32 [N+1] with N >= 1")
+        _dense(cu_seqlens, (cu_seqlens.numel(),), torch.int32, "cu_seqlens")
+    n = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    _dense(initial_state, (n, H, dk, dv), torch.float32, "initial_state")
+    _dense(final_state, (n, H, dk, dv), torch.float32, "final_state")
+    o_dtype = q.dtype if o_dtype is None else o_dtype
+    _dense(o, v.shape, o_dtype, "o")
+    if o is None:
+        o = torch.empty(v.shape, dtype=o_dtype, device=v.device)
+    if final_state is None:
+        final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
+    params = chunk_params(q, v, cu_seqlens, chunk_size, scale, o_dtype)
+    _check("kda_chunk_fwd_noalloc",
+           load().kda_chunk_fwd_noalloc(ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                        _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(final_state),
+                                        _stream(stream)))
+    return o, final_state
 
 
 def decode_step(q, k, v, alpha, beta, state, scale: float = 1.0, o=None, stream=None,

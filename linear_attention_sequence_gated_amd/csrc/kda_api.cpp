@@ -5,7 +5,17 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "kda_kernels.h"
+
+// Scratch of kda_chunk_fwd_noalloc: device memory the library owns, so that
+// that entry point needs no allocation by anyone.  Each device that loads the
+// library holds its own copy until the process ends.  In host code the name
+// `scratch` is only a host-side stand-in; its device address is taken once
+// per device with hipGetSymbolAddress (noalloc_scratch() below) and that
+// address is what the kernels receive.
+static __device__ __align__(256) char scratch[KDA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -250,6 +260,51 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
 }
 
 }  // namespace
+
+}  // extern "C"
+
+namespace {
+
+// Device address of `scratch` on each device, taken on the first
+// kda_chunk_fwd_noalloc call with that device current (null: not yet).  Two
+// threads racing on the first call store the same address.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+kda_status_t noalloc_scratch(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return KDA_ERR_UNSUPPORTED;
+    void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();   // consume the error: the call reports it
+            return KDA_ERR_HIP;
+        }
+        g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+    *out = ptr;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_fwd_noalloc(const kda_chunk_params_t* p, const void* q, const void* k, const void* v,
+                                   const float* alpha, const float* beta, const float* initial_state,
+                                   const int32_t* cu_seqlens, void* o, float* final_state, void* stream) {
+    kda_status_t st = check_params(p);
+    if (st != KDA_OK) return st;
+    if (base_workspace(p) > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    st = noalloc_scratch(&ws);
+    if (st != KDA_OK) return st;
+    // every byte of the scratch a kernel reads is written earlier in the same
+    // call (chunk offsets, then the per-chunk blocks), so nothing is cleared
+    return chunk_fwd_impl(p, nullptr, q, k, v, alpha, beta, initial_state, cu_seqlens, o, final_state, ws,
+                          (size_t)KDA_NOALLOC_SCRATCH_BYTES, stream, kBoth);
+}
 
 kda_status_t kda_chunk_fwd(const kda_chunk_params_t* p, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, const float* initial_state,

@@ -163,3 +163,15 @@ def test_decode_step_ex_rejects_bad_options_before_launch(lib):
     assert call(Opt(norm_weight=0x30000)) == INVALID                 # a norm weight needs a gate
     assert call(Opt(), alpha=MISALIGNED) == INVALID                  # per-channel alpha: 16-byte aligned
     assert call(Opt(alpha_mode=1), alpha=ctypes.c_void_p(0x10003)) == INVALID
+
+
+def test_noalloc_rejects_before_any_launch(lib):
+    # the library-held scratch holds 64 MiB: a long-context shape is refused,
+    # and bad parameters are refused as by kda_chunk_fwd, with no device call
+    fn = lib.kda_chunk_fwd_noalloc
+    args = [FAKE] * 9 + [None]
+    big = _params(seqlen=65536, num_heads=32)
+    assert fn(ctypes.byref(big), *args) == WORKSPACE
+    assert fn(ctypes.byref(_params(head_dim_k=96)), *args) == UNSUPPORTED
+    assert fn(ctypes.byref(_params(num_heads=0)), *args) == INVALID
+    assert fn(None, *args) == INVALID
