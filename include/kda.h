@@ -57,7 +57,8 @@ typedef enum {
     KDA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or shape    */
     KDA_ERR_UNSUPPORTED = 2, /* head dim, chunk size or dtype not built       */
     KDA_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned    */
-    KDA_ERR_HIP = 4          /* a HIP launch or runtime call failed           */
+    KDA_ERR_HIP = 4,         /* a HIP launch or runtime call failed           */
+    KDA_ERR_RANGE = 5        /* the result is not finite (kda_chunk_fwd_status) */
 } kda_status_t;
 
 /* Shape of one chunked-prefill call.  All fields are plain int32/int64/float
@@ -111,9 +112,14 @@ kda_status_t kda_chunk_fwd_workspace_size(const kda_chunk_params_t* params, size
  * The chunk form evaluates the same recurrence with intra-chunk products on
  * the matrix cores; results agree with the token-by-token recurrence up to
  * rounding.  fp32 inputs: fp32 arithmetic throughout.  bf16 inputs: matrix-
- * core operands and chunk intermediates in fp16 (11-bit mantissa) with fp32
- * accumulation and an fp32 state, so |v| and the state must stay well inside
- * the fp16 range (below about 1e4 in magnitude). */
+ * core operands and chunk intermediates in fp16 (11-bit mantissa, largest
+ * value 65504) with fp32 accumulation and an fp32 state.  Range contract: a
+ * call whose intermediates leave that range (in practice |v| or the state of
+ * order 1e4 and above, or keys far from unit norm) does not return a silent
+ * result: every value the call writes to o, final_state and checkpoints is
+ * checked on the device, and kda_chunk_fwd_status then reports
+ * KDA_ERR_RANGE; the outputs of such a call hold inf or NaN and must not be
+ * used.  Results that kda_chunk_fwd_status accepts are finite. */
 kda_status_t kda_chunk_fwd(const kda_chunk_params_t* params,
                            const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta,
@@ -146,6 +152,16 @@ kda_status_t kda_chunk_fwd_noalloc(const kda_chunk_params_t* params,
                                    const float* alpha, const float* beta,
                                    const float* initial_state, const int32_t* cu_seqlens,
                                    void* o, float* final_state, void* stream);
+
+/* Range status of the last kda_chunk_fwd / kda_chunk_fwd_ex call (or
+ * _intra + _inter pair) made with `workspace`: KDA_OK when every value it
+ * wrote to o, final_state and checkpoints is finite, KDA_ERR_RANGE when one
+ * is not (see the range contract above).  The intra-chunk half clears the
+ * status word (the first 256 bytes of the workspace) and the inter-chunk
+ * half sets it, so it is read after both on the same stream.  This call
+ * copies 4 bytes to the host and SYNCHRONISES `stream`.  Errors:
+ * KDA_ERR_INVALID_ARG (NULL or misaligned workspace), KDA_ERR_HIP. */
+kda_status_t kda_chunk_fwd_status(const void* workspace, void* stream);
 
 /* The two halves of kda_chunk_fwd, for callers that schedule them separately
  * (for example to time them, or to overlap the intra-chunk half of one call

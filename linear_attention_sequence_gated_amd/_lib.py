@@ -19,12 +19,13 @@ from . import build as _build
 KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
-           4: "KDA_ERR_HIP"}
+           4: "KDA_ERR_HIP", 5: "KDA_ERR_RANGE"}
+KDA_ERR_RANGE = 5
 
 # Every symbol include/kda.h declares.
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
             "kda_chunk_fwd_inter", "kda_chunk_fwd_ex", "kda_chunk_fwd_ex_workspace_size", "kda_decode_step",
-            "kda_decode_step_ex", "kda_chunk_fwd_noalloc")
+            "kda_decode_step_ex", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_status")
 # Bytes of the library-held scratch of kda_chunk_fwd_noalloc (KDA_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -88,6 +89,8 @@ def load() -> ctypes.CDLL:
     lib.kda_chunk_fwd_ex.restype = ctypes.c_int
     lib.kda_chunk_fwd_ex.argtypes = [ctypes.POINTER(ChunkParams), ctypes.POINTER(ChunkOptions),
                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kda_chunk_fwd_status.restype = ctypes.c_int
+    lib.kda_chunk_fwd_status.argtypes = [vp, vp]
     lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(ChunkParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
@@ -242,6 +245,17 @@ class Prefill:
             _check("kda_chunk_fwd", self._lib.kda_chunk_fwd(*self._args))
         return self.o, self.final_state
 
+    def status(self) -> int:
+        """kda_chunk_fwd_status of the last run (synchronises the stream): 0, or KDA_ERR_RANGE."""
+        st = self._lib.kda_chunk_fwd_status(self._args[10], self._args[12])
+        if st not in (0, KDA_ERR_RANGE):
+            _check("kda_chunk_fwd_status", st)
+        return st
+
+    def check_range(self):
+        """Raise KdaError(KDA_ERR_RANGE) if the last run wrote a value that is not finite."""
+        _check("kda_chunk_fwd_status", self.status())
+
     def intra(self):
         _check("kda_chunk_fwd_intra", self._lib.kda_chunk_fwd_intra(*self._args))
 
@@ -254,7 +268,8 @@ def chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_s
               scale: float = 1.0, output_final_state: bool = True, o=None, final_state=None,
               workspace=None, stream=None, o_dtype: Optional[torch.dtype] = None,
               checkpoints=None, ckpt_every: int = 0, decay_floor: float = 0.0, alpha_scalar: bool = False,
-              fuse_inputs: bool = False, gate=None, norm_weight=None, norm_eps: float = 0.0):
+              fuse_inputs: bool = False, gate=None, norm_weight=None, norm_eps: float = 0.0,
+              check_range: bool = True):
     """Chunked KDA prefill through kda_chunk_fwd.  Returns (o, final_state or None).
 
     q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32, same dtype), alpha [B,T,H,dk] fp32,
@@ -266,11 +281,18 @@ def chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_s
     ``decay_floor``, ``alpha_scalar`` (alpha [B,T,H]), ``fuse_inputs`` (L2 norm of q, k;
     alpha, beta given as logits) and ``gate`` [B,T,H,dv] with ``norm_weight`` [dv] and
     ``norm_eps`` (output norm and sigmoid gate) are the other kda_chunk_options_t fields.
+    With ``check_range`` (the default) the call then reads kda_chunk_fwd_status, which
+    synchronises the stream, and raises KdaError (status KDA_ERR_RANGE) when a written
+    value is not finite (an intermediate left the fp16 operand range of the bf16 path).
     """
-    return Prefill(q, k, v, alpha, beta, initial_state, cu_seqlens, chunk_size, scale,
-                   output_final_state, o, final_state, workspace, stream, o_dtype,
-                   checkpoints, ckpt_every, decay_floor, alpha_scalar, fuse_inputs, gate, norm_weight,
-                   norm_eps).run()
+    pre = Prefill(q, k, v, alpha, beta, initial_state, cu_seqlens, chunk_size, scale,
+                  output_final_state, o, final_state, workspace, stream, o_dtype,
+                  checkpoints, ckpt_every, decay_floor, alpha_scalar, fuse_inputs, gate, norm_weight,
+                  norm_eps)
+    out = pre.run()
+    if check_range:
+        pre.check_range()
+    return out
 
 
 def chunk_fwd_noalloc(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, o=None, final_state=None,

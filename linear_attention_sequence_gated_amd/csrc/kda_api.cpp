@@ -25,6 +25,10 @@ bool head_dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Workspace: [range status word (kWsAlign bytes)] [chunk-offset table (packed
+// input only)] [per (chunk, head) blocks] [gate scratch (split gated calls)].
+constexpr size_t kStatusBytes = kWsAlign;
+
 struct PrefillPlan {
     int64_t max_chunks;     // per head, worst case
     int64_t block_bytes;    // per (chunk, head)
@@ -64,7 +68,7 @@ PrefillPlan plan_prefill(const kda_chunk_params_t* p, bool packed, bool whole) {
     pl.block_bytes = kda::chunk_block_bytes(p->head_dim_k, (int)C, p->head_dim_v, p->qkv_dtype == KDA_DTYPE_BF16,
                                             kda::slice_group(p->head_dim_v, whole));
     pl.off_bytes = packed ? round_up(sizeof(int32_t) * ((size_t)p->num_seqs + 1), kWsAlign) : 0;
-    pl.total = pl.off_bytes + (size_t)pl.max_chunks * (size_t)p->num_heads * (size_t)pl.block_bytes;
+    pl.total = kStatusBytes + pl.off_bytes + (size_t)pl.max_chunks * (size_t)p->num_heads * (size_t)pl.block_bytes;
     return pl;
 }
 
@@ -97,6 +101,9 @@ const char* kda_status_string(kda_status_t s) {
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: head dim, chunk size or dtype not supported";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing, too small or misaligned";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch or runtime call failed";
+        case KDA_ERR_RANGE:
+            return "KDA_ERR_RANGE: the result is not finite (an fp16 matrix-core operand of the bf16 path, or an "
+                   "fp32 value, left its range)";
     }
     return "KDA: unknown status";
 }
@@ -193,7 +200,14 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
         if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_WORKSPACE;
         if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
     }
-    if (!final_state && !has_tokens) return KDA_OK;  // nothing to compute or write (no checkpoint is reached)
+    if (!final_state && !has_tokens) {   // nothing to compute or write (no checkpoint is reached)
+        if (!(phases & kIntra)) return KDA_OK;
+        // the range status still reads clear afterwards
+        return kda::launch_clear_status(reinterpret_cast<int32_t*>(workspace), reinterpret_cast<hipStream_t>(stream)) ==
+                       hipSuccess
+                   ? KDA_OK
+                   : KDA_ERR_HIP;
+    }
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* ws = reinterpret_cast<char*>(workspace);
@@ -206,9 +220,10 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
     a.s0 = initial_state;
     a.s_final = final_state;
     a.cu_seqlens = cu_seqlens;
-    a.chunk_off = packed ? reinterpret_cast<const int32_t*>(ws) : nullptr;
+    a.status = reinterpret_cast<int32_t*>(ws);
+    a.chunk_off = packed ? reinterpret_cast<const int32_t*>(ws + kStatusBytes) : nullptr;
     a.o = o;
-    a.ws_chunks = ws + pl.off_bytes;
+    a.ws_chunks = ws + kStatusBytes + pl.off_bytes;
     a.T = p->seqlen;
     a.N = p->num_seqs;
     a.H = p->num_heads;
@@ -242,10 +257,13 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
     hipError_t e = hipSuccess;
     if (phases & kIntra) {
         if (packed) {
-            e = kda::launch_chunk_offsets(cu_seqlens, p->num_seqs, C, reinterpret_cast<int32_t*>(ws), s);
+            e = kda::launch_chunk_offsets(cu_seqlens, p->num_seqs, C, reinterpret_cast<int32_t*>(ws + kStatusBytes), s);
             if (e != hipSuccess) return KDA_ERR_HIP;
         }
-        e = kda::launch_intra(a, p->head_dim_k, C, bf16, (int)pl.max_chunks, s);
+        // the intra-chunk kernel clears the range status; without chunks to
+        // process it is not launched and a one-thread kernel clears it
+        e = pl.max_chunks > 0 ? kda::launch_intra(a, p->head_dim_k, C, bf16, (int)pl.max_chunks, s)
+                              : kda::launch_clear_status(a.status, s);
         if (e != hipSuccess) return KDA_ERR_HIP;
     }
     if (phases & kInter) {
@@ -304,6 +322,18 @@ kda_status_t kda_chunk_fwd_noalloc(const kda_chunk_params_t* p, const void* q, c
     // call (chunk offsets, then the per-chunk blocks), so nothing is cleared
     return chunk_fwd_impl(p, nullptr, q, k, v, alpha, beta, initial_state, cu_seqlens, o, final_state, ws,
                           (size_t)KDA_NOALLOC_SCRATCH_BYTES, stream, kBoth);
+}
+
+kda_status_t kda_chunk_fwd_status(const void* workspace, void* stream) {
+    if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_INVALID_ARG;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int32_t flag = 0;
+    if (hipMemcpyAsync(&flag, workspace, sizeof flag, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess) {
+        (void)hipGetLastError();
+        return KDA_ERR_HIP;
+    }
+    return flag ? KDA_ERR_RANGE : KDA_OK;
 }
 
 kda_status_t kda_chunk_fwd(const kda_chunk_params_t* p, const void* q, const void* k, const void* v,

@@ -19,6 +19,8 @@ struct PrefillArgs {
     const int32_t* chunk_off;    // [N + 1] chunk index of each sequence (packed input)
     void* o;
     char* ws_chunks;             // per-(chunk, head) blocks
+    int32_t* status;             // range status of the call: cleared by the intra-chunk kernel, set to 1 by
+                                 // the inter-chunk kernel when a value it writes is not finite
     int64_t T;                   // tokens per row, or total packed tokens
     int32_t N, H, DV;
     int32_t chunks_per_seq;      // fixed length: ceil(T / C)
@@ -62,6 +64,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_chunk_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t* chunk_off, hipStream_t s);
+// Clears the range status word (calls without tokens launch no intra-chunk kernel).
+hipError_t launch_clear_status(int32_t* status, hipStream_t s);
 // C is the requested chunk size; the chunk the kernels use is
 // effective_chunk(DK, C, bf16) (fp32 operands with dk = 128 use at most 32).
 int effective_chunk(int DK, int C, bool bf16);

@@ -73,6 +73,14 @@ constexpr float kFastRange = 12.f;
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
 
+// Whether all four values are finite.  The inter-chunk kernel checks what it
+// writes: with finite inputs, an operand that left its format's range (fp16
+// matrix-core operands on the bf16 path) shows up as inf or NaN in o or in
+// the state, and the call's status word records it.
+__device__ __forceinline__ bool finite4(const f32x4& v) {
+    return __builtin_isfinite(v[0]) & __builtin_isfinite(v[1]) & __builtin_isfinite(v[2]) & __builtin_isfinite(v[3]);
+}
+
 // Workgroup barrier for LDS producer/consumer hand-offs only.  __syncthreads
 // also waits for every outstanding global load and store of the wave (vmcnt),
 // which would expose the workspace stores and the early v loads of the
@@ -255,6 +263,9 @@ void kda_intra_kernel(const PrefillArgs a) {
     // (1.365 ms against 1.448 ms per launch with chunks fastest on the
     // long-context workload)
     const int x = (int)(blockIdx.x / (unsigned)a.H), h = (int)(blockIdx.x % (unsigned)a.H);
+    // the call's range status starts clear; the inter-chunk kernel, which runs
+    // after this one on the stream, may set it
+    if (blockIdx.x == 0 && tid == 0) *a.status = 0;
     ChunkPos pos;
     if (!locate_chunk(a, C, x, pos)) return;  // uniform over the workgroup
     const int valid = pos.valid;
@@ -1221,10 +1232,17 @@ void kda_inter_kernel(const PrefillArgs a) {
                     for (int j = 0; j < 4; ++j)
                         a.s_final[sbase + (int64_t)(16 * t + 4 * g + j) * DV + 16 * sl + cl] = acc[t][j];
             }
+            // a non-finite state element stays non-finite through every later
+            // chunk (and reaches its checkpoints), so the final one tells
+            bool fin = true;
+#pragma unroll
+            for (int t = 0; t < NQK; ++t) fin &= finite4(acc[t]);
+            if (!fin) *a.status = 1;
             return;
         }
         // ---- output wave: O^T = S^T Qtilde^T + U^T P^T of chunk jn - 1 ------------
         // (lane: columns 16 sl + 4g + j, token 16tb + cl)
+        bool fin = true;   // every output this lane formed was finite
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         for (int jn = 0; jn < nint; ++jn) {
             if (jn >= 1) {
@@ -1248,6 +1266,7 @@ void kda_inter_kernel(const PrefillArgs a) {
                     const int r = 16 * tb + cl;
                     // two chains summed on the VALU (no K=16 step accumulates onto a K=32 result)
                     const f32x4 sc = (mma_quads(sb, qq, zero4()) + mma_quads_upto(ub, pq, tb, zero4())) * a.scale;
+                    fin &= finite4(sc);
                     if constexpr (kMode == kOutSplit) {
                         float sn = sc[0] * sc[0] + sc[1] * sc[1] + sc[2] * sc[2] + sc[3] * sc[3];
                         sn += __shfl_xor(sn, 16, 64);
@@ -1266,6 +1285,7 @@ void kda_inter_kernel(const PrefillArgs a) {
             }
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         }
+        if (!fin) *a.status = 1;
     } else {
         if (wave >= ncw) {
             // ---- I/O waves -----------------------------------------------------------
@@ -1325,6 +1345,7 @@ void kda_inter_kernel(const PrefillArgs a) {
                 for (int j = 0; j < 4; ++j)
                     acc[n][t][j] = (a.s0 && n < nsl) ? a.s0[sbase + (int64_t)(16 * t + 4 * g + j) * DV + 16 * (s0 + n) + cl] : 0.f;
 
+        bool fin = true;   // every output this lane formed was finite
         // gated calls: a chunk's outputs wait in registers until every wave's
         // partial sums of squares are in LDS (after the chunk's barrier); the
         // norm, weight and gate are then applied and the outputs stored
@@ -1430,6 +1451,7 @@ void kda_inter_kernel(const PrefillArgs a) {
                     // single K=16 step, which must not accumulate onto a K=32 result
                     const f32x4 ot = mma_quads(sb[n], qq, zero4()) + mma_quads_upto(ub[n], pq, tb, zero4());
                     const f32x4 sc = ot * a.scale;
+                    if (n < nsl) fin &= finite4(sc);
                     if constexpr (kGate) {
                         opend[tb][n] = sc;
                         if (n < nsl) ss += sc[0] * sc[0] + sc[1] * sc[1] + sc[2] * sc[2] + sc[3] * sc[3];
@@ -1463,6 +1485,12 @@ void kda_inter_kernel(const PrefillArgs a) {
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         }
         if (kGate && pending) flush();   // the last chunk, past its barrier
+#pragma unroll
+        for (int n = 0; n < SPW; ++n)
+            if (n < nsl)
+#pragma unroll
+                for (int t = 0; t < NQK; ++t) fin &= finite4(acc[n][t]);
+        if (!fin) *a.status = 1;
         if (a.s_final) {
 #pragma unroll
             for (int n = 0; n < SPW; ++n)
@@ -1559,6 +1587,15 @@ template <typename T> static bool fits(int DK, int C) {
 int effective_chunk(int DK, int C, bool bf16) {
     while (C > 16 && !(bf16 ? fits<_Float16>(DK, C) : fits<float>(DK, C))) C /= 2;
     return C;
+}
+
+__global__ __launch_bounds__(64) void kda_clear_status(int32_t* status) {
+    if (threadIdx.x == 0) *status = 0;
+}
+
+hipError_t launch_clear_status(int32_t* status, hipStream_t s) {
+    hipLaunchKernelGGL(kda_clear_status, dim3(1), dim3(64), 0, s, status);
+    return hipGetLastError();
 }
 
 hipError_t launch_chunk_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t* chunk_off, hipStream_t s) {

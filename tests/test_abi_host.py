@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         s = kda.status_string(code)
         assert s.startswith("KDA_")
     assert "unknown" in kda.status_string(99)
@@ -175,3 +175,8 @@ def test_noalloc_rejects_before_any_launch(lib):
     assert fn(ctypes.byref(_params(head_dim_k=96)), *args) == UNSUPPORTED
     assert fn(ctypes.byref(_params(num_heads=0)), *args) == INVALID
     assert fn(None, *args) == INVALID
+
+
+def test_status_query_rejects_bad_workspace(lib):
+    assert lib.kda_chunk_fwd_status(None, None) == INVALID
+    assert lib.kda_chunk_fwd_status(ctypes.c_void_p(0x10010), None) == INVALID   # not 256-byte aligned

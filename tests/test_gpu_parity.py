@@ -709,3 +709,44 @@ def test_decay_floor_fast_instance(floor):
         inp = _prefill_opts_inputs(1, 0, 3, 128, 128, torch.bfloat16, seed=720, lengths=lens, alpha_mu=alpha_mu,
                                    decay_floor=floor)
         _prefill_opts_check(inp, 64, TOL[torch.bfloat16], f"packed {lens} mu {alpha_mu}", decay_floor=floor)
+
+
+# --- range contract of the bf16 path (fp16 matrix-core operands) --------------------
+
+def _large(dtype, v_scale=1.0, s0_scale=1.0, seed=900):
+    inp = workloads.make_inputs(1, 200, 2, 128, 128, dtype, s0_std=0.02, seed=seed)
+    inp["v"] = (inp["v"].float() * v_scale).to(dtype)
+    inp["S0"] = inp["S0"] * s0_scale
+    return inp
+
+
+@pytest.mark.parametrize("v_scale,s0_scale", [(1e5, 1.0), (1.0, 5e6)])
+def test_range_guard_reports_overflow(v_scale, s0_scale):
+    """|v| or the state past the fp16 range: KDA_ERR_RANGE, never a silent inf; fp32 inputs compute it."""
+    say(f"[case] range guard v x{v_scale:g} S0 x{s0_scale:g}")
+    inp = _large(torch.bfloat16, v_scale, s0_scale)
+    with pytest.raises(kda.KdaError) as e:
+        gpu_prefill(inp, 64)
+    assert e.value.status == kda.KDA_ERR_RANGE
+    # the same values in fp32 inputs run in fp32 and match the oracle
+    inp32 = _large(torch.float32, v_scale, s0_scale)
+    check(inp32, 64, TOL[torch.float32], label=f"fp32 v x{v_scale:g} S0 x{s0_scale:g}")
+
+
+def test_range_guard_large_values_inside_range():
+    """Values well above 1 but inside the fp16 range compute normally and pass the status check."""
+    check(_large(torch.bfloat16, v_scale=300.0, s0_scale=3000.0), 64, TOL[torch.bfloat16], label="v x300 S0 x3000")
+
+
+def test_range_status_reads_clear_after_an_empty_call():
+    """A call that writes no token (T = 0) leaves the status word clear even after an overflowing call."""
+    inp = _large(torch.bfloat16, 1e5)
+    d = to_dev(inp)
+    pre = kda.Prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], None, chunk_size=64)
+    pre.run()
+    assert pre.status() == kda.KDA_ERR_RANGE
+    e = {k: (v[:, :0].contiguous() if k in ("q", "k", "v", "alpha", "beta") else v) for k, v in d.items()}
+    pre0 = kda.Prefill(e["q"], e["k"], e["v"], e["alpha"], e["beta"], e["S0"], None, chunk_size=64,
+                       workspace=pre.workspace)
+    pre0.run()
+    assert pre0.status() == 0
