@@ -90,6 +90,30 @@ const char* kda_status_string(kda_status_t status);
  * Errors: KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED as for kda_chunk_fwd. */
 kda_status_t kda_chunk_fwd_workspace_size(const kda_chunk_params_t* params, size_t* bytes);
 
+/* How kda_chunk_fwd runs a call of `params` on the current device, for tuning
+ * and diagnostics (the results do not depend on it beyond rounding).
+ * `packed` != 0 describes a call with cu_seqlens (then batch must be 1).
+ * Without a usable device the plan assumes 256 compute units.  Fields:
+ *   chunk_size    the chunk length used (fp32 inputs with dk = 128: <= 32)
+ *   whole_rows    1 when each inter-chunk workgroup carries whole state rows
+ *                 of one (sequence, head), 0 when it carries 16 columns
+ *   range_chunks  L > 0 when the inter-chunk pass cuts every sequence into
+ *                 ranges of L chunks that run side by side: the affine map
+ *                 S -> A S + B of each range is formed first, a scan of those
+ *                 maps gives every range its start state, then the ranges
+ *                 run.  0 when one workgroup walks each whole sequence.
+ *   max_ranges    ranges per head held in the workspace (0 without ranges)
+ * Errors: KDA_ERR_INVALID_ARG (NULL plan, packed with batch != 1) and the
+ * shape errors of kda_chunk_fwd. */
+typedef struct {
+    int32_t chunk_size;
+    int32_t whole_rows;
+    int32_t range_chunks;
+    int32_t max_ranges;
+} kda_chunk_plan_t;
+
+kda_status_t kda_chunk_fwd_plan(const kda_chunk_params_t* params, int32_t packed, kda_chunk_plan_t* plan);
+
 /* Chunked prefill: run the recurrence over every token of every sequence.
  *
  * Layout (D = params->qkv_dtype, B = batch, T = seqlen, H = num_heads):

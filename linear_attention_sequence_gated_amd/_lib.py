@@ -25,7 +25,7 @@ KDA_ERR_RANGE = 5
 # Every symbol include/kda.h declares.
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
             "kda_chunk_fwd_inter", "kda_chunk_fwd_ex", "kda_chunk_fwd_ex_workspace_size", "kda_decode_step",
-            "kda_decode_step_ex", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_status")
+            "kda_decode_step_ex", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_status", "kda_chunk_fwd_plan")
 # Bytes of the library-held scratch of kda_chunk_fwd_noalloc (KDA_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -41,6 +41,12 @@ class ChunkParams(ctypes.Structure):
                 ("num_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32),
                 ("head_dim_v", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("qkv_dtype", ctypes.c_int32), ("o_dtype", ctypes.c_int32)]
+
+
+class ChunkPlan(ctypes.Structure):
+    """kda_chunk_plan_t (include/kda.h)."""
+    _fields_ = [("chunk_size", ctypes.c_int32), ("whole_rows", ctypes.c_int32),
+                ("range_chunks", ctypes.c_int32), ("max_ranges", ctypes.c_int32)]
 
 
 class ChunkOptions(ctypes.Structure):
@@ -79,6 +85,8 @@ def load() -> ctypes.CDLL:
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_int
     lib.kda_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(ChunkParams), ctypes.POINTER(sz)]
+    lib.kda_chunk_fwd_plan.restype = ctypes.c_int
+    lib.kda_chunk_fwd_plan.argtypes = [ctypes.POINTER(ChunkParams), i32, ctypes.POINTER(ChunkPlan)]
     for name in ("kda_chunk_fwd", "kda_chunk_fwd_intra", "kda_chunk_fwd_inter"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
@@ -164,6 +172,16 @@ def workspace_size(q: torch.Tensor, v: torch.Tensor, cu_seqlens=None, chunk_size
     _check("kda_chunk_fwd_workspace_size", load().kda_chunk_fwd_workspace_size(ctypes.byref(p),
                                                                               ctypes.byref(out)))
     return out.value
+
+
+def chunk_plan(q: torch.Tensor, v: torch.Tensor, cu_seqlens=None, chunk_size: int = 64) -> dict:
+    """How kda_chunk_fwd runs a call of this shape on the current device
+    (kda_chunk_fwd_plan): chunk_size, whole_rows, range_chunks, max_ranges."""
+    p = chunk_params(q, v, cu_seqlens, chunk_size, 1.0)
+    out = ChunkPlan()
+    _check("kda_chunk_fwd_plan", load().kda_chunk_fwd_plan(ctypes.byref(p), int(cu_seqlens is not None),
+                                                          ctypes.byref(out)))
+    return {name: getattr(out, name) for name, _ in ChunkPlan._fields_}
 
 
 class Prefill:

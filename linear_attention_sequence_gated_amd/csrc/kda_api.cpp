@@ -26,13 +26,22 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace: [range status word (kWsAlign bytes)] [chunk-offset table (packed
-// input only)] [per (chunk, head) blocks] [gate scratch (split gated calls)].
+// input only)] [per (chunk, head) blocks] [chunk-range scan: range-offset
+// table (packed), range maps, range start states] [gate scratch (split gated
+// calls)].
 constexpr size_t kStatusBytes = kWsAlign;
 
 struct PrefillPlan {
     int64_t max_chunks;     // per head, worst case
     int64_t block_bytes;    // per (chunk, head)
     size_t off_bytes;       // chunk-offset table (packed input only)
+    bool whole;             // whole-row inter-chunk workgroups
+    int range_len;          // chunks per range of the chunk-range scan (0: none)
+    int64_t max_ranges;     // ranges of the call at most
+    int ranges_per_seq;     // fixed-length input
+    size_t range_off;       // byte offsets of the range tables in the workspace
+    size_t range_ab;
+    size_t range_start;
     size_t total;
 };
 
@@ -58,17 +67,42 @@ int chunk_of(const kda_chunk_params_t* p) {
     return kda::effective_chunk(p->head_dim_k, p->chunk_size, p->qkv_dtype == KDA_DTYPE_BF16);
 }
 
-PrefillPlan plan_prefill(const kda_chunk_params_t* p, bool packed, bool whole) {
+// The layout of one call: packed or fixed-length input, with or without the
+// output gate (gated calls keep the one-slice / fused-gate structure and take
+// no chunk ranges).
+PrefillPlan plan_prefill(const kda_chunk_params_t* p, bool packed, bool gate) {
     PrefillPlan pl{};
     const int64_t C = chunk_of(p);
+    const bool bf16 = p->qkv_dtype == KDA_DTYPE_BF16;
+    const int64_t units = (int64_t)p->num_seqs * p->num_heads;
+    const int64_t cps = (p->seqlen + C - 1) / C;   // fixed-length chunks per sequence
     if (packed)
         pl.max_chunks = p->seqlen / C + p->num_seqs + 1;
     else
-        pl.max_chunks = (int64_t)p->batch * ((p->seqlen + C - 1) / C);
-    pl.block_bytes = kda::chunk_block_bytes(p->head_dim_k, (int)C, p->head_dim_v, p->qkv_dtype == KDA_DTYPE_BF16,
-                                            kda::slice_group(p->head_dim_v, whole));
+        pl.max_chunks = (int64_t)p->batch * cps;
+    // average chunks per sequence, for the choice of ranges
+    const int64_t per_unit = packed ? (p->seqlen / C + p->num_seqs) / p->num_seqs : cps;
+    pl.range_len = gate ? 0 : kda::range_length(p->head_dim_k, p->head_dim_v, (int)C, bf16, units, per_unit);
+    pl.whole = kda::whole_rows(units) || pl.range_len > 0;
+    pl.block_bytes = kda::chunk_block_bytes(p->head_dim_k, (int)C, p->head_dim_v, bf16,
+                                            kda::slice_group(p->head_dim_v, pl.whole));
     pl.off_bytes = packed ? round_up(sizeof(int32_t) * ((size_t)p->num_seqs + 1), kWsAlign) : 0;
-    pl.total = kStatusBytes + pl.off_bytes + (size_t)pl.max_chunks * (size_t)p->num_heads * (size_t)pl.block_bytes;
+    size_t at = kStatusBytes + pl.off_bytes + (size_t)pl.max_chunks * (size_t)p->num_heads * (size_t)pl.block_bytes;
+    if (pl.range_len > 0) {
+        const int64_t L = pl.range_len;
+        // every sequence has max(1, ceil(chunks / L)) ranges
+        pl.ranges_per_seq = (int)(cps > L ? (cps + L - 1) / L : 1);
+        pl.max_ranges = packed ? pl.max_chunks / L + p->num_seqs + 1 : (int64_t)p->num_seqs * pl.ranges_per_seq;
+        at = round_up(at, kWsAlign);
+        pl.range_off = at;
+        at += packed ? round_up(sizeof(int32_t) * ((size_t)p->num_seqs + 1), kWsAlign) : 0;
+        const size_t dk = p->head_dim_k, dv = p->head_dim_v, rh = (size_t)pl.max_ranges * p->num_heads;
+        pl.range_ab = at;
+        at += round_up(rh * dk * (dk + dv) * sizeof(float), kWsAlign);
+        pl.range_start = at;
+        at += round_up(rh * dk * dv * sizeof(float), kWsAlign);
+    }
+    pl.total = at;
     return pl;
 }
 
@@ -80,13 +114,13 @@ size_t gate_scratch_bytes(const kda_chunk_params_t* p) {
            round_up(rows * (size_t)(p->head_dim_v / 16) * 4, kWsAlign);
 }
 
-size_t base_workspace(const kda_chunk_params_t* p) {
+// The quote covers packed and fixed-length calls of the shape.
+size_t base_workspace(const kda_chunk_params_t* p, bool gate) {
     size_t most = 0;
-    for (int packed = 0; packed < 2; ++packed)
-        for (int whole = 0; whole < 2; ++whole) {
-            const PrefillPlan pl = plan_prefill(p, packed, whole);
-            most = pl.total > most ? pl.total : most;
-        }
+    for (int packed = 0; packed < 2; ++packed) {
+        const PrefillPlan pl = plan_prefill(p, packed, gate);
+        most = pl.total > most ? pl.total : most;
+    }
     return most;
 }
 
@@ -114,7 +148,20 @@ kda_status_t kda_chunk_fwd_workspace_size(const kda_chunk_params_t* p, size_t* b
     if (st != KDA_OK) return st;
     // the size is quoted for the worst case of either layout so that one
     // buffer serves packed and fixed-length calls of the same shape
-    *bytes = base_workspace(p);
+    *bytes = base_workspace(p, false);
+    return KDA_OK;
+}
+
+kda_status_t kda_chunk_fwd_plan(const kda_chunk_params_t* p, int32_t packed, kda_chunk_plan_t* plan) {
+    if (!plan) return KDA_ERR_INVALID_ARG;
+    const kda_status_t st = check_params(p);
+    if (st != KDA_OK) return st;
+    if (packed && p->batch != 1) return KDA_ERR_INVALID_ARG;
+    const PrefillPlan pl = plan_prefill(p, packed != 0, false);
+    plan->chunk_size = chunk_of(p);
+    plan->whole_rows = pl.whole ? 1 : 0;
+    plan->range_chunks = pl.range_len;
+    plan->max_ranges = pl.range_len > 0 ? (int32_t)pl.max_ranges : 0;
     return KDA_OK;
 }
 
@@ -123,7 +170,8 @@ kda_status_t kda_chunk_fwd_ex_workspace_size(const kda_chunk_params_t* p, const 
     if (!bytes) return KDA_ERR_INVALID_ARG;
     const kda_status_t st = check_params(p);
     if (st != KDA_OK) return st;
-    *bytes = base_workspace(p) + (options && options->gate ? gate_scratch_bytes(p) : 0);
+    const bool gate = options && options->gate;
+    *bytes = round_up(base_workspace(p, gate), kWsAlign) + (gate ? gate_scratch_bytes(p) : 0);
     return KDA_OK;
 }
 
@@ -192,9 +240,9 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
         if (overlaps(initial_state, sb, final_state, sb)) return KDA_ERR_INVALID_ARG;
     }
     const bool gate = op && op->gate;
-    const bool whole = kda::whole_rows((int64_t)p->num_seqs * p->num_heads);
+    const PrefillPlan pl = plan_prefill(p, packed, gate);
+    const bool whole = pl.whole;
     const bool split = gate && !whole;
-    const PrefillPlan pl = plan_prefill(p, packed, whole);
     const size_t need = round_up(pl.total, kWsAlign) + (split ? gate_scratch_bytes(p) : 0);
     if (need > 0) {
         if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_WORKSPACE;
@@ -245,6 +293,14 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
     }
     a.gsl = kda::slice_group(p->head_dim_v, whole);
     a.whole_rows = whole;
+    if (pl.range_len > 0) {
+        a.range_len = pl.range_len;
+        a.ranges_per_seq = pl.ranges_per_seq;
+        a.max_ranges = (int32_t)pl.max_ranges;
+        a.range_off = packed ? reinterpret_cast<const int32_t*>(ws + pl.range_off) : nullptr;
+        a.range_ab = reinterpret_cast<float*>(ws + pl.range_ab);
+        a.range_start = reinterpret_cast<float*>(ws + pl.range_start);
+    }
     const int64_t rows = (int64_t)p->batch * p->seqlen * p->num_heads;
     if (split) {
         a.gate_split = 1;
@@ -257,7 +313,10 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
     hipError_t e = hipSuccess;
     if (phases & kIntra) {
         if (packed) {
-            e = kda::launch_chunk_offsets(cu_seqlens, p->num_seqs, C, reinterpret_cast<int32_t*>(ws + kStatusBytes), s);
+            int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + kStatusBytes);
+            e = pl.range_len > 0 ? kda::launch_chunk_range_offsets(cu_seqlens, p->num_seqs, C, pl.range_len, chunk_off,
+                                                                   reinterpret_cast<int32_t*>(ws + pl.range_off), s)
+                                 : kda::launch_chunk_offsets(cu_seqlens, p->num_seqs, C, chunk_off, s);
             if (e != hipSuccess) return KDA_ERR_HIP;
         }
         // the intra-chunk kernel clears the range status; without chunks to
@@ -314,7 +373,7 @@ kda_status_t kda_chunk_fwd_noalloc(const kda_chunk_params_t* p, const void* q, c
                                    const int32_t* cu_seqlens, void* o, float* final_state, void* stream) {
     kda_status_t st = check_params(p);
     if (st != KDA_OK) return st;
-    if (base_workspace(p) > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
+    if (base_workspace(p, false) > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
     void* ws = nullptr;
     st = noalloc_scratch(&ws);
     if (st != KDA_OK) return st;

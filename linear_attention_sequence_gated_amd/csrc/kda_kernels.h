@@ -38,6 +38,17 @@ struct PrefillArgs {
     int32_t gsl;                 // value slices per slice group (slice_group())
     int32_t gate_split;          // gated output through o_scratch + part_scratch and an epilogue
     int32_t whole_rows;          // plain output from whole-row inter-chunk workgroups
+    // Chunk-range scan (few (sequence, head) pairs, long sequences): each
+    // sequence's chunks are cut into ranges of range_len chunks (at least one
+    // range per sequence, empty or not); a range's map S_end = A S_start + B
+    // is formed first, the ranges' start states are then scanned, and the
+    // whole-row pass runs every range from its own start state.
+    int32_t range_len;           // chunks per range, 0: no ranges
+    int32_t ranges_per_seq;      // fixed-length input: max(1, ceil(chunks_per_seq / range_len))
+    int32_t max_ranges;          // ranges of the call at most (the range kernels' grid)
+    const int32_t* range_off;    // packed input: [N + 1] first range of each sequence
+    float* range_ab;             // [ranges, H, dk, dk + dv] fp32: A (dk columns), then B (dv columns)
+    float* range_start;          // [ranges, H, dk, dv] fp32: state at the start of each range (first unused)
     float* o_scratch;            // [B*T*H, dv] un-normalised outputs (split gate)
     float* part_scratch;         // [B*T*H, dv/16] per-slice sums of squares (split gate)
 };
@@ -64,6 +75,14 @@ struct DecodeArgs {
 };
 
 hipError_t launch_chunk_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t* chunk_off, hipStream_t s);
+// Also the first range of each packed sequence (range_off [n + 1]) for ranges of L chunks.
+hipError_t launch_chunk_range_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t L, int32_t* chunk_off,
+                                      int32_t* range_off, hipStream_t s);
+// Chunks per range of the chunk-range scan for this call shape, or 0 when the
+// scan does not run (it needs dk == dv in {64, 128}, bf16 inputs, 64-token
+// chunks, fewer (sequence, head) pairs than CUs and at least three ranges per
+// sequence on average).
+int range_length(int DK, int DV, int C, bool bf16, int64_t units, int64_t chunks_per_unit);
 // Clears the range status word (calls without tokens launch no intra-chunk kernel).
 hipError_t launch_clear_status(int32_t* status, hipStream_t s);
 // C is the requested chunk size; the chunk the kernels use is

@@ -98,36 +98,51 @@ __device__ __forceinline__ float alpha_at(const PrefillArgs& a, int64_t tok, int
 }
 
 // ---------------------------------------------------------------------------
-// K0: exclusive prefix of ceil(len_n / C) over the packed sequences.
+// K0: exclusive prefix of ceil(len_n / C) over the packed sequences, and, for
+// the chunk-range scan (range_off non-null), of max(1, ceil(chunks_n / L)).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void kda_chunk_offsets(const int32_t* __restrict__ cu, int32_t n_seqs,
-                                                         int32_t C, int32_t* __restrict__ chunk_off) {
-    __shared__ int32_t part[256];
-    __shared__ int32_t carry;
+                                                         int32_t C, int32_t L, int32_t* __restrict__ chunk_off,
+                                                         int32_t* __restrict__ range_off) {
+    __shared__ int32_t part[2][256];
+    __shared__ int32_t carry[2];
     const int tid = threadIdx.x;
-    if (tid == 0) carry = 0;
+    if (tid < 2) carry[tid] = 0;
     __syncthreads();
     for (int base = 0; base < n_seqs; base += 256) {
         const int n = base + tid;
-        int32_t c = 0;
+        int32_t c = 0, rr = 0;
         if (n < n_seqs) {
             const int32_t len = cu[n + 1] - cu[n];
             c = len > 0 ? (len + C - 1) / C : 0;
+            rr = range_off ? max(1, (c + L - 1) / L) : 0;
         }
-        part[tid] = c;
+        part[0][tid] = c;
+        part[1][tid] = rr;
         __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
-            const int32_t add = tid >= off ? part[tid - off] : 0;
+        for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scans
+            const int32_t add0 = tid >= off ? part[0][tid - off] : 0;
+            const int32_t add1 = tid >= off ? part[1][tid - off] : 0;
             __syncthreads();
-            part[tid] += add;
+            part[0][tid] += add0;
+            part[1][tid] += add1;
             __syncthreads();
         }
-        if (n < n_seqs) chunk_off[n] = carry + part[tid] - c;
+        if (n < n_seqs) {
+            chunk_off[n] = carry[0] + part[0][tid] - c;
+            if (range_off) range_off[n] = carry[1] + part[1][tid] - rr;
+        }
         __syncthreads();
-        if (tid == 255) carry += part[255];
+        if (tid == 255) {
+            carry[0] += part[0][255];
+            carry[1] += part[1][255];
+        }
         __syncthreads();
     }
-    if (tid == 0) chunk_off[n_seqs] = carry;
+    if (tid == 0) {
+        chunk_off[n_seqs] = carry[0];
+        if (range_off) range_off[n_seqs] = carry[1];
+    }
 }
 
 // Where chunk x of the (flattened) chunk list lives.
@@ -155,6 +170,45 @@ __device__ __forceinline__ bool locate_chunk(const PrefillArgs& a, int C, int x,
         pos.tok0 = (int64_t)n * a.T + (int64_t)j * C;
         pos.valid = (int)min((int64_t)C, a.T - (int64_t)j * C);
     }
+    return true;
+}
+
+// Where range x of the (flattened) range list lives: sequence n, its range r of
+// nr, and the chunk window [c0, c1) inside the sequence's chunks starting at
+// c_seq (indices of the flattened chunk list).
+struct RangePos {
+    int n, r, nr;
+    int c_seq, c0, c1;
+};
+
+__device__ __forceinline__ bool locate_range(const PrefillArgs& a, int x, RangePos& rp) {
+    const int L = a.range_len;
+    int cb, ce;
+    if (a.cu_seqlens) {
+        const int32_t* off = a.range_off;
+        if (x >= off[a.N]) return false;
+        int lo = 0, hi = a.N;  // off[lo] <= x < off[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (off[mid] <= x) lo = mid; else hi = mid;
+        }
+        rp.n = lo;
+        rp.r = x - off[lo];
+        rp.nr = off[lo + 1] - off[lo];
+        cb = a.chunk_off[lo];
+        ce = a.chunk_off[lo + 1];
+    } else {
+        const int R = a.ranges_per_seq;
+        if (x >= a.N * R) return false;
+        rp.n = x / R;
+        rp.r = x % R;
+        rp.nr = R;
+        cb = rp.n * a.chunks_per_seq;
+        ce = cb + a.chunks_per_seq;
+    }
+    rp.c_seq = cb;
+    rp.c0 = min(cb + rp.r * L, ce);
+    rp.c1 = min(rp.c0 + L, ce);
     return true;
 }
 
@@ -1085,9 +1139,19 @@ void kda_inter_kernel(const PrefillArgs a) {
     // blocks are dealt round-robin over the 8 XCDs: keep the slice groups of
     // one (sequence, head) on one XCD so they share its L2
     const int b = blockIdx.x, xcd = b & 7, jx = b >> 3;
-    const int grp = jx % ngroups;
-    const int unit = (jx / ngroups) * 8 + xcd;
-    if (unit >= a.N * a.H) return;  // whole workgroup
+    int grp = jx % ngroups;
+    int unit = (jx / ngroups) * 8 + xcd;
+    // chunk-range scan (whole-row plain calls with range_len > 0): workgroup b
+    // runs range b / H of head b % H
+    RangePos rp{};
+    const bool ranged = kMode == kOutRow && a.range_len > 0;
+    if (ranged) {
+        grp = 0;
+        if (!locate_range(a, b / H, rp)) return;   // whole workgroup
+        unit = rp.n * H + b % H;
+    } else if (unit >= a.N * a.H) {
+        return;  // whole workgroup
+    }
     const int n = unit / H, h = unit % H, seq = n;
 
     int c_begin, c_end;
@@ -1103,6 +1167,13 @@ void kda_inter_kernel(const PrefillArgs a) {
         tok_begin = (int64_t)n * a.T;
         seq_len = a.T;
     }
+    // the chunks this workgroup walks, the state it starts from and whether it
+    // ends the sequence (a range other than the last hands over to the next)
+    const int cw_begin = ranged ? rp.c0 : c_begin, cw_end = ranged ? rp.c1 : c_end;
+    const float* s_init = ranged && rp.r > 0 ? a.range_start + ((int64_t)(b / H) * H + h) * DK * DV
+                          : a.s0 ? a.s0 + (int64_t)unit * DK * DV
+                                 : nullptr;
+    const bool ends_seq = !ranged || rp.r == rp.nr - 1;
 
     if constexpr (X::kOWave) {
         // ---- two compute waves: wave 0 walks the state chain, wave 1 forms the
@@ -1296,7 +1367,7 @@ void kda_inter_kernel(const PrefillArgs a) {
                 dma_to_lds(src, dst, cb.shared, lane, io, kIoWaves);
                 dma_to_lds(src + cb.u + grp * cb.group, dst + X::kShared, cb.group, lane, io, kIoWaves);
             };
-            if (c_begin < c_end) fetch(c_begin, 0);
+            if (cw_begin < cw_end) fetch(cw_begin, 0);
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
             // The ring holds two chunks, so the copy of chunk x + 1 is issued only
             // one chunk ahead and would pay the full HBM latency.  One dword per
@@ -1317,10 +1388,10 @@ void kda_inter_kernel(const PrefillArgs a) {
                             : pl < my_shared + group_lines ? cb.u + grp * cb.group + (pl - my_shared) * 128
                             : 0;
             }
-            for (int x = c_begin; x < c_end; ++x) {
-                if (x + 1 < c_end) fetch(x + 1, (x + 1 - c_begin) & 1);
+            for (int x = cw_begin; x < cw_end; ++x) {
+                if (x + 1 < cw_end) fetch(x + 1, (x + 1 - cw_begin) & 1);
                 asm volatile("" ::: "memory");   // the line loads stay after the copies
-                const char* pblk = a.ws_chunks + ((int64_t)min(x + 1 + kL2Ahead, c_end - 1) * H + h) * cb.bytes;
+                const char* pblk = a.ws_chunks + ((int64_t)min(x + 1 + kL2Ahead, cw_end - 1) * H + h) * cb.bytes;
 #pragma unroll
                 for (int i = 0; i < X::kPfLoads; ++i)
                     __builtin_amdgcn_global_load_lds((gbl_void_t*)(pblk + pf_off[i]), (lds_void_t*)pf_sink, 4, 0, 0);
@@ -1343,7 +1414,7 @@ void kda_inter_kernel(const PrefillArgs a) {
             for (int t = 0; t < NQK; ++t)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[n][t][j] = (a.s0 && n < nsl) ? a.s0[sbase + (int64_t)(16 * t + 4 * g + j) * DV + 16 * (s0 + n) + cl] : 0.f;
+                    acc[n][t][j] = (s_init && n < nsl) ? s_init[(int64_t)(16 * t + 4 * g + j) * DV + 16 * (s0 + n) + cl] : 0.f;
 
         bool fin = true;   // every output this lane formed was finite
         // gated calls: a chunk's outputs wait in registers until every wave's
@@ -1380,11 +1451,11 @@ void kda_inter_kernel(const PrefillArgs a) {
         };
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-        for (int x = c_begin; x < c_end; ++x) {
-            const int jc = x - c_begin;
+        for (int x = cw_begin; x < cw_end; ++x) {
+            const int jc = x - c_begin;   // chunk index inside the sequence
             const int64_t tok0 = tok_begin + (int64_t)jc * C;
             const int valid = (int)min((int64_t)C, seq_len - (int64_t)jc * C);
-            const char* buf = ring + (jc & 1) * X::kBuf;
+            const char* buf = ring + ((x - cw_begin) & 1) * X::kBuf;
             const char* Wl = buf + cb.w;
             const char* Ql = buf + cb.q;
             const char* Kl = buf + cb.kb;
@@ -1491,7 +1562,7 @@ void kda_inter_kernel(const PrefillArgs a) {
 #pragma unroll
                 for (int t = 0; t < NQK; ++t) fin &= finite4(acc[n][t]);
         if (!fin) *a.status = 1;
-        if (a.s_final) {
+        if (a.s_final && ends_seq) {
 #pragma unroll
             for (int n = 0; n < SPW; ++n)
                 if (n < nsl)
@@ -1502,6 +1573,244 @@ void kda_inter_kernel(const PrefillArgs a) {
                         a.s_final[sbase + (int64_t)(16 * t + 4 * g + j) * DV + 16 * (s0 + n) + cl] = acc[n][t][j];
         }
     }   // one compute wave per slice group
+}
+
+// ---------------------------------------------------------------------------
+// Chunk-range scan.  Over a range of chunks the chain is affine in its start
+// state: S_end = A S_start + B, with A = prod_c (diag(gamma_c) - Kbar_c^T W_c)
+// (dk x dk) and B the state reached from zero.  Both are the chain itself run
+// on the (dk + dv)-column state [I | 0]: for A's columns U = -W X, for B's
+// U = U~ - W X; then X <- diag(gamma) X + Kbar^T U.  With the maps of every
+// range but each sequence's last, the ranges' start states follow from a
+// short scan, and every range's outputs can be formed at once.
+// ---------------------------------------------------------------------------
+template <int DK, int C, typename T> struct RangeSum {
+    static constexpr int kSlices = 2 * DK / 16;   // A's DK/16 column slices, then B's (dv == dk)
+    static constexpr int SPW = 2;                 // slices per compute wave
+    static constexpr int kCompute = kSlices / SPW;
+    static constexpr int kIo = 4;
+    static constexpr int kThreads = 64 * (kCompute + kIo);
+    static constexpr int64_t kSzW = Frag<T>::elems(C, DK) * (int64_t)sizeof(T);
+    static constexpr int64_t kSzK = Frag<T>::elems(DK, C) * (int64_t)sizeof(T);
+    static constexpr int64_t kSzG = round_kib(DK * 4);
+    static constexpr int64_t kSzU = round_kib((int64_t)(DK / 16) * C * 16 * sizeof(T));   // the row's U~ slices
+    // ring slot: [W | Kbar^T | gamma_C | U~]; Q~ and P are not needed here
+    static constexpr int64_t kSlot = kSzW + kSzK + kSzG + kSzU;
+    static constexpr int64_t kLds = 2 * kSlot;
+    static constexpr int kPfLoads = (int)((kSlot / 128 + kIo * 64 - 1) / (kIo * 64));
+    static constexpr bool kFits = kLds <= 163840 && kSzW % 1024 == 0 && kSzK % 1024 == 0;
+};
+
+template <int DK, int C, typename In>
+__global__ __launch_bounds__((RangeSum<DK, C, typename OperandOf<In>::type>::kThreads))
+void kda_range_kernel(const PrefillArgs a) {
+    using T = typename OperandOf<In>::type;
+    using Q = quad_t<T>;
+    using X = RangeSum<DK, C, T>;
+    static_assert(X::kFits, "LDS ring of the range kernel exceeds one workgroup");
+    constexpr int NB = C / 16, NQK = DK / 16, SPW = X::SPW;
+    __shared__ __attribute__((aligned(1024))) char ring[X::kLds];
+    __shared__ __attribute__((aligned(256))) int pf_sink[64];   // L2 prefetch target (never read)
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, cl = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = a.H, DV = a.DV;
+    const ChunkBlock<T> cb(DK, C, DV, a.gsl);
+    const int xr = blockIdx.x / H, h = blockIdx.x % H;
+    RangePos rp;
+    // the last range of a sequence needs no map (nothing follows it)
+    if (!locate_range(a, xr, rp) || rp.r == rp.nr - 1) return;   // whole workgroup
+    const int cw_begin = rp.c0, cw_end = rp.c1;   // a range before the last is full: L chunks
+
+    if (wave >= X::kCompute) {
+        // ---- I/O waves: W, Kbar^T, gamma_C and the row's U~ of chunk x + 1 ----
+        const int io = wave - X::kCompute;
+        auto fetch = [&](int x, int slot) {
+            const char* src = a.ws_chunks + ((int64_t)x * H + h) * cb.bytes;
+            char* dst = ring + slot * X::kSlot;
+            int first = io;   // 1 KiB units dealt round-robin over the I/O waves across segments
+            auto seg = [&](const char* sp, char* dp, int64_t bytes) {
+                dma_to_lds(sp, dp, bytes, lane, first, X::kIo);
+                first = ((first - (int)(bytes / 1024)) % X::kIo + X::kIo) % X::kIo;
+            };
+            seg(src + cb.w, dst, X::kSzW);
+            seg(src + cb.kb, dst + X::kSzW, X::kSzK);
+            seg(src + cb.gam, dst + X::kSzW + X::kSzK, X::kSzG);
+            seg(src + cb.u, dst + X::kSzW + X::kSzK + X::kSzG, X::kSzU);
+        };
+        // one dword of each 128-byte line of the slot's four regions, kL2Ahead
+        // chunks past the copy, into an LDS sink: brings them into L2 early
+        int64_t pf_off[X::kPfLoads];
+#pragma unroll
+        for (int i = 0; i < X::kPfLoads; ++i) {
+            const int64_t pl = ((int64_t)i * X::kIo + io) * 64 + lane;
+            const int64_t lw = X::kSzW / 128, lk = X::kSzK / 128, lg = X::kSzG / 128, lu = X::kSzU / 128;
+            pf_off[i] = pl < lw ? cb.w + pl * 128
+                        : pl < lw + lk ? cb.kb + (pl - lw) * 128
+                        : pl < lw + lk + lg ? cb.gam + (pl - lw - lk) * 128
+                        : pl < lw + lk + lg + lu ? cb.u + (pl - lw - lk - lg) * 128
+                        : cb.w;
+        }
+        if (cw_begin < cw_end) fetch(cw_begin, 0);
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        for (int x = cw_begin; x < cw_end; ++x) {
+            if (x + 1 < cw_end) fetch(x + 1, (x + 1 - cw_begin) & 1);
+            asm volatile("" ::: "memory");   // the line loads stay after the copies
+            const char* pblk = a.ws_chunks + ((int64_t)min(x + 1 + kL2Ahead, cw_end - 1) * H + h) * cb.bytes;
+#pragma unroll
+            for (int i = 0; i < X::kPfLoads; ++i)
+                __builtin_amdgcn_global_load_lds((gbl_void_t*)(pblk + pf_off[i]), (lds_void_t*)pf_sink, 4, 0, 0);
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(X::kPfLoads) : "memory");
+        }
+        return;
+    }
+
+    // ---- compute waves: slices s0, s0 + 1 of [A | B] (16 columns each) ---------
+    const int s0 = wave * SPW;
+    const bool partB = s0 >= NQK;   // wave-uniform: a wave's slices are all of A or all of B
+    // acc[n][t][j] = X[16t + 4g + j][16 (s0 + n) + cl]; A starts as the identity, B as zero
+    f32x4 acc[SPW][NQK];
+#pragma unroll
+    for (int n = 0; n < SPW; ++n)
+#pragma unroll
+        for (int t = 0; t < NQK; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[n][t][j] = (!partB && 16 * t + 4 * g + j == 16 * (s0 + n) + cl) ? 1.f : 0.f;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int x = cw_begin; x < cw_end; ++x) {
+        const char* buf = ring + ((x - cw_begin) & 1) * X::kSlot;
+        const char* Wl = buf;
+        const char* Kl = buf + X::kSzW;
+        const float* gl = reinterpret_cast<const float*>(buf + X::kSzW + X::kSzK);
+        const T* Ul = reinterpret_cast<const T*>(buf + X::kSzW + X::kSzK + X::kSzG);
+        Q sb[SPW][NQK];
+#pragma unroll
+        for (int n = 0; n < SPW; ++n)
+#pragma unroll
+            for (int t = 0; t < NQK; ++t) sb[n][t] = make_quad<T>(acc[n][t]);
+        // U = (U~ for B's columns, 0 for A's) - W X
+        Q ub[SPW][NB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+            Q wq[NQK];
+            load_frag(wq, Wl, tb, lane);
+#pragma unroll
+            for (int n = 0; n < SPW; ++n) {
+                const f32x4 xw = mma_quads(wq, sb[n], zero4());
+                f32x4 ut = zero4();
+                if (partB)
+                    ut = from_quad(*reinterpret_cast<const Q*>(Ul + (s0 + n - NQK) * (cb.slice / sizeof(T)) +
+                                                               (lane * NB + tb) * 4));
+                ub[n][tb] = make_quad<T>(ut - xw);
+            }
+        }
+        // X <- diag(gamma_C) X + Kbar^T U
+#pragma unroll
+        for (int t = 0; t < NQK; ++t) {
+            const f32x4 gv = *reinterpret_cast<const f32x4*>(gl + 16 * t + 4 * g);
+            Q kq[NB];
+            load_frag(kq, Kl, t, lane);
+#pragma unroll
+            for (int n = 0; n < SPW; ++n) acc[n][t] = mma_quads(kq, ub[n], acc[n][t] * gv);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    // the map, row-major [dk][dk + dv]: A in columns [0, dk), B in [dk, dk + dv)
+    float* ab = a.range_ab + ((int64_t)xr * H + h) * DK * (DK + DV);
+    bool fin = true;
+#pragma unroll
+    for (int n = 0; n < SPW; ++n)
+#pragma unroll
+        for (int t = 0; t < NQK; ++t) {
+            fin &= finite4(acc[n][t]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ab[(int64_t)(16 * t + 4 * g + j) * (DK + DV) + 16 * (s0 + n) + cl] = acc[n][t][j];
+        }
+    if (!fin) *a.status = 1;
+}
+
+// Start states of the ranges of one (sequence, head), 16 value columns per
+// workgroup: S_{r+1} = A_r S_r + B_r in fp32 from S_0 = the initial state,
+// written for ranges 1 .. nr - 1.  The products run on fp32 MFMA
+// (16x16x4): each of the four waves forms dk/64 16-row tiles of S_{r+1}.
+// The contraction order is permuted so that a lane's A operand is a run of
+// consecutive columns: in K-step 4m + u, lane (g, c) contracts column
+// 16m + 4g + u, so it reads its row of A_r as float4 loads.  Only S is
+// serial, so the operands of step r + 1 are loaded while step r runs.
+template <int DK>
+__global__ __launch_bounds__(256) void kda_range_scan_kernel(const PrefillArgs a) {
+    constexpr int DV = DK, NSL = DV / 16, KQ = DK / 16, TW = DK / 64, RS = DK + DV;
+    // blocks are dealt round-robin over the 8 XCDs: the slices of one
+    // (sequence, head) share its range maps, so they go to one XCD
+    const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+    const int unit = (jx / NSL) * 8 + xcd, sl = jx % NSL;
+    const int H = a.H;
+    if (unit >= a.N * H) return;
+    const int n = unit / H, h = unit % H;
+    int x0, nr;
+    if (a.cu_seqlens) {
+        x0 = a.range_off[n];
+        nr = a.range_off[n + 1] - x0;
+    } else {
+        x0 = n * a.ranges_per_seq;
+        nr = a.ranges_per_seq;
+    }
+    if (nr <= 1) return;   // uniform over the workgroup
+    __shared__ float sS[DK][17];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, cl = lane & 15;
+    for (int e = tid; e < DK * 16; e += 256) {
+        const int c = e >> 4, j = e & 15;
+        sS[c][j] = a.s0 ? a.s0[((int64_t)unit * DK + c) * DV + 16 * sl + j] : 0.f;
+    }
+    f32x4 aN[TW][KQ], cN[TW];   // operands of the next step: A rows, B tile
+    auto fetch = [&](int r) {
+        const float* ab = a.range_ab + ((int64_t)(x0 + r) * H + h) * DK * RS;
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+            const int t = wave * TW + i;
+#pragma unroll
+            for (int m = 0; m < KQ; ++m) aN[i][m] = *(const f32x4*)(ab + (int64_t)(16 * t + cl) * RS + 16 * m + 4 * g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cN[i][j] = ab[(int64_t)(16 * t + 4 * g + j) * RS + DK + 16 * sl + cl];
+        }
+    };
+    fetch(0);
+    __syncthreads();
+    bool fin = true;
+    for (int r = 0; r + 1 < nr; ++r) {
+        f32x4 aC[TW][KQ], acc[TW];
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+            acc[i] = cN[i];
+#pragma unroll
+            for (int m = 0; m < KQ; ++m) aC[i][m] = aN[i][m];
+        }
+        if (r + 2 < nr) fetch(r + 1);
+#pragma unroll
+        for (int m = 0; m < KQ; ++m)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float b = sS[16 * m + 4 * g + u][cl];
+#pragma unroll
+                for (int i = 0; i < TW; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(aC[i][m][u], b, acc[i], 0, 0, 0);
+            }
+        __syncthreads();   // every wave has read S_r
+        float* out = a.range_start + ((int64_t)(x0 + r + 1) * H + h) * DK * DV;
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+            const int t = wave * TW + i;
+            fin &= finite4(acc[i]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = 16 * t + 4 * g + j;
+                sS[c][cl] = acc[i][j];
+                out[(int64_t)c * DV + 16 * sl + cl] = acc[i][j];
+            }
+        }
+        __syncthreads();
+    }
+    if (!fin) *a.status = 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -1533,6 +1842,22 @@ static hipError_t launch_phase_t(const PrefillArgs& a, int max_chunks, bool intr
                 constexpr int spw = Inter<DK, C, typename OperandOf<In>::type, true>::SPW;
                 hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutGate>), dim3(blocks),
                                    dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
+            } else if (a.whole_rows && a.range_len > 0) {
+                // chunk-range scan: range maps, the ranges' start states, then
+                // every range's whole-row pass
+                using T = typename OperandOf<In>::type;
+                if constexpr (C == 64 && (DK == 64 || DK == 128) && sizeof(T) == 2 && RangeSum<DK, C, T>::kFits) {
+                    constexpr int spw = Inter<DK, C, T, true>::SPW;
+                    const dim3 grid((unsigned)a.max_ranges * (unsigned)a.H);
+                    hipLaunchKernelGGL((kda_range_kernel<DK, C, In>), grid, dim3(RangeSum<DK, C, T>::kThreads), 0,
+                                       stream, a);
+                    hipLaunchKernelGGL((kda_range_scan_kernel<DK>), dim3((unsigned)(((units + 7) / 8) * 8 * (a.DV / 16))), dim3(256),
+                                       0, stream, a);
+                    hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutRow>), grid,
+                                       dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
+                } else {
+                    return hipErrorInvalidValue;   // range_length() never selects this
+                }
             } else if (a.whole_rows) {
                 constexpr int spw = Inter<DK, C, typename OperandOf<In>::type, true>::SPW;
                 hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutRow>), dim3(blocks),
@@ -1599,7 +1924,13 @@ hipError_t launch_clear_status(int32_t* status, hipStream_t s) {
 }
 
 hipError_t launch_chunk_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t* chunk_off, hipStream_t s) {
-    hipLaunchKernelGGL(kda_chunk_offsets, dim3(1), dim3(256), 0, s, cu, n, C, chunk_off);
+    hipLaunchKernelGGL(kda_chunk_offsets, dim3(1), dim3(256), 0, s, cu, n, C, 1, chunk_off, (int32_t*)nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_range_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t L, int32_t* chunk_off,
+                                      int32_t* range_off, hipStream_t s) {
+    hipLaunchKernelGGL(kda_chunk_offsets, dim3(1), dim3(256), 0, s, cu, n, C, L, chunk_off, range_off);
     return hipGetLastError();
 }
 
@@ -1683,16 +2014,31 @@ hipError_t launch_gate_epilogue(const PrefillArgs& a, int64_t rows, bool bf16, h
 constexpr int kMaxDevices = 64;
 static std::atomic<int> g_cu_count[kMaxDevices];
 
-bool whole_rows(int64_t units) {
+static int cu_count() {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return units >= 256;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
     int cus = g_cu_count[dev].load(std::memory_order_relaxed);
     if (cus == 0) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
         g_cu_count[dev].store(cus, std::memory_order_relaxed);
     }
-    return units >= cus;
+    return cus;
+}
+
+bool whole_rows(int64_t units) { return units >= cu_count(); }
+
+int range_length(int DK, int DV, int C, bool bf16, int64_t units, int64_t chunks_per_unit) {
+    if (!bf16 || DK != DV || (DK != 64 && DK != 128) || C != 64) return 0;
+    const int64_t cus = cu_count();
+    if (units <= 0 || units >= cus) return 0;
+    // about one range per compute unit, and no range shorter than 16 chunks
+    int64_t L = (chunks_per_unit * units + cus - 1) / cus;
+    if (L < 16) L = 16;
+    // with fewer than three ranges per sequence the maps would cost as much as
+    // the walk they shorten
+    if (chunks_per_unit < 3 * L || L > (1 << 24)) return 0;
+    return (int)L;
 }
 
 int slice_group(int DV, bool whole) { return whole ? DV / 16 : group_slices(DV); }

@@ -9,9 +9,10 @@ import os
 import re
 
 import pytest
+import torch
 
 import linear_attention_sequence_gated_amd as kda
-from linear_attention_sequence_gated_amd._lib import ChunkParams
+from linear_attention_sequence_gated_amd._lib import ChunkParams, ChunkPlan
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
@@ -79,6 +80,39 @@ def test_workspace_size(lib):
     assert _ws(lib, _params(qkv_dtype=0, chunk_size=64)) == _ws(lib, _params(qkv_dtype=0, chunk_size=32))
     assert _ws(lib, _params(num_heads=0))[0] == INVALID
     assert lib.kda_chunk_fwd_workspace_size(None, None) == INVALID
+
+
+def _plan(lib, p, packed=0):
+    out = ChunkPlan()
+    st = lib.kda_chunk_fwd_plan(ctypes.byref(p), packed, ctypes.byref(out))
+    return st, (out.chunk_size, out.whole_rows, out.range_chunks, out.max_ranges)
+
+
+def test_plan(lib):
+    """Chunk ranges for bf16 dk = dv in {64, 128} with fewer (sequence, head)
+    pairs than compute units (256 assumed without a device) and at least three
+    ranges of max(16, ceil(chunks * pairs / 256)) chunks per sequence."""
+    if torch.cuda.device_count() > 0 and torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("expected values assume 256 compute units")
+    # 32 heads of 1024 chunks: ranges of 1024 * 32 / 256 = 128 chunks, 8 per sequence
+    assert _plan(lib, _params(seqlen=65536, num_heads=32)) == (OK, (64, 1, 128, 8))
+    # 48 chunks make three 16-chunk ranges; 47 do not
+    assert _plan(lib, _params(seqlen=3072, num_heads=4)) == (OK, (64, 1, 16, 3))
+    assert _plan(lib, _params(seqlen=3008, num_heads=4)) == (OK, (64, 0, 0, 0))
+    assert _plan(lib, _params(batch=2, num_seqs=2, seqlen=5000, num_heads=2, head_dim_k=64,
+                              head_dim_v=64)) == (OK, (64, 1, 16, 10))
+    # as many pairs as compute units: whole rows, no ranges
+    assert _plan(lib, _params(seqlen=65536, num_heads=256)) == (OK, (64, 1, 0, 0))
+    # fp32 operands (32-token chunks at dk = 128), dk != dv and 32-token chunks take no ranges
+    assert _plan(lib, _params(seqlen=65536, qkv_dtype=0, o_dtype=0)) == (OK, (32, 0, 0, 0))
+    assert _plan(lib, _params(seqlen=65536, head_dim_v=64)) == (OK, (64, 0, 0, 0))
+    assert _plan(lib, _params(seqlen=65536, chunk_size=32)) == (OK, (32, 0, 0, 0))
+    # packed, 20073 tokens in 5 sequences: at most 313 + 5 + 1 chunks per head,
+    # 63 on average; ranges of 16, at most 319 / 16 + 5 + 1 of them
+    assert _plan(lib, _params(num_seqs=5, seqlen=20073), packed=1) == (OK, (64, 1, 16, 25))
+    assert _plan(lib, _params(batch=2, num_seqs=2, seqlen=20073), packed=1)[0] == INVALID
+    assert _plan(lib, _params(head_dim_k=96))[0] == UNSUPPORTED
+    assert lib.kda_chunk_fwd_plan(ctypes.byref(_params()), 0, None) == INVALID
 
 
 def _fwd(lib, p, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s0=None, cu=None, o=FAKE, sf=None,

@@ -750,3 +750,60 @@ def test_range_status_reads_clear_after_an_empty_call():
                        workspace=pre.workspace)
     pre0.run()
     assert pre0.status() == 0
+
+
+# --- chunk-range scan (few (sequence, head) pairs, long sequences) -----------------
+# With fewer pairs than CUs and at least three 16-chunk ranges per sequence the
+# inter-chunk pass forms each range's map, scans the ranges' start states and
+# runs the ranges side by side.
+
+def _ranged(B, T, H, d, lengths=None):
+    cu = None if lengths is None else torch.tensor(np.cumsum([0] + lengths), dtype=torch.int32, device="cuda")
+    Tq = T if lengths is None else sum(lengths)
+    x = torch.empty(B, Tq, H, d, dtype=torch.bfloat16, device="cuda")
+    return kda.chunk_plan(x, x, cu)["range_chunks"] > 0
+
+
+@pytest.mark.parametrize("B,T,H,d,lengths,expect", [
+    (2, 5000, 2, 128, None, True), (1, 4096, 4, 64, None, True), (1, 6200, 3, 128, None, True),
+    (1, 0, 2, 128, [9000, 0, 7000, 1, 3072], True), (1, 65536, 32, 128, None, True),
+    (1, 3072, 4, 128, None, True),       # 48 chunks: three 16-chunk ranges
+    (1, 3008, 4, 128, None, False),      # 47 chunks: fewer than three
+    (1, 8192, 256, 64, None, False),     # as many pairs as CUs
+])
+def test_chunk_range_scan_selection(B, T, H, d, lengths, expect):
+    if H >= 256 and torch.cuda.get_device_properties(0).multi_processor_count > 256:
+        pytest.skip("device has more than 256 CUs")
+    assert _ranged(B, T, H, d, lengths) == expect
+
+
+@pytest.mark.parametrize("B,T,H,d", [(2, 5000, 2, 128), (1, 4096, 4, 64), (1, 6200, 3, 128)])
+def test_chunk_range_scan_fixed_length(B, T, H, d):
+    inp = workloads.make_inputs(B, T, H, d, d, torch.bfloat16, s0_std=0.02, seed=1100 + T + d)
+    check(inp, 64, TOL[torch.bfloat16], label=f"ranges B{B} T{T} H{H} d{d}")
+    check_bf16_output(inp, 64)
+
+
+def test_chunk_range_scan_packed_with_empty_and_tiny_sequences():
+    lens = [9000, 0, 7000, 1, 3072]
+    inp = workloads.make_inputs(1, 0, 2, 128, 128, torch.bfloat16, s0_std=0.02, seed=1110, lengths=lens)
+    check(inp, 64, TOL[torch.bfloat16], label=f"ranges packed {lens}")
+
+
+def test_chunk_range_scan_checkpoints_cross_ranges():
+    # 1024-token checkpoints land inside and at the ends of the 16-chunk ranges
+    inp = workloads.make_inputs(1, 0, 2, 128, 128, torch.bfloat16, s0_std=0.02, seed=1111, lengths=[9000, 4100])
+    _ckpt_check(inp, 64, 1024, 9, TOL[torch.bfloat16], "ranges packed [9000, 4100]")
+
+
+def test_chunk_range_scan_resume_equals_one_pass():
+    inp = workloads.make_inputs(1, 8192, 2, 128, 128, torch.bfloat16, s0_std=0.02, seed=1112)
+    o_full, S_full = gpu_prefill(inp, 64)
+    cut = 5000
+    first = {k: (v[:, :cut].contiguous() if k in ("q", "k", "v", "alpha", "beta") else v) for k, v in inp.items()}
+    o1, S1 = gpu_prefill(first, 64)
+    second = {k: (v[:, cut:].contiguous() if k in ("q", "k", "v", "alpha", "beta") else v) for k, v in inp.items()}
+    second["S0"] = torch.from_numpy(S1)
+    o2, S2 = gpu_prefill(second, 64)
+    assert rel_err(np.concatenate([o1, o2], axis=1), o_full) < 2e-2
+    assert rel_err(S2, S_full) < 2e-2
