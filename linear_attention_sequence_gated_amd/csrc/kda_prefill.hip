@@ -792,17 +792,26 @@ void kda_intra_kernel(const PrefillArgs a) {
                         pres[pi][j] *= dm;
                     }
                 }
+                // the accumulator is P's fragment (row tile R, quad Ib) as the
+                // workspace stores it: it goes out from here
                 if (pI[pi] < pR[pi]) {
                     *reinterpret_cast<f32x4*>(MX + r * LD_F + i0) = br * mres[pi];
-                    *reinterpret_cast<f32x4*>(Pm + r * LD_F + i0) = pres[pi];
                 } else {   // diagonal tile: keep the strictly lower (M) / lower (P) part
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         if (i0 + j < r) MX[r * LD_F + i0 + j] = br * mres[pi][j];
-                        Pm[r * LD_F + i0 + j] = (i0 + j <= r) ? pres[pi][j] : 0.f;
+                        if (i0 + j > r) pres[pi][j] = 0.f;
                     }
                 }
+                *reinterpret_cast<Q*>(Pf + Frag<T>::off(pR[pi], pI[pi], lane, C)) = make_quad<T>(pres[pi]);
             }
+        }
+        // P's tiles above the diagonal are zero
+        for (int q = wave; q < I::NOFF; q += 4) {
+            int R = 0;
+            while ((R + 1) * (R + 2) / 2 <= q) ++R;   // q-th pair (R' < Ib') above the diagonal, by columns
+            const int Rt = q - R * (R + 1) / 2, Ib = R + 1;
+            *reinterpret_cast<Q*>(Pf + Frag<T>::off(Rt, Ib, lane, C)) = make_quad<T>(zero4());
         }
     } else {
         // exact pairwise path: decay products taken in linear space
@@ -836,6 +845,15 @@ void kda_intra_kernel(const PrefillArgs a) {
             }
         }
     }
+    // Tm's tiles above the diagonal are zero (the region is free of the Gram
+    // operands from here on); the solve writes the others
+    for (int e = tid; e < I::NOFF * 64; e += I::kThreads) {
+        const int q = e >> 6, rr = (e >> 2) & 15, qq = e & 3;
+        int R = 0;
+        while ((R + 1) * (R + 2) / 2 <= q) ++R;   // q-th tile (Rt < It) above the diagonal, by columns
+        const int Rt = q - R * (R + 1) / 2, It = R + 1;
+        store_q<T>(Tb + (16 * Rt + rr) * LD_CT + 16 * It + 4 * qq, zero4());
+    }
     lds_barrier();
 
     load_v();
@@ -859,10 +877,12 @@ void kda_intra_kernel(const PrefillArgs a) {
             }
             if (r > ci) xv[r] = -s;
         }
+        const float bc = sbeta[b0 + ci];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             XD[R * 256 + r * 16 + ci] = xv[r];                        // X_RR[r][ci], row-major
             if (r > ci) MX[(b0 + ci) * LD_F + b0 + r] = xv[r];       // X[b0+r][b0+ci], transposed
+            Tb[(b0 + r) * LD_CT + b0 + ci] = (T)(xv[r] * bc);         // Tm = X diag(beta)
         }
     }
     lds_barrier();
@@ -893,25 +913,16 @@ void kda_intra_kernel(const PrefillArgs a) {
             const f32x4 xr = *reinterpret_cast<const f32x4*>(XD + R * 256 + cl * 16 + 4 * g);  // X_RR[rr=cl][4g..]
             const f32x4 z = mma_step(yt, xr, zero4());
             // lane holds Z^T[ii = 4g + j][rr = cl]; X_RIb^T[ii][rr] = -Z^T[ii][rr]
+            f32x4 t4;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) MX[(16 * Ib + 4 * g + jj) * LD_F + 16 * R + cl] = -z[jj];
+            for (int jj = 0; jj < 4; ++jj) {
+                MX[(16 * Ib + 4 * g + jj) * LD_F + 16 * R + cl] = -z[jj];
+                t4[jj] = -z[jj] * sbeta[16 * Ib + 4 * g + jj];
+            }
+            store_q<T>(Tb + (16 * R + cl) * LD_CT + 16 * Ib + 4 * g, t4);   // Tm row 16R + cl
         }
         lds_barrier();
     }
-    // Tm = X diag(beta), lower triangle, in the operand type; lanes run over
-    // rows r so that reading X^T (stored in MX's upper part) is conflict-free
-    for (int e = tid; e < C * C / 4; e += I::kThreads) {
-        const int r = e % C, i0 = 4 * (e / C);
-        float t4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = i0 + j;
-            const float xv = i == r ? 1.f : (i < r ? MX[i * LD_F + r] : 0.f);
-            t4[j] = xv * sbeta[i];
-        }
-        store_q<T>(Tb + r * LD_CT + i0, f32x4{t4[0], t4[1], t4[2], t4[3]});
-    }
-    lds_barrier();
 
     // ---- phase 4: value tile, P fragments, W = Tm Ktilde, Utilde = Tm V ------
     if (pv) {
@@ -928,7 +939,9 @@ void kda_intra_kernel(const PrefillArgs a) {
         for (int e = 0; e < 8; ++e)
             store_q<T>(VT + (8 * cgv + e) * LD_CT + 4 * sgv, f32x4{vr[0][e], vr[1][e], vr[2][e], vr[3][e]});
     }
-    if constexpr (sizeof(T) == 2 && NB % 2 == 0) {   // both quads of a 16-byte slot per thread
+    if (kSureFast || fast) {
+        // P went out from the Gram accumulators
+    } else if constexpr (sizeof(T) == 2 && NB % 2 == 0) {   // both quads of a 16-byte slot per thread
         for (int e = tid; e < NB * (NB / 2) * 64; e += I::kThreads) {
             const int ct = e / (NB / 2 * 64), ut = 2 * ((e / 64) % (NB / 2)), ln = e & 63;
             const int r = 16 * ct + (ln & 15), i0 = 16 * ut + 4 * (ln >> 4);
