@@ -60,9 +60,11 @@ KERNEL_SOURCES = {
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {  # kernel: (sources, sha256[:16] of the sources, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "kda_intra_kernel": ("prefill", "91efdf7be86212ad", 1343686.0, 2376222.0),
-    "kda_inter_kernel": ("prefill", "91efdf7be86212ad", 1196130.0, 526336.0),
-    "kda_decode_kernel": ("decode", "8169c036a2227051", 267576.0, 526420.0),
+    "kda_intra_kernel": ("prefill", "9e992431bef40ffc", 1343688.4, 2377917.4),
+    "kda_range_kernel": ("prefill", "9e992431bef40ffc", 702802.6, 29917.1),
+    "kda_range_scan_kernel": ("prefill", "9e992431bef40ffc", 14374.2, 14336.0),
+    "kda_inter_kernel": ("prefill", "9e992431bef40ffc", 1204759.2, 526416.5),
+    "kda_decode_kernel": ("decode", "f676fbf479d26200", 267575.9, 526418.7),
 }
 
 
@@ -77,6 +79,8 @@ def source_sha(which):
 
 def traffic(kernel):
     """Measured HBM bytes per launch, or None if the kernel changed since."""
+    if kernel not in TRAFFIC:
+        return None
     which, sha, fetch_kib, write_kib = TRAFFIC[kernel]
     if source_sha(which) != sha:
         return None
@@ -193,10 +197,17 @@ def main():
     alg = algorithmic(w.dk, w.dv, w.chunk)
     intra_roof = roof("hbm", th * alg["intra_bytes_per_token_head"], intra_ms / 1e3, "GB/s",
                       "kda_intra_kernel", traffic("kda_intra_kernel"))
+    # the inter-chunk pass is one kernel, or three when the call cuts its
+    # sequences into chunk ranges (range maps, start-state scan, ranged walk)
+    plan = kda.chunk_plan(d["q"], d["v"], d["cu_seqlens"], chunk_size=w.chunk)
+    inter_kernels = (["kda_range_kernel", "kda_range_scan_kernel", "kda_inter_kernel"] if plan["range_chunks"] > 0
+                     else ["kda_inter_kernel"])
+    t_parts = [traffic(k) for k in inter_kernels]
+    t_out = None if None in t_parts else sum(t_parts)
     inter_roof = roof("mfma", th * alg["inter_flops_per_token_head"], inter_ms / 1e3, "TFLOP/s",
-                      "kda_inter_kernel", traffic("kda_inter_kernel"))
+                      " + ".join(inter_kernels), t_out)
     step_bytes = th * alg["prefill_bytes_per_token_head"] + w.batch * w.heads * alg["state_bytes_per_seq_head"]
-    t_in, t_out = traffic("kda_intra_kernel"), traffic("kda_inter_kernel")
+    t_in = traffic("kda_intra_kernel")
     step_roof = roof("hbm", step_bytes, step_ms / 1e3, "GB/s", "kda_chunk_fwd (whole step)",
                      t_in + t_out if t_in is not None and t_out is not None else None)
     # ---- prefill variants (kda_chunk_fwd_ex options), whole call ----------------
@@ -369,7 +380,7 @@ def main():
         cpu = cpu_baseline(host, w.heads)
 
     kernels = {"kda_intra_kernel": dict(intra_roof, ms_per_launch=round(intra_ms, 4)),
-               "kda_inter_kernel": dict(inter_roof, ms_per_launch=round(inter_ms, 4)),
+               "inter_chunk_pass": dict(inter_roof, ms_per_launch=round(inter_ms, 4), plan=plan),
                "kda_decode_kernel": dict(dec_roof, ms_per_launch=round(dec_ms, 4))}
     dominant = intra_roof if intra_ms >= inter_ms else inter_roof
     out = {

@@ -806,13 +806,6 @@ void kda_intra_kernel(const PrefillArgs a) {
                 *reinterpret_cast<Q*>(Pf + Frag<T>::off(pR[pi], pI[pi], lane, C)) = make_quad<T>(pres[pi]);
             }
         }
-        // P's tiles above the diagonal are zero
-        for (int q = wave; q < I::NOFF; q += 4) {
-            int R = 0;
-            while ((R + 1) * (R + 2) / 2 <= q) ++R;   // q-th pair (R' < Ib') above the diagonal, by columns
-            const int Rt = q - R * (R + 1) / 2, Ib = R + 1;
-            *reinterpret_cast<Q*>(Pf + Frag<T>::off(Rt, Ib, lane, C)) = make_quad<T>(zero4());
-        }
     } else {
         // exact pairwise path: decay products taken in linear space
         for (int e = tid; e < 2 * C * LD_F; e += I::kThreads) Pm[e] = 0.f;  // P and MX
@@ -845,15 +838,6 @@ void kda_intra_kernel(const PrefillArgs a) {
             }
         }
     }
-    // Tm's tiles above the diagonal are zero (the region is free of the Gram
-    // operands from here on); the solve writes the others
-    for (int e = tid; e < I::NOFF * 64; e += I::kThreads) {
-        const int q = e >> 6, rr = (e >> 2) & 15, qq = e & 3;
-        int R = 0;
-        while ((R + 1) * (R + 2) / 2 <= q) ++R;   // q-th tile (Rt < It) above the diagonal, by columns
-        const int Rt = q - R * (R + 1) / 2, It = R + 1;
-        store_q<T>(Tb + (16 * Rt + rr) * LD_CT + 16 * It + 4 * qq, zero4());
-    }
     lds_barrier();
 
     load_v();
@@ -883,6 +867,28 @@ void kda_intra_kernel(const PrefillArgs a) {
             XD[R * 256 + r * 16 + ci] = xv[r];                        // X_RR[r][ci], row-major
             if (r > ci) MX[(b0 + ci) * LD_F + b0 + r] = xv[r];       // X[b0+r][b0+ci], transposed
             Tb[(b0 + r) * LD_CT + b0 + ci] = (T)(xv[r] * bc);         // Tm = X diag(beta)
+        }
+    } else if (tid >= 64) {
+        // meanwhile the other waves write the zero tiles above the diagonal: Tm's
+        // (the solve writes the others; the Gram operands are dead) and, on the
+        // fast path, P's in the workspace (the exact path converts all of P later)
+        auto above = [](int q, int& Rt, int& It) {   // q-th tile (Rt < It) above the diagonal, by columns
+            int R = 0;
+            while ((R + 1) * (R + 2) / 2 <= q) ++R;
+            Rt = q - R * (R + 1) / 2;
+            It = R + 1;
+        };
+        for (int e = tid - 64; e < I::NOFF * 64; e += I::kThreads - 64) {
+            int Rt, It;
+            above(e >> 6, Rt, It);
+            store_q<T>(Tb + (16 * Rt + ((e >> 2) & 15)) * LD_CT + 16 * It + 4 * (e & 3), zero4());
+        }
+        if (kSureFast || fast) {
+            for (int q = wave - 1; q < I::NOFF; q += 3) {
+                int Rt, It;
+                above(q, Rt, It);
+                *reinterpret_cast<Q*>(Pf + Frag<T>::off(Rt, It, lane, C)) = make_quad<T>(zero4());
+            }
         }
     }
     lds_barrier();
@@ -1403,6 +1409,14 @@ void kda_inter_kernel(const PrefillArgs a) {
             }
             for (int x = cw_begin; x < cw_end; ++x) {
                 if (x + 1 < cw_end) fetch(x + 1, (x + 1 - cw_begin) & 1);
+                if (ranged) {
+                    // a range's blocks are read by its workgroup alone, and with
+                    // one workgroup per CU the blocks a chunk ahead of all of an
+                    // XCD's ranges exceed its L2: the line loads were evicted
+                    // before use (25 % more HBM reads, no gain in time)
+                    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+                    continue;
+                }
                 asm volatile("" ::: "memory");   // the line loads stay after the copies
                 const char* pblk = a.ws_chunks + ((int64_t)min(x + 1 + kL2Ahead, cw_end - 1) * H + h) * cb.bytes;
 #pragma unroll
