@@ -213,8 +213,11 @@ def main():
     # ---- prefill variants (kda_chunk_fwd_ex options), whole call ----------------
     variants = {}
     if not args.no_variants:
-        def time_call(fn, reps=5):
-            fn()
+        def time_call(fn, reps=5, warm=3):
+            # a fresh call object's first runs touch its new workspace (several
+            # GiB): they are left out
+            for _ in range(warm):
+                fn()
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)

@@ -257,9 +257,11 @@ typedef struct {
 /* Workspace bytes kda_chunk_fwd_ex needs for `params` with `options` (NULL:
  * as kda_chunk_fwd_workspace_size).  A gate adds scratch for un-normalised
  * fp32 outputs and per-slice sums of squares (about (dv + dv/16) * 4 bytes
- * per token and head), used when there are fewer (sequence, head) pairs than
- * compute units: the norm is then finished by a small epilogue kernel instead
- * of inside the inter-chunk kernel. */
+ * per token and head) when the shape takes one-slice inter-chunk workgroups
+ * (kda_chunk_fwd_plan: whole_rows == 0, i.e. fewer (sequence, head) pairs
+ * than compute units and no chunk ranges): the norm is then finished by a
+ * small epilogue kernel.  Otherwise the inter-chunk pass finishes it and no
+ * scratch is quoted. */
 kda_status_t kda_chunk_fwd_ex_workspace_size(const kda_chunk_params_t* params, const kda_chunk_options_t* options,
                                              size_t* bytes);
 

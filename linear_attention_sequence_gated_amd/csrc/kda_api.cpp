@@ -68,8 +68,9 @@ int chunk_of(const kda_chunk_params_t* p) {
 }
 
 // The layout of one call: packed or fixed-length input, with or without the
-// output gate (gated calls keep the one-slice / fused-gate structure and take
-// no chunk ranges).
+// output gate (gated calls take whole rows or chunk ranges where plain calls
+// do, and otherwise one-slice workgroups with the norm finished by the
+// epilogue kernel).
 PrefillPlan plan_prefill(const kda_chunk_params_t* p, bool packed, bool gate) {
     PrefillPlan pl{};
     const int64_t C = chunk_of(p);
@@ -82,7 +83,7 @@ PrefillPlan plan_prefill(const kda_chunk_params_t* p, bool packed, bool gate) {
         pl.max_chunks = (int64_t)p->batch * cps;
     // average chunks per sequence, for the choice of ranges
     const int64_t per_unit = packed ? (p->seqlen / C + p->num_seqs) / p->num_seqs : cps;
-    pl.range_len = gate ? 0 : kda::range_length(p->head_dim_k, p->head_dim_v, (int)C, bf16, units, per_unit);
+    pl.range_len = kda::range_length(p->head_dim_k, p->head_dim_v, (int)C, bf16, units, per_unit);
     pl.whole = kda::whole_rows(units) || pl.range_len > 0;
     pl.block_bytes = kda::chunk_block_bytes(p->head_dim_k, (int)C, p->head_dim_v, bf16,
                                             kda::slice_group(p->head_dim_v, pl.whole));
@@ -171,7 +172,15 @@ kda_status_t kda_chunk_fwd_ex_workspace_size(const kda_chunk_params_t* p, const 
     const kda_status_t st = check_params(p);
     if (st != KDA_OK) return st;
     const bool gate = options && options->gate;
-    *bytes = round_up(base_workspace(p, gate), kWsAlign) + (gate ? gate_scratch_bytes(p) : 0);
+    // gated calls add the epilogue's scratch only where they take one-slice
+    // workgroups (few (sequence, head) pairs and no chunk ranges)
+    size_t most = 0;
+    for (int packed = 0; packed < 2; ++packed) {
+        const PrefillPlan pl = plan_prefill(p, packed, gate);
+        const size_t need = round_up(pl.total, kWsAlign) + (gate && !pl.whole ? gate_scratch_bytes(p) : 0);
+        most = need > most ? need : most;
+    }
+    *bytes = most;
     return KDA_OK;
 }
 

@@ -27,6 +27,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "kda_kernels.h"
 #include "kda_quads.h"
@@ -1055,16 +1056,20 @@ __device__ __forceinline__ void load_frag(f32x4 (&q)[N], const char* base, int r
     for (int u = 0; u < N; ++u) q[u] = *reinterpret_cast<const f32x4*>(p + u * 64 * 4);
 }
 
-// Whole-row workgroups (gated calls, and plain calls with at least as many
-// (sequence, head) pairs as compute units) keep all dv / 16 slices (8 at
-// dv = 128) in one workgroup, two per compute wave, so that a workgroup still
-// has two waves per SIMD (8 waves).  Each chunk's shared operands (W, Q~,
-// Kbar^T, P) are then fetched once for the whole row instead of once per
-// slice: a compute unit takes in about 26 bytes per cycle from L2, and a
-// one-slice workgroup needs ~57 KiB of shared operands per chunk, which caps
-// it near 1 us per chunk whatever the number of workgroups in flight.
-constexpr int kGateSlices = 8;
-constexpr int kGateSlicesPerWave = 2;
+// Whole-row workgroups (plain calls with at least as many (sequence, head)
+// pairs as compute units or with chunk ranges, and gated calls there) keep all
+// dv / 16 slices (8 at dv = 128) in one workgroup.  Each chunk's shared
+// operands (W, Q~, Kbar^T, P) are then fetched once for the whole row instead
+// of once per slice: a compute unit takes in about 26 bytes per cycle from L2,
+// and a one-slice workgroup needs ~57 KiB of shared operands per chunk, which
+// caps it near 1 us per chunk whatever the number of workgroups in flight.
+// Plain workgroups run two slices per compute wave (8 waves: two per SIMD).
+// Gated ones hold a chunk's outputs across the barrier that completes the
+// row norm and run one slice per wave (12 waves): 2.59 against 2.85 ms for
+// the gated long-context call, where the plain call is 0.6 % faster with two.
+constexpr int kRowSlices = 8;
+constexpr int kRowSlicesPerWave = 2;
+constexpr int kGatedSlicesPerWave = 1;
 
 // Waves per workgroup that copy chunk blocks into LDS (they split the 1 KiB
 // units), both beside one compute wave per slice group and beside the state
@@ -1073,15 +1078,15 @@ constexpr int kGateSlicesPerWave = 2;
 // waves were best: 1.26 against 1.33 ms with 4).
 constexpr int kIoWaves = 4;
 
-template <int DK, int C, typename T, bool kGate = false> struct Inter {
-    static constexpr int G = kGate ? kGateSlices : kGroupSlices;   // most slices per workgroup
-    static constexpr int SPW = kGate ? kGateSlicesPerWave : 1;
+template <int DK, int C, typename T, bool kWhole = false, bool kGated = false> struct Inter {
+    static constexpr int G = kWhole ? kRowSlices : kGroupSlices;   // most slices per workgroup
+    static constexpr int SPW = kWhole ? (kGated ? kGatedSlicesPerWave : kRowSlicesPerWave) : 1;
     static constexpr int kMaxCompute = (G + SPW - 1) / SPW;
     static constexpr int64_t kShared = (2 * Frag<T>::elems(C, DK) + Frag<T>::elems(DK, C) + Frag<T>::elems(C, C)) *
                                            (int64_t)sizeof(T) + round_kib(DK * 4);
     static constexpr int64_t kGroupMax = round_kib((int64_t)G * C * 16 * sizeof(T));
     static constexpr int64_t kBuf = kShared + kGroupMax;
-    static constexpr int64_t kPart = kGate ? 2ll * kMaxCompute * C * 4 : 0;   // output-norm partial sums
+    static constexpr int64_t kPart = kGated ? 2ll * kMaxCompute * C * 4 : 0;   // output-norm partial sums
     // Output-wave layout (one value slice per workgroup): ring A (W, Kbar^T,
     // gamma_C, the slice of U~) has two slots, ring B (Q~, P) three, since the
     // output wave reads a chunk one interval after the state wave; the state
@@ -1094,7 +1099,7 @@ template <int DK, int C, typename T, bool kGate = false> struct Inter {
     static constexpr int64_t kBufB = kSzW + kSzP;
     static constexpr int64_t kHand = (int64_t)(DK / 16 + C / 16) * 64 * sizeof(quad_t<T>);
     static constexpr int64_t kOWaveLds = 2 * kBufA + 3 * kBufB + 2 * kHand;
-    static constexpr bool kOWave = !kGate && G == 1 && SPW == 1 && kSzW % 1024 == 0 &&
+    static constexpr bool kOWave = !kWhole && G == 1 && SPW == 1 && kSzW % 1024 == 0 &&
                                    kSzP % 1024 == 0 && kSzK == kSzW && kOWaveLds <= 163840;
     static constexpr int kComputeWaves = kOWave ? 2 : kMaxCompute;
     static constexpr int kIo = kIoWaves;
@@ -1135,12 +1140,13 @@ enum OutMode { kOutPlain = 0, kOutGate = 1, kOutSplit = 2, kOutRow = 3 };
 template <int kMode> constexpr bool whole_row_mode() { return kMode == kOutGate || kMode == kOutRow; }
 
 template <int DK, int C, typename In, int kMode>
-__global__ __launch_bounds__((Inter<DK, C, typename OperandOf<In>::type, whole_row_mode<kMode>()>::kThreads))
+__global__ __launch_bounds__((Inter<DK, C, typename OperandOf<In>::type, whole_row_mode<kMode>(),
+                                   kMode == kOutGate>::kThreads))
 void kda_inter_kernel(const PrefillArgs a) {
     constexpr bool kGate = kMode == kOutGate;
     using T = typename OperandOf<In>::type;
     using Q = quad_t<T>;
-    using X = Inter<DK, C, T, whole_row_mode<kMode>()>;
+    using X = Inter<DK, C, T, whole_row_mode<kMode>(), kGate>;
     static_assert(X::kFits, "LDS ring of the inter-chunk kernel exceeds one workgroup");
     constexpr int NB = C / 16, NQK = DK / 16, SPW = X::SPW;
     __shared__ __attribute__((aligned(1024))) char ring[X::kLds];
@@ -1160,10 +1166,10 @@ void kda_inter_kernel(const PrefillArgs a) {
     const int b = blockIdx.x, xcd = b & 7, jx = b >> 3;
     int grp = jx % ngroups;
     int unit = (jx / ngroups) * 8 + xcd;
-    // chunk-range scan (whole-row plain calls with range_len > 0): workgroup b
-    // runs range b / H of head b % H
+    // chunk-range scan (whole-row calls with range_len > 0): workgroup b runs
+    // range b / H of head b % H
     RangePos rp{};
-    const bool ranged = kMode == kOutRow && a.range_len > 0;
+    const bool ranged = whole_row_mode<kMode>() && a.range_len > 0;
     if (ranged) {
         grp = 0;
         if (!locate_range(a, b / H, rp)) return;   // whole workgroup
@@ -1451,9 +1457,40 @@ void kda_inter_kernel(const PrefillArgs a) {
         int64_t ptok0 = 0;
         int pvalid = 0, pbuf = 0;
         bool pending = false;
+        // the gate logits of the pending outputs, as loaded: they are loaded
+        // when the chunk's interval begins and used when its outputs are
+        // stored, one interval later (loading them there exposed an HBM round
+        // trip per chunk: 2.86 against 2.58 ms for the gated long-context call)
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        using GRaw = typename std::conditional<sizeof(In) == 2, u32x2, f32x4>::type;
+        GRaw gpend[kGate ? NB : 1][kGate ? SPW : 1];
+        const bool gvec = (reinterpret_cast<uintptr_t>(a.gate) & (4 * sizeof(In) - 1)) == 0;
+        auto gate_load = [&](int64_t tok0, int valid) {
+            if constexpr (kGate) {
+#pragma unroll
+                for (int tb = 0; tb < NB; ++tb) {
+                    const int r = 16 * tb + cl;
+#pragma unroll
+                    for (int n = 0; n < SPW; ++n) {
+                        if (r < valid && n < nsl) {
+                            const int64_t oi = ((tok0 + r) * H + h) * DV + 16 * (s0 + n) + 4 * g;
+                            const In* gp = reinterpret_cast<const In*>(a.gate) + oi;
+                            if constexpr (sizeof(In) == 2) {
+                                const unsigned short* gs = reinterpret_cast<const unsigned short*>(gp);
+                                gpend[tb][n] = gvec ? *reinterpret_cast<const u32x2*>(gp)
+                                                    : u32x2{gs[0] | ((unsigned)gs[1] << 16), gs[2] | ((unsigned)gs[3] << 16)};
+                            } else {
+                                const float* gf = reinterpret_cast<const float*>(gp);
+                                gpend[tb][n] = gvec ? *reinterpret_cast<const f32x4*>(gf)
+                                                    : f32x4{gf[0], gf[1], gf[2], gf[3]};
+                            }
+                        }
+                    }
+                }
+            }
+        };
         auto flush = [&]() {
             if constexpr (kGate) {
-                const In* __restrict__ gt = reinterpret_cast<const In*>(a.gate);
 #pragma unroll
                 for (int tb = 0; tb < NB; ++tb) {
                     const int r = 16 * tb + cl;
@@ -1465,10 +1502,21 @@ void kda_inter_kernel(const PrefillArgs a) {
                         if (r < pvalid && n < nsl) {
                             const int col = 16 * (s0 + n) + 4 * g;
                             const int64_t oi = ((ptok0 + r) * H + h) * DV + col;
+                            float gl4[4];
+                            if constexpr (sizeof(In) == 2) {
+                                const u32x2 w2 = gpend[tb][n];
+                                gl4[0] = __uint_as_float(w2[0] << 16);
+                                gl4[1] = __uint_as_float(w2[0] & 0xffff0000u);
+                                gl4[2] = __uint_as_float(w2[1] << 16);
+                                gl4[3] = __uint_as_float(w2[1] & 0xffff0000u);
+                            } else {
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) gl4[j] = gpend[tb][n][j];
+                            }
                             f32x4 o4 = opend[tb][n] * inv;
 #pragma unroll
                             for (int j = 0; j < 4; ++j)
-                                o4[j] *= (a.norm_w ? a.norm_w[col + j] : 1.f) * sigmoid(load_as_float(gt, oi + j));
+                                o4[j] *= (a.norm_w ? a.norm_w[col + j] : 1.f) * sigmoid(gl4[j]);
                             if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + oi, o4);
                             else store4(reinterpret_cast<__bf16*>(a.o) + oi, o4);
                         }
@@ -1490,6 +1538,7 @@ void kda_inter_kernel(const PrefillArgs a) {
             const float* gl = reinterpret_cast<const float*>(buf + cb.gam);
             const T* Ul = reinterpret_cast<const T*>(buf + X::kShared + (s0 - grp * cb.gsl) * cb.slice);
             if (kGate && pending) flush();   // the previous chunk: its partial sums are complete
+            if (kGate) gate_load(tok0, valid);
 
             Q sb[SPW][NQK];
 #pragma unroll
@@ -1847,7 +1896,8 @@ template <int DK, int C, typename In>
 static hipError_t launch_phase_t(const PrefillArgs& a, int max_chunks, bool intra, hipStream_t stream) {
     if constexpr (!Intra<DK, C, typename OperandOf<In>::type>::kFits ||
                   !Inter<DK, C, typename OperandOf<In>::type>::kFits ||
-                  !Inter<DK, C, typename OperandOf<In>::type, true>::kFits) {
+                  !Inter<DK, C, typename OperandOf<In>::type, true>::kFits ||
+                  !Inter<DK, C, typename OperandOf<In>::type, true, true>::kFits) {
         return hipErrorInvalidValue;  // effective_chunk() never selects this
     } else {
         if (intra) {
@@ -1865,26 +1915,30 @@ static hipError_t launch_phase_t(const PrefillArgs& a, int max_chunks, bool intr
         } else {
             const int units = a.N * a.H;
             const int blocks = ((units + 7) / 8) * 8 * (a.DV / 16 / a.gsl);
-            if (a.gate && !a.gate_split) {
-                constexpr int spw = Inter<DK, C, typename OperandOf<In>::type, true>::SPW;
-                hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutGate>), dim3(blocks),
-                                   dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
-            } else if (a.whole_rows && a.range_len > 0) {
+            if (a.whole_rows && a.range_len > 0) {
                 // chunk-range scan: range maps, the ranges' start states, then
-                // every range's whole-row pass
+                // every range's whole-row pass (gated calls finish the output
+                // norm in that pass)
                 using T = typename OperandOf<In>::type;
                 if constexpr (C == 64 && (DK == 64 || DK == 128) && sizeof(T) == 2 && RangeSum<DK, C, T>::kFits) {
-                    constexpr int spw = Inter<DK, C, T, true>::SPW;
+                    const int spw = a.gate ? Inter<DK, C, T, true, true>::SPW : Inter<DK, C, T, true>::SPW;
                     const dim3 grid((unsigned)a.max_ranges * (unsigned)a.H);
+                    const dim3 threads(64 * ((a.gsl + spw - 1) / spw + kIoWaves));
                     hipLaunchKernelGGL((kda_range_kernel<DK, C, In>), grid, dim3(RangeSum<DK, C, T>::kThreads), 0,
                                        stream, a);
-                    hipLaunchKernelGGL((kda_range_scan_kernel<DK>), dim3((unsigned)(((units + 7) / 8) * 8 * (a.DV / 16))), dim3(256),
-                                       0, stream, a);
-                    hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutRow>), grid,
-                                       dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
+                    hipLaunchKernelGGL((kda_range_scan_kernel<DK>), dim3((unsigned)(((units + 7) / 8) * 8 * (a.DV / 16))),
+                                       dim3(256), 0, stream, a);
+                    if (a.gate)
+                        hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutGate>), grid, threads, 0, stream, a);
+                    else
+                        hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutRow>), grid, threads, 0, stream, a);
                 } else {
                     return hipErrorInvalidValue;   // range_length() never selects this
                 }
+            } else if (a.gate && !a.gate_split) {
+                constexpr int spw = Inter<DK, C, typename OperandOf<In>::type, true, true>::SPW;
+                hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutGate>), dim3(blocks),
+                                   dim3(64 * ((a.gsl + spw - 1) / spw + kIoWaves)), 0, stream, a);
             } else if (a.whole_rows) {
                 constexpr int spw = Inter<DK, C, typename OperandOf<In>::type, true>::SPW;
                 hipLaunchKernelGGL((kda_inter_kernel<DK, C, In, kOutRow>), dim3(blocks),
@@ -1926,8 +1980,10 @@ static hipError_t launch_phase_k(const PrefillArgs& a, int DK, int C, int max_ch
 }
 
 template <typename T> static bool fits(int DK, int C) {
-#define KDA_FITS_CASE(D, CC) \
-    if (DK == D && C == CC) return Intra<D, CC, T>::kFits && Inter<D, CC, T>::kFits && Inter<D, CC, T, true>::kFits;
+#define KDA_FITS_CASE(D, CC)                                                                  \
+    if (DK == D && C == CC)                                                                   \
+        return Intra<D, CC, T>::kFits && Inter<D, CC, T>::kFits && Inter<D, CC, T, true>::kFits && \
+               Inter<D, CC, T, true, true>::kFits;
     KDA_FITS_CASE(16, 16) KDA_FITS_CASE(16, 32) KDA_FITS_CASE(16, 64)
     KDA_FITS_CASE(32, 16) KDA_FITS_CASE(32, 32) KDA_FITS_CASE(32, 64)
     KDA_FITS_CASE(64, 16) KDA_FITS_CASE(64, 32) KDA_FITS_CASE(64, 64)

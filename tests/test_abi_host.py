@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import linear_attention_sequence_gated_amd as kda
-from linear_attention_sequence_gated_amd._lib import ChunkParams, ChunkPlan
+from linear_attention_sequence_gated_amd._lib import ChunkOptions, ChunkParams, ChunkPlan
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
@@ -113,6 +113,30 @@ def test_plan(lib):
     assert _plan(lib, _params(batch=2, num_seqs=2, seqlen=20073), packed=1)[0] == INVALID
     assert _plan(lib, _params(head_dim_k=96))[0] == UNSUPPORTED
     assert lib.kda_chunk_fwd_plan(ctypes.byref(_params()), 0, None) == INVALID
+
+
+def test_gated_workspace_adds_epilogue_scratch_only_for_one_slice_shapes(lib):
+    """The epilogue's scratch (fp32 outputs and per-slice sums of squares) is
+    quoted for gated calls only where they take one-slice workgroups."""
+    if torch.cuda.device_count() > 0 and torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the layouts assume 256 compute units")
+    gated = ChunkOptions(gate=FAKE.value)
+
+    def quotes(**kw):
+        p = _params(**kw)
+        plain, gate = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        assert lib.kda_chunk_fwd_ex_workspace_size(ctypes.byref(p), None, ctypes.byref(plain)) == OK
+        assert lib.kda_chunk_fwd_ex_workspace_size(ctypes.byref(p), ctypes.byref(gated), ctypes.byref(gate)) == OK
+        return plain.value, gate.value
+
+    T, H, dv = 2048, 4, 128   # 32 chunks over 4 pairs: one-slice workgroups in either layout
+    plain, gate = quotes(seqlen=T, num_heads=H)
+    scratch = -(-T * H * dv * 4 // 256) * 256 + -(-T * H * (dv // 16) * 4 // 256) * 256
+    assert gate >= plain + scratch
+    for kw in (dict(seqlen=65536, num_heads=32),     # chunk ranges
+               dict(seqlen=256, num_heads=256)):     # whole rows
+        plain, gate = quotes(**kw)
+        assert gate == plain, kw
 
 
 def _fwd(lib, p, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s0=None, cu=None, o=FAKE, sf=None,

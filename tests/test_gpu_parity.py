@@ -796,6 +796,32 @@ def test_chunk_range_scan_checkpoints_cross_ranges():
     _ckpt_check(inp, 64, 1024, 9, TOL[torch.bfloat16], "ranges packed [9000, 4100]")
 
 
+@pytest.mark.parametrize("B,T,H,lengths", [(2, 5000, 2, None), (1, 0, 2, [9000, 0, 7000, 1, 3072])])
+def test_chunk_range_scan_gated(B, T, H, lengths):
+    # the output norm and gate are finished in the ranged whole-row pass
+    inp = workloads.make_inputs(B, T, H, 128, 128, torch.bfloat16, s0_std=0.02, seed=1120 + T, lengths=lengths)
+    assert _ranged(B, T, H, 128, lengths)
+    _gate_case(inp, 64, TOL[torch.bfloat16], f"ranges B{B} T{T} H{H} {lengths}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16])
+def test_chunk_range_scan_gated_unaligned_gate(dtype):
+    # gate logits one element past an aligned allocation take element loads
+    # in the whole-row pass; the result is the same bit for bit
+    inp = workloads.make_inputs(2, 5000, 2, 128, 128, dtype, s0_std=0.02, seed=1123)
+    assert _ranged(2, 5000, 2, 128)
+    oa = _gate_case(inp, 64, TOL[dtype], "ranges aligned").cpu()
+    om = _gate_case(inp, 64, TOL[dtype], "ranges gate and weight one element off", misalign=True).cpu()
+    assert torch.equal(oa, om)
+
+
+def test_chunk_range_scan_gated_fused_inputs():
+    opts = {"fuse_inputs": True}
+    inp = _prefill_opts_inputs(1, 6200, 3, 128, 128, torch.bfloat16, seed=1122, **opts)
+    assert _ranged(1, 6200, 3, 128)
+    _gate_case(inp, 64, TOL[torch.bfloat16], "ranges B1 T6200 H3 fused", **opts)
+
+
 def test_chunk_range_scan_resume_equals_one_pass():
     inp = workloads.make_inputs(1, 8192, 2, 128, 128, torch.bfloat16, s0_std=0.02, seed=1112)
     o_full, S_full = gpu_prefill(inp, 64)
