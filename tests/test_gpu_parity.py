@@ -822,6 +822,22 @@ def test_chunk_range_scan_gated_fused_inputs():
     _gate_case(inp, 64, TOL[torch.bfloat16], "ranges B1 T6200 H3 fused", **opts)
 
 
+@pytest.mark.parametrize("opts", [{"decay_floor": 0.6}, {"alpha_scalar": True}, {"decay_floor": 0.3}])
+def test_chunk_range_scan_with_input_options(opts):
+    # the floor and scalar-gate instances of the intra-chunk kernel feed the
+    # range maps and the ranged walk like the plain one
+    lens = [9000, 6100, 0, 64]
+    inp = _prefill_opts_inputs(1, 0, 2, 128, 128, torch.bfloat16, seed=1124, lengths=lens, alpha_mu=2.0, **opts)
+    assert _ranged(1, 0, 2, 128, lens)
+    _prefill_opts_check(inp, 64, TOL[torch.bfloat16], f"ranges packed {lens}", **opts)
+
+
+def test_chunk_range_scan_dk64_packed_with_checkpoints():
+    inp = workloads.make_inputs(1, 0, 3, 64, 64, torch.bfloat16, s0_std=0.02, seed=1125, lengths=[5000, 1, 4096])
+    assert _ranged(1, 0, 3, 64, [5000, 1, 4096])
+    _ckpt_check(inp, 64, 512, 10, TOL[torch.bfloat16], "ranges dk64 packed [5000, 1, 4096]")
+
+
 def test_chunk_range_scan_resume_equals_one_pass():
     inp = workloads.make_inputs(1, 8192, 2, 128, 128, torch.bfloat16, s0_std=0.02, seed=1112)
     o_full, S_full = gpu_prefill(inp, 64)
