@@ -394,11 +394,13 @@ void kda_intra_kernel(const PrefillArgs a) {
                     for (int e = 0; e < 8; ++e) al[u][e] = fmaxf(al[u][e], a.alpha_floor);
                 }
             }
+            if (!p1 || valid < C) {   // a partial chunk's tail, threads outside the mapping
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                kr[u][e] = ok ? kr[u][e] : 0.f;
-                qr[u][e] = ok ? qr[u][e] : 0.f;
-                al[u][e] = ok ? al[u][e] : 1.f;
+                for (int e = 0; e < 8; ++e) {
+                    kr[u][e] = ok ? kr[u][e] : 0.f;
+                    qr[u][e] = ok ? qr[u][e] : 0.f;
+                    al[u][e] = ok ? al[u][e] : 1.f;
+                }
             }
         }
     }
@@ -582,65 +584,31 @@ void kda_intra_kernel(const PrefillArgs a) {
     // and products ran for every element.
     auto factor_phase = [&](auto path) {
         constexpr bool fast = decltype(path)::value;
-        float sh[8], gb[8], pre[8], tail[8];
+        // fast path, per channel of block R: the row factor fa = 2^{g_r - G_R + h_R}
+        // runs as a product of alpha from pre; Ktilde and Qtilde are the row-side
+        // operands times cq = 2^{G_R - h_R}, and Kbar = k 2^{g_C - g_r} is the
+        // column-side operand times dq = 2^{g_C - G_R + h_R}
+        float sh[8], cq[8], pre[8], dq[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int c = 8 * cg + e;
             const float G0 = Gs[Rb * DK + c];
             const float hR = 0.5f * (G0 - Ge[Rb * DK + c]);
             sh[e] = __builtin_amdgcn_exp2f(fminf(hR, 30.f));          // 2^{h_R}
-            gb[e] = __builtin_amdgcn_exp2f(G0);                        // 2^{G_R}
+            cq[e] = __builtin_amdgcn_exp2f(G0 - hR);                   // 2^{G_R - h_R}
             pre[e] = sp == 0 ? 1.f : __builtin_amdgcn_exp2f(off[e] - G0);  // decay from the block's first token
-            tail[e] = __builtin_amdgcn_exp2f(fminf(tot[e] - (off[e] + lg[3][e]), 0.f));  // to the chunk's end
+            dq[e] = __builtin_amdgcn_exp2f(fminf(tot[e] - G0 + hR, 30.f));  // 2^{g_C - G_R + h_R}
         }
-        // backward pass: Kbar = k 2^{g_C - g_r} (suffix products), straight to the workspace
-        {
-            const int ut = sgi >> 2, gq = sgi & 3;
-            f32x4 kbq[8];
+        // Kbar quads (4 tokens of a channel); the exact path forms them here, the
+        // fast path in the forward pass below
+        const int ut = sgi >> 2, gq = sgi & 3;
+        f32x4 kbq[8];
+        if constexpr (!fast) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if (fast) {
-                    float sf = tail[e];
+            for (int e = 0; e < 8; ++e)
 #pragma unroll
-                    for (int u = 3; u >= 0; --u) {
-                        kbq[e][u] = kr[u][e] * sf;
-                        sf *= al[u][e];
-                    }
-                } else {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        kbq[e][u] = kr[u][e] * __builtin_amdgcn_exp2f(fminf(tot[e] - (off[e] + lg[u][e]), 0.f));
-                }
-            }
-            if constexpr (sizeof(T) == 2 && I::NSEG == 16) {
-                // a fragment lane's 16 bytes hold the token quads ut and ut ^ 1 of one
-                // channel, which lie with this thread and the one 4 lanes away (same DPP
-                // row).  Per channel pair the even-ut thread writes channel e0 and the
-                // odd-ut thread channel e1, each fetching the partner's quad by DPP
-                // (moves unconditional, the choice by select).
-                const bool odd = (ut & 1) != 0;
-#pragma unroll
-                for (int e0 = 0; e0 < 8; e0 += 2) {
-                    const Q q0 = make_quad<T>(kbq[e0]), q1 = make_quad<T>(kbq[e0 + 1]);
-                    typedef int i32x2 __attribute__((ext_vector_type(2)));
-                    const i32x2 w0 = __builtin_bit_cast(i32x2, q0), w1 = __builtin_bit_cast(i32x2, q1);
-                    i32x2 up, dn;   // partner's e0 quad (from 4 lanes above), e1 quad (from 4 below)
-                    up[0] = __builtin_amdgcn_update_dpp(0, w0[0], 0x104, 0xf, 0xf, true);
-                    up[1] = __builtin_amdgcn_update_dpp(0, w0[1], 0x104, 0xf, 0xf, true);
-                    dn[0] = __builtin_amdgcn_update_dpp(0, w1[0], 0x114, 0xf, 0xf, true);
-                    dn[1] = __builtin_amdgcn_update_dpp(0, w1[1], 0x114, 0xf, 0xf, true);
-                    typedef int i32x4 __attribute__((ext_vector_type(4)));
-                    const i32x4 v = odd ? i32x4{dn[0], dn[1], w1[0], w1[1]} : i32x4{w0[0], w0[1], up[0], up[1]};
-                    const int c = 8 * cg + e0 + (odd ? 1 : 0);
-                    *reinterpret_cast<i32x4*>(Kbf + Frag<T>::off(c >> 4, ut & ~1, 16 * gq + (c & 15), C)) = v;
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int c = 8 * cg + e;
-                    store_q<T>(Kbf + Frag<T>::off(c >> 4, ut, 16 * gq + (c & 15), C), kbq[e]);
-                }
-            }
+                for (int u = 0; u < 4; ++u)
+                    kbq[e][u] = kr[u][e] * __builtin_amdgcn_exp2f(fminf(tot[e] - (off[e] + lg[u][e]), 0.f));
         }
         // forward pass: prefix products give the row / column factors and 2^{g_r}
         float ktil[4][8];
@@ -653,7 +621,6 @@ void kda_intra_kernel(const PrefillArgs a) {
             float ak[8], aq[8], bd[8], qt[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float gm;
                 if (fast) {
                     if (!(sp == 0 && u == 0)) pr[e] *= al[u][e];   // 2^{g_r - G_R}
                     const float fa = pr[e] * sh[e];                // in 2^[-h, h]
@@ -661,12 +628,14 @@ void kda_intra_kernel(const PrefillArgs a) {
                     ak[e] = kr[u][e] * fa;
                     aq[e] = qr[u][e] * fa;
                     bd[e] = kr[u][e] * fb;
-                    gm = pr[e] * gb[e];                            // 2^{g_r}
+                    kbq[e][u] = bd[e] * dq[e];                     // k 2^{g_C - g_r}
+                    ktil[u][e] = ak[e] * cq[e];                    // k 2^{g_r}
+                    qt[e] = aq[e] * cq[e];
                 } else {
-                    gm = __builtin_amdgcn_exp2f(off[e] + lg[u][e]);
+                    const float gm = __builtin_amdgcn_exp2f(off[e] + lg[u][e]);   // 2^{g_r}
+                    ktil[u][e] = kr[u][e] * gm;
+                    qt[e] = qr[u][e] * gm;
                 }
-                ktil[u][e] = kr[u][e] * gm;
-                qt[e] = qr[u][e] * gm;
             }
             if (fast) {
                 store8(Ak + r * LD_ROW + 8 * cg, ak);
@@ -705,6 +674,35 @@ void kda_intra_kernel(const PrefillArgs a) {
                     store_q<T>(Qf + Frag<T>::off(r >> 4, ut, 16 * gq + (r & 15), DK),
                                f32x4{qt[4 * hq], qt[4 * hq + 1], qt[4 * hq + 2], qt[4 * hq + 3]});
                 }
+            }
+        }
+        if constexpr (sizeof(T) == 2 && I::NSEG == 16) {
+            // Kbar to the workspace: a fragment lane's 16 bytes hold the token quads
+            // ut and ut ^ 1 of one channel, which lie with this thread and the one 4
+            // lanes away (same DPP row).  Per channel pair the even-ut thread writes
+            // channel e0 and the odd-ut thread channel e1, each fetching the partner's
+            // quad by DPP (moves unconditional, the choice by select).
+            const bool odd = (ut & 1) != 0;
+#pragma unroll
+            for (int e0 = 0; e0 < 8; e0 += 2) {
+                const Q q0 = make_quad<T>(kbq[e0]), q1 = make_quad<T>(kbq[e0 + 1]);
+                typedef int i32x2 __attribute__((ext_vector_type(2)));
+                const i32x2 w0 = __builtin_bit_cast(i32x2, q0), w1 = __builtin_bit_cast(i32x2, q1);
+                i32x2 up, dn;   // partner's e0 quad (from 4 lanes above), e1 quad (from 4 below)
+                up[0] = __builtin_amdgcn_update_dpp(0, w0[0], 0x104, 0xf, 0xf, true);
+                up[1] = __builtin_amdgcn_update_dpp(0, w0[1], 0x104, 0xf, 0xf, true);
+                dn[0] = __builtin_amdgcn_update_dpp(0, w1[0], 0x114, 0xf, 0xf, true);
+                dn[1] = __builtin_amdgcn_update_dpp(0, w1[1], 0x114, 0xf, 0xf, true);
+                typedef int i32x4 __attribute__((ext_vector_type(4)));
+                const i32x4 v = odd ? i32x4{dn[0], dn[1], w1[0], w1[1]} : i32x4{w0[0], w0[1], up[0], up[1]};
+                const int c = 8 * cg + e0 + (odd ? 1 : 0);
+                *reinterpret_cast<i32x4*>(Kbf + Frag<T>::off(c >> 4, ut & ~1, 16 * gq + (c & 15), C)) = v;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = 8 * cg + e;
+                store_q<T>(Kbf + Frag<T>::off(c >> 4, ut, 16 * gq + (c & 15), C), kbq[e]);
             }
         }
 #pragma unroll
