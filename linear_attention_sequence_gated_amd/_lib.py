@@ -187,8 +187,10 @@ def chunk_plan(q: torch.Tensor, v: torch.Tensor, cu_seqlens=None, chunk_size: in
 class Prefill:
     """A kda_chunk_fwd call with its arguments marshalled once.
 
-    ``run()`` issues kda_chunk_fwd; ``intra()`` / ``inter()`` issue its two
-    halves.  The tensors are kept alive by this object.
+    ``run()`` issues kda_chunk_fwd (kda_chunk_fwd_ex with options);
+    ``intra()`` / ``inter()`` issue the two halves of a plain call and raise
+    ValueError for a call with options.  The tensors are kept alive by this
+    object.
     """
 
     def __init__(self, q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_size: int = 64,
@@ -274,11 +276,19 @@ class Prefill:
         """Raise KdaError(KDA_ERR_RANGE) if the last run wrote a value that is not finite."""
         _check("kda_chunk_fwd_status", self.status())
 
+    def _plain_phase(self, name):
+        # kda_chunk_fwd_intra / _inter are the two halves of the plain call: they
+        # take no options, so a call with options (a per-token alpha, a gate,
+        # checkpoints ...) would run with its tensors read in the plain layout
+        if self.options is not None:
+            raise ValueError(f"{name}: the split phases run the plain call only; this call has options")
+        return getattr(self._lib, name)
+
     def intra(self):
-        _check("kda_chunk_fwd_intra", self._lib.kda_chunk_fwd_intra(*self._args))
+        _check("kda_chunk_fwd_intra", self._plain_phase("kda_chunk_fwd_intra")(*self._args))
 
     def inter(self):
-        _check("kda_chunk_fwd_inter", self._lib.kda_chunk_fwd_inter(*self._args))
+        _check("kda_chunk_fwd_inter", self._plain_phase("kda_chunk_fwd_inter")(*self._args))
         return self.o, self.final_state
 
 

@@ -107,3 +107,22 @@ def test_whole_tensor_error_equals_rel_err_of_the_concatenation():
 def test_whole_tensor_error_rejects_non_finite():
     with pytest.raises(AssertionError):
         WholeTensorError().add(np.array([1.0, np.inf]), np.array([1.0, 1.0]))
+
+
+@pytest.mark.parametrize("opts", [dict(alpha_scalar=True), dict(decay_floor=0.5), dict(fuse_inputs=True)])
+def test_split_phases_refuse_calls_with_options(monkeypatch, opts, guarded):
+    """kda_chunk_fwd_intra / _inter take no options: a call object with options
+    (here a per-token alpha, a floor, fused inputs) must not reach them, or its
+    tensors would be read in the plain layout."""
+    monkeypatch.setattr(_lib, "_on_device", lambda t: t.device.type == "meta")
+    args = _prefill_args()
+    if opts.get("alpha_scalar"):
+        args["alpha"] = _meta(B, T, H, dtype=torch.float32)
+    pre = _lib.Prefill(**args, **opts, stream=type("S", (), {"cuda_stream": 0})())   # no device here
+
+    def reached(*a, **k):
+        raise AssertionError("a split phase reached the library")
+    monkeypatch.setattr(pre, "_lib", type("L", (), {"kda_chunk_fwd_intra": reached, "kda_chunk_fwd_inter": reached}))
+    for phase in (pre.intra, pre.inter):
+        with pytest.raises(ValueError, match="plain call only"):
+            phase()
