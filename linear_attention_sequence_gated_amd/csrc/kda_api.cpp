@@ -25,17 +25,18 @@ bool head_dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace: [range status word (kWsAlign bytes)] [chunk-offset table (packed
-// input only)] [per (chunk, head) blocks] [chunk-range scan: range-offset
-// table (packed), range maps, range start states] [gate scratch (split gated
-// calls)].
+// Workspace: [range status word (kWsAlign bytes)] [chunk-offset table and
+// sequence order (packed input only)] [per (chunk, head) blocks] [chunk-range
+// scan: range-offset table (packed), range maps, range start states] [gate
+// scratch (split gated calls)].
 constexpr size_t kStatusBytes = kWsAlign;
 
 struct PrefillPlan {
     int64_t max_chunks;     // per head, worst case
     int64_t block_bytes;    // per (chunk, head)
-    size_t off_bytes;       // chunk-offset table (packed input only)
+    size_t off_bytes;       // chunk-offset table and sequence order (packed input only)
     bool whole;             // whole-row inter-chunk workgroups
+    bool seq_order;         // the whole-row pass takes the packed sequences longest first
     int range_len;          // chunks per range of the chunk-range scan (0: none)
     int64_t max_ranges;     // ranges of the call at most
     int ranges_per_seq;     // fixed-length input
@@ -87,7 +88,10 @@ PrefillPlan plan_prefill(const kda_chunk_params_t* p, bool packed, bool gate) {
     pl.whole = kda::whole_rows(units) || pl.range_len > 0;
     pl.block_bytes = kda::chunk_block_bytes(p->head_dim_k, (int)C, p->head_dim_v, bf16,
                                             kda::slice_group(p->head_dim_v, pl.whole));
-    pl.off_bytes = packed ? round_up(sizeof(int32_t) * ((size_t)p->num_seqs + 1), kWsAlign) : 0;
+    pl.off_bytes = packed ? round_up(sizeof(int32_t) * ((size_t)p->num_seqs + 1), kWsAlign) +
+                                round_up(sizeof(int32_t) * (size_t)p->num_seqs, kWsAlign)
+                          : 0;
+    pl.seq_order = packed && pl.whole && pl.range_len == 0;
     size_t at = kStatusBytes + pl.off_bytes + (size_t)pl.max_chunks * (size_t)p->num_heads * (size_t)pl.block_bytes;
     if (pl.range_len > 0) {
         const int64_t L = pl.range_len;
@@ -279,6 +283,11 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
     a.cu_seqlens = cu_seqlens;
     a.status = reinterpret_cast<int32_t*>(ws);
     a.chunk_off = packed ? reinterpret_cast<const int32_t*>(ws + kStatusBytes) : nullptr;
+    int32_t* const seq_order =
+        packed ? reinterpret_cast<int32_t*>(ws + kStatusBytes +
+                                            round_up(sizeof(int32_t) * ((size_t)p->num_seqs + 1), kWsAlign))
+               : nullptr;
+    a.seq_order = pl.seq_order ? seq_order : nullptr;
     a.o = o;
     a.ws_chunks = ws + kStatusBytes + pl.off_bytes;
     a.T = p->seqlen;
@@ -327,6 +336,10 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
                                                                    reinterpret_cast<int32_t*>(ws + pl.range_off), s)
                                  : kda::launch_chunk_offsets(cu_seqlens, p->num_seqs, C, chunk_off, s);
             if (e != hipSuccess) return KDA_ERR_HIP;
+            if (pl.seq_order) {
+                e = kda::launch_seq_order(cu_seqlens, p->num_seqs, C, seq_order, s);
+                if (e != hipSuccess) return KDA_ERR_HIP;
+            }
         }
         // the intra-chunk kernel clears the range status; without chunks to
         // process it is not launched and a one-thread kernel clears it

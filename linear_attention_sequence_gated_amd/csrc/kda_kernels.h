@@ -49,6 +49,9 @@ struct PrefillArgs {
     const int32_t* range_off;    // packed input: [N + 1] first range of each sequence
     float* range_ab;             // [ranges, H, dk, dk + dv] fp32: A (dk columns), then B (dv columns)
     float* range_start;          // [ranges, H, dk, dv] fp32: state at the start of each range (first unused)
+    // packed input, whole-row pass without ranges: [N] the sequences by
+    // decreasing chunk count (workgroup b walks sequence seq_order[b / H]), or null
+    const int32_t* seq_order;
     float* o_scratch;            // [B*T*H, dv] un-normalised outputs (split gate)
     float* part_scratch;         // [B*T*H, dv/16] per-slice sums of squares (split gate)
 };
@@ -78,6 +81,10 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t
 // Also the first range of each packed sequence (range_off [n + 1]) for ranges of L chunks.
 hipError_t launch_chunk_range_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t L, int32_t* chunk_off,
                                       int32_t* range_off, hipStream_t s);
+// Packed sequences by decreasing chunk count, ties by index (order [n]); more
+// than kSeqOrderMax sequences keep their input order.
+constexpr int kSeqOrderMax = 4096;
+hipError_t launch_seq_order(const int32_t* cu, int32_t n, int32_t C, int32_t* order, hipStream_t s);
 // Chunks per range of the chunk-range scan for this call shape, or 0 when the
 // scan does not run (it needs dk == dv in {64, 128}, bf16 inputs, 64-token
 // chunks, fewer (sequence, head) pairs than CUs and at least three ranges per

@@ -655,6 +655,15 @@ def test_whole_row_workgroups(dk, dv, C, dtype):
     check_bf16_output(inp, C)
 
 
+def test_whole_row_packed_beyond_the_sequence_sort():
+    # more packed sequences than the longest-first sort holds keep their input
+    # order in the whole-row pass
+    g = torch.Generator().manual_seed(611)
+    lens = torch.randint(0, 40, (4100,), generator=g).tolist()
+    inp = workloads.make_inputs(1, 0, 1, 64, 64, torch.bfloat16, s0_std=0.02, seed=611, lengths=lens)
+    check(inp, 64, TOL[torch.bfloat16], label="4100 packed sequences x H1")
+
+
 def test_whole_row_workgroups_packed_with_checkpoints():
     g = torch.Generator().manual_seed(610)
     lens = torch.randint(0, 200, (130,), generator=g).tolist()
