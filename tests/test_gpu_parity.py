@@ -635,6 +635,15 @@ def test_prefill_gate_unaligned_gate_and_weight(dtype):
     assert torch.equal(oa, om)
 
 
+def test_prefill_gate_many_packed_sequences_whole_rows():
+    # packed, at least as many pairs as CUs: whole rows in the longest-first
+    # sequence order, norm and gate finished in the inter-chunk pass
+    g = torch.Generator().manual_seed(507)
+    lens = torch.randint(0, 200, (300,), generator=g).tolist()
+    inp = workloads.make_inputs(1, 0, 1, 128, 128, torch.bfloat16, s0_std=0.02, seed=507, lengths=lens)
+    _gate_case(inp, 64, TOL[torch.bfloat16], "300 packed sequences x H1")
+
+
 def test_prefill_gate_many_units_fused_in_inter_kernel():
     # at least as many (sequence, head) pairs as CUs: the whole-row workgroups
     # apply the norm and gate inside the inter-chunk kernel
