@@ -60,11 +60,11 @@ KERNEL_SOURCES = {
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {  # kernel: (sources, sha256[:16] of the sources, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "kda_intra_kernel": ("prefill", "9e992431bef40ffc", 1343688.4, 2377917.4),
-    "kda_range_kernel": ("prefill", "9e992431bef40ffc", 702802.6, 29917.1),
-    "kda_range_scan_kernel": ("prefill", "9e992431bef40ffc", 14374.2, 14336.0),
-    "kda_inter_kernel": ("prefill", "9e992431bef40ffc", 1204759.2, 526416.5),
-    "kda_decode_kernel": ("decode", "f676fbf479d26200", 267575.9, 526418.7),
+    "kda_intra_kernel": ("prefill", "13b6c1d83772f234", 1343691.2, 2379334.2),
+    "kda_range_kernel": ("prefill", "13b6c1d83772f234", 702821.6, 30134.4),
+    "kda_range_scan_kernel": ("prefill", "13b6c1d83772f234", 14374.2, 14336.0),
+    "kda_inter_kernel": ("prefill", "13b6c1d83772f234", 1205869.5, 526421.3),
+    "kda_decode_kernel": ("decode", "e7084b214235b198", 267576.3, 526418.5),
 }
 
 
