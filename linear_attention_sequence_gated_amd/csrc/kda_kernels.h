@@ -103,10 +103,11 @@ int decode_columns(int DV);
 // Value slices per inter-chunk workgroup (and per Utilde group of the
 // workspace): all dv / 16 for whole-row workgroups, else the plain grouping.
 int slice_group(int DV, bool whole);
-// Whether the inter-chunk pass runs whole-row workgroups: with at least as
-// many (sequence, head) units as the device has CUs (queried once per
-// device).  With fewer, one-slice workgroups spread the units over every CU,
-// and gated calls finish the norm in an epilogue kernel.
+// Whether there are enough (sequence, head) units for whole-row workgroups:
+// at least as many as the device has CUs (queried once per device).  With
+// fewer, calls that take chunk ranges still run whole rows (one per range);
+// the others spread one-slice workgroups over every CU, and gated ones then
+// finish the norm in an epilogue kernel.
 bool whole_rows(int64_t units);
 hipError_t launch_gate_epilogue(const PrefillArgs& a, int64_t rows, bool bf16, hipStream_t s);
 int64_t chunk_block_bytes(int DK, int C, int DV, bool bf16, int gsl);

@@ -1113,10 +1113,10 @@ constexpr int kRowSlicesPerWave = 2;
 constexpr int kGatedSlicesPerWave = 1;
 
 // Waves per workgroup that copy chunk blocks into LDS (they split the 1 KiB
-// units), both beside one compute wave per slice group and beside the state
-// and output waves.  Long-context inter-chunk pass with the ring B wait
-// deferred: 4 waves 1.036 ms, 6: 1.039, 8: 1.059 (before the deferral 8
-// waves were best: 1.26 against 1.33 ms with 4).
+// units), both beside the compute waves of whole rows and beside the state
+// and output waves of the one-slice form.  One-slice form on the long-context
+// workload with the ring B wait deferred: 4 waves 1.036 ms, 6: 1.039, 8: 1.059
+// (before the deferral 8 waves were best: 1.26 against 1.33 ms with 4).
 constexpr int kIoWaves = 4;
 
 template <int DK, int C, typename T, bool kWhole = false, bool kGated = false> struct Inter {
@@ -1159,8 +1159,9 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 // The I/O waves also pull the block kL2Ahead chunks past the one they copy
-// into L2 (long-context workload: 1 chunk 1.047 ms, 2: 1.056, 3: 1.077;
-// without any prefetch the copies are exposed).
+// into L2 (one-slice form on the long-context workload: 1 chunk 1.047 ms,
+// 2: 1.056, 3: 1.077; without any prefetch the copies are exposed).  The
+// ranged walk issues none: its blocks are its own and would not stay in L2.
 constexpr int kL2Ahead = 1;
 
 // Copy the 1 KiB units first, first + step, ... of `bytes` (a multiple of
@@ -1503,7 +1504,7 @@ void kda_inter_kernel(const PrefillArgs a) {
         // the gate logits of the pending outputs, as loaded: they are loaded
         // when the chunk's interval begins and used when its outputs are
         // stored, one interval later (loading them there exposed an HBM round
-        // trip per chunk: 2.86 against 2.58 ms for the gated long-context call)
+        // trip per chunk: 2.58 against 2.34 ms for the gated long-context call)
         typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
         using GRaw = typename std::conditional<sizeof(In) == 2, u32x2, f32x4>::type;
         GRaw gpend[kGate ? NB : 1][kGate ? SPW : 1];

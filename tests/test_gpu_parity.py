@@ -180,6 +180,32 @@ def test_shapes(B, T, H, dk, dv, C, dtype, s0):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def _random_case(seed):
+    """A seeded random shape: batch or packed lengths (empty, one-token and
+    partial-chunk sequences included), heads, dk, dv, chunk, dtype, initial
+    state, decay level."""
+    g = torch.Generator().manual_seed(seed)
+    pick = lambda xs: xs[int(torch.randint(0, len(xs), (1,), generator=g))]
+    dtype = pick([torch.bfloat16, torch.bfloat16, torch.float32])
+    dk, dv, C = pick([16, 32, 64, 128]), pick([16, 32, 64, 128]), pick([16, 32, 64])
+    H = int(torch.randint(1, 5, (1,), generator=g))
+    s0 = pick([0.0, 0.02])
+    if int(torch.randint(0, 2, (1,), generator=g)):
+        lens = torch.randint(0, 300, (int(torch.randint(1, 9, (1,), generator=g)),), generator=g)
+        lens[torch.rand(lens.shape, generator=g) < 0.2] = int(torch.randint(0, 2, (1,), generator=g))
+        return dict(B=1, T=0, H=H, dk=dk, dv=dv, C=C, dtype=dtype, s0=s0, lengths=lens.tolist())
+    return dict(B=int(torch.randint(1, 4, (1,), generator=g)), T=int(torch.randint(1, 400, (1,), generator=g)),
+                H=H, dk=dk, dv=dv, C=C, dtype=dtype, s0=s0, lengths=None)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes(seed):
+    c = _random_case(4000 + seed)
+    inp = workloads.make_inputs(c["B"], c["T"], c["H"], c["dk"], c["dv"], c["dtype"], s0_std=c["s0"],
+                                seed=4100 + seed, lengths=c["lengths"])
+    check(inp, c["C"], TOL[c["dtype"]], label=f"random {c}")
+
+
 def test_packed_ragged_with_empty_sequences(dtype):
     lens = [0, 1, 63, 64, 65, 200, 0, 129, 7]
     inp = workloads.make_inputs(1, 0, 2, 128, 128, dtype, s0_std=0.02, seed=77, lengths=lens)
