@@ -50,6 +50,16 @@ def test_noalloc_matches_chunk_fwd_two_calls_second_smaller():
     _compare(inp, d, 64)
 
 
+def test_noalloc_with_chunk_ranges():
+    # few long sequences: the range maps, the scanned start states and the
+    # ranged walk all live in the library's scratch
+    inp, d = _case(1, 3072, 4, 128, 128, torch.bfloat16, seed=804)
+    plan = kda.chunk_plan(d["q"], d["v"])
+    assert plan["range_chunks"] > 0, plan
+    assert kda.workspace_size(d["q"], d["v"]) <= kda._lib.NOALLOC_SCRATCH_BYTES
+    _compare(inp, d, 64)
+
+
 def test_noalloc_fp32_and_rejects_oversize():
     inp, d = _case(1, 150, 2, 64, 32, torch.float32, seed=803)
     _compare(inp, d, 32)
