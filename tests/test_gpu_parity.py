@@ -179,7 +179,6 @@ def test_shapes(B, T, H, dk, dv, C, dtype, s0):
     check_bf16_output(inp, C, scale=0.75)
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def _random_case(seed):
     """A seeded random shape: batch or packed lengths (empty, one-token and
     partial-chunk sequences included), heads, dk, dv, chunk, dtype, initial
@@ -206,6 +205,7 @@ def test_random_shapes(seed):
     check(inp, c["C"], TOL[c["dtype"]], label=f"random {c}")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_packed_ragged_with_empty_sequences(dtype):
     lens = [0, 1, 63, 64, 65, 200, 0, 129, 7]
     inp = workloads.make_inputs(1, 0, 2, 128, 128, dtype, s0_std=0.02, seed=77, lengths=lens)
