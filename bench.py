@@ -60,11 +60,11 @@ KERNEL_SOURCES = {
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {  # kernel: (sources, sha256[:16] of the sources, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "kda_intra_kernel": ("prefill", "13b6c1d83772f234", 1343691.2, 2379334.2),
-    "kda_range_kernel": ("prefill", "13b6c1d83772f234", 702821.6, 30134.4),
-    "kda_range_scan_kernel": ("prefill", "13b6c1d83772f234", 14374.2, 14336.0),
-    "kda_inter_kernel": ("prefill", "13b6c1d83772f234", 1205869.5, 526421.3),
-    "kda_decode_kernel": ("decode", "e7084b214235b198", 267576.3, 526418.5),
+    "kda_intra_kernel": ("prefill", "ae1be03a61118a79", 1343690.0, 2379349.8),
+    "kda_range_kernel": ("prefill", "ae1be03a61118a79", 702833.3, 29845.5),
+    "kda_range_scan_kernel": ("prefill", "ae1be03a61118a79", 14374.2, 14336.0),
+    "kda_inter_kernel": ("prefill", "ae1be03a61118a79", 1206300.9, 526430.5),
+    "kda_decode_kernel": ("decode", "11c2598ce8f4d20c", 267576.2, 526422.1),
 }
 
 
