@@ -20,7 +20,8 @@
  * cache lifecycles", and "Kimi K3 Architecture Teardown", section "Scale".
  *
  * Conventions shared by every entry point:
- *  - Every tensor argument is a DEVICE pointer owned by the caller.  The
+ *  - Every tensor argument is a DEVICE pointer owned by the caller (the one
+ *    host array is kda_chunk_fwd_windowed's copy of cu_seqlens).  The
  *    library allocates no device memory, keeps no pointer after returning and
  *    takes scratch only through the caller's workspace; the one exception is
  *    kda_chunk_fwd_noalloc, whose scratch is a fixed device array the
@@ -177,8 +178,44 @@ kda_status_t kda_chunk_fwd_noalloc(const kda_chunk_params_t* params,
                                    const float* initial_state, const int32_t* cu_seqlens,
                                    void* o, float* final_state, void* stream);
 
-/* Range status of the last kda_chunk_fwd / kda_chunk_fwd_ex call (or
- * _intra + _inter pair) made with `workspace`: KDA_OK when every value it
+/* kda_chunk_fwd in bounded memory, for callers that cannot hold the whole
+ * call's workspace: the per-(chunk, head) blocks take about 73 KiB each at
+ * dk = dv = 128, chunk 64, bf16, so a pack of 1M tokens over 16 heads would
+ * need 18 GB at once.  The operation and its results are those of
+ * kda_chunk_fwd (same sources); the work is split into calls that each fit
+ * `workspace_bytes`, run in order on `stream`:
+ *  - whole sequences (batch rows) are grouped while the group's
+ *    kda_chunk_fwd_workspace_size fits;
+ *  - a sequence that does not fit alone runs in windows of whole chunks; each
+ *    window starts from the state the previous one left in final_state (the
+ *    prefix-cache resume of "Kimi K3 architecture: KDA, MLA and MoE", section
+ *    "Serving K3 means managing two cache lifecycles").
+ * Results agree with kda_chunk_fwd up to rounding (the windows end on chunk
+ * boundaries; the inter-chunk pass may be organised differently).
+ * Arguments: those of kda_chunk_fwd, plus `cu_seqlens_host`, a HOST copy of
+ * cu_seqlens (the one host pointer of this ABI; NULL exactly when
+ * cu_seqlens is NULL), which the call reads to plan the windows and checks
+ * (cu[0] == 0, non-decreasing, cu[N] == T).  final_state is required (it
+ * carries the state between windows) and may alias initial_state exactly.
+ * kda_chunk_fwd_status(workspace) afterwards reports a range error of any of
+ * the calls.  The host reads nothing from the device.
+ * Errors (before anything is launched): KDA_ERR_INVALID_ARG (a NULL
+ * final_state, cu_seqlens without its host copy or the reverse, a bad host
+ * cu_seqlens, the argument errors of kda_chunk_fwd), KDA_ERR_WORKSPACE (NULL
+ * or misaligned workspace, or `workspace_bytes` below what one chunk of one
+ * sequence needs: kda_chunk_fwd_workspace_size of one sequence of `chunk`
+ * tokens), the shape errors of kda_chunk_fwd; KDA_ERR_HIP from a launch. */
+kda_status_t kda_chunk_fwd_windowed(const kda_chunk_params_t* params,
+                                    const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta,
+                                    const float* initial_state, const int32_t* cu_seqlens,
+                                    const int32_t* cu_seqlens_host,
+                                    void* o, float* final_state,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* Range status of the last kda_chunk_fwd / kda_chunk_fwd_ex /
+ * kda_chunk_fwd_windowed call (or _intra + _inter pair) made with `workspace`: KDA_OK when every value it
  * wrote to o, final_state and checkpoints is finite, KDA_ERR_RANGE when one
  * is not (see the range contract above).  The intra-chunk half clears the
  * status word (the first 256 bytes of the workspace) and the inter-chunk

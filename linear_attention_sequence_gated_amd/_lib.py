@@ -25,7 +25,8 @@ KDA_ERR_RANGE = 5
 # Every symbol include/kda.h declares.
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
             "kda_chunk_fwd_inter", "kda_chunk_fwd_ex", "kda_chunk_fwd_ex_workspace_size", "kda_decode_step",
-            "kda_decode_step_ex", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_status", "kda_chunk_fwd_plan")
+            "kda_decode_step_ex", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_status", "kda_chunk_fwd_plan",
+            "kda_chunk_fwd_windowed")
 # Bytes of the library-held scratch of kda_chunk_fwd_noalloc (KDA_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -101,6 +102,9 @@ def load() -> ctypes.CDLL:
     lib.kda_chunk_fwd_status.argtypes = [vp, vp]
     lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(ChunkParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kda_chunk_fwd_windowed.restype = ctypes.c_int
+    lib.kda_chunk_fwd_windowed.argtypes = [ctypes.POINTER(ChunkParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           sz, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_step_ex.restype = ctypes.c_int
@@ -357,6 +361,53 @@ def chunk_fwd_noalloc(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
            load().kda_chunk_fwd_noalloc(ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                         _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(final_state),
                                         _stream(stream)))
+    return o, final_state
+
+
+def chunk_fwd_windowed(q, k, v, alpha, beta, workspace, initial_state=None, cu_seqlens=None, o=None,
+                       final_state=None, chunk_size: int = 64, scale: float = 1.0,
+                       o_dtype: Optional[torch.dtype] = None, stream=None, check_range: bool = True):
+    """kda_chunk_fwd_windowed: kda_chunk_fwd in the memory of ``workspace`` (a
+    256-byte aligned device buffer of any size that holds one chunk's call).
+
+    Shapes and dtypes as chunk_fwd.  ``cu_seqlens`` is copied to the host here
+    (the library plans the windows from that copy; the copy synchronises).
+    ``final_state`` is allocated when not given.  Returns (o, final_state).
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(k.shape == q.shape and alpha.shape == q.shape, "q, k, alpha must share [B,T,H,dk]")
+    _need(v.shape == (B, T, H, dv) and beta.shape == (B, T, H), "v/beta shapes")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
+    _need(alpha.dtype == torch.float32 and beta.dtype == torch.float32, "alpha, beta must be fp32")
+    for t in (q, k, v, alpha, beta):
+        _need(_on_device(t) and t.is_contiguous(), "inputs must be contiguous device tensors")
+    _need(isinstance(workspace, torch.Tensor) and _on_device(workspace) and workspace.is_contiguous(),
+          "workspace must be a contiguous device tensor")
+    cu_host = None
+    if cu_seqlens is not None:
+        _need(cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 2, "cu_seqlens must be int32 [N+1] with N >= 1")
+        _dense(cu_seqlens, (cu_seqlens.numel(),), torch.int32, "cu_seqlens")
+        cu_host = cu_seqlens.cpu()
+    n = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    _dense(initial_state, (n, H, dk, dv), torch.float32, "initial_state")
+    _dense(final_state, (n, H, dk, dv), torch.float32, "final_state")
+    o_dtype = q.dtype if o_dtype is None else o_dtype
+    _dense(o, v.shape, o_dtype, "o")
+    if o is None:
+        o = torch.empty(v.shape, dtype=o_dtype, device=v.device)
+    if final_state is None:
+        final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
+    params = chunk_params(q, v, cu_seqlens, chunk_size, scale, o_dtype)
+    lib = load()
+    _check("kda_chunk_fwd_windowed",
+           lib.kda_chunk_fwd_windowed(ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                      _ptr(initial_state), _ptr(cu_seqlens),
+                                      None if cu_host is None else cu_host.data_ptr(), _ptr(o), _ptr(final_state),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)))
+    if check_range:
+        _check("kda_chunk_fwd_status", lib.kda_chunk_fwd_status(_ptr(workspace), _stream(stream)))
     return o, final_state
 
 

@@ -5,7 +5,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
+#include <vector>
 
 #include "kda_kernels.h"
 
@@ -403,6 +405,153 @@ kda_status_t kda_chunk_fwd_noalloc(const kda_chunk_params_t* p, const void* q, c
     // call (chunk offsets, then the per-chunk blocks), so nothing is cleared
     return chunk_fwd_impl(p, nullptr, q, k, v, alpha, beta, initial_state, cu_seqlens, o, final_state, ws,
                           (size_t)KDA_NOALLOC_SCRATCH_BYTES, stream, kBoth);
+}
+
+}  // extern "C"
+
+namespace {
+
+// One call of a windowed prefill: a shape, where its token pointers start,
+// its cu_seqlens (device, absolute token offsets) or none, its first sequence
+// and whether it resumes from final_state.
+struct SubCall {
+    kda_chunk_params_t p;
+    int64_t tok;
+    const int32_t* cu;
+    int64_t seq0;
+    bool resume;
+};
+
+size_t plain_quote(const kda_chunk_params_t& sp, bool packed) {
+    return round_up(plan_prefill(&sp, packed, false).total, kWsAlign);
+}
+
+// Cuts a run of `len` tokens of one sequence (starting at token `tok` of the
+// flattened token axis) into windows of whole chunks that fit `bytes`; each
+// window after the first resumes from the state the one before left.  An
+// empty sequence is one call without tokens (its final state is the initial
+// one).
+kda_status_t plan_windows(const kda_chunk_params_t* p, int64_t tok, int64_t len, int64_t seq, size_t bytes,
+                          std::vector<SubCall>& calls) {
+    kda_chunk_params_t w = *p;
+    w.batch = 1;
+    w.num_seqs = 1;
+    if (len == 0) {
+        w.seqlen = 0;
+        if (plain_quote(w, false) > bytes) return KDA_ERR_WORKSPACE;
+        calls.push_back({w, tok, nullptr, seq, false});
+        return KDA_OK;
+    }
+    const int64_t C = chunk_of(p);
+    auto fits = [&](int64_t m) {
+        w.seqlen = m * C;
+        return plain_quote(w, false) <= bytes;
+    };
+    if (!fits(1)) return KDA_ERR_WORKSPACE;
+    int64_t lo = 1, hi = (len + C - 1) / C;   // the largest chunk count that fits
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo + 1) / 2;
+        if (fits(mid)) lo = mid; else hi = mid - 1;
+    }
+    for (int64_t t0 = 0; t0 < len; t0 += lo * C) {
+        w.seqlen = std::min(lo * C, len - t0);
+        calls.push_back({w, tok + t0, nullptr, seq, t0 > 0});
+    }
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_fwd_windowed(const kda_chunk_params_t* p, const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta, const float* initial_state,
+                                    const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, void* o,
+                                    float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+    kda_status_t st = check_params(p);
+    if (st != KDA_OK) return st;
+    const bool packed = cu_seqlens != nullptr;
+    if (packed != (cu_seqlens_host != nullptr)) return KDA_ERR_INVALID_ARG;
+    if (packed && p->batch != 1) return KDA_ERR_INVALID_ARG;
+    if (!packed && p->num_seqs != p->batch) return KDA_ERR_INVALID_ARG;
+    if (!final_state || !aligned(final_state, 16)) return KDA_ERR_INVALID_ARG;
+    if (initial_state && !aligned(initial_state, 16)) return KDA_ERR_INVALID_ARG;
+    if (initial_state && initial_state != final_state) {
+        const size_t sb = (size_t)p->num_seqs * p->num_heads * p->head_dim_k * p->head_dim_v * sizeof(float);
+        if (overlaps(initial_state, sb, final_state, sb)) return KDA_ERR_INVALID_ARG;
+    }
+    // every window's pointers keep the alignment of the call's (a token's row
+    // is a multiple of 32 bytes), so checking them here covers every window
+    if (p->seqlen > 0) {
+        if (!q || !k || !v || !alpha || !beta || !o) return KDA_ERR_INVALID_ARG;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(alpha, 16) ||
+            !aligned(beta, 4))
+            return KDA_ERR_INVALID_ARG;
+    }
+    if (packed && !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARG;
+    if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_WORKSPACE;
+    const int64_t N = p->num_seqs, T = p->seqlen;
+    if (packed) {   // the host copy makes the layout checkable
+        if (cu_seqlens_host[0] != 0 || cu_seqlens_host[N] != T) return KDA_ERR_INVALID_ARG;
+        for (int64_t n = 0; n < N; ++n)
+            if (cu_seqlens_host[n + 1] < cu_seqlens_host[n]) return KDA_ERR_INVALID_ARG;
+    }
+    // Plan every call before launching any: whole sequences (rows) are grouped
+    // while their quote fits, a sequence that does not fit alone runs in
+    // windows of whole chunks.
+    std::vector<SubCall> calls;
+    int64_t n0 = 0;
+    while (n0 < N) {
+        auto group = [&](int64_t n1) {
+            kda_chunk_params_t g = *p;
+            g.num_seqs = (int32_t)(n1 - n0);
+            if (packed) {
+                g.batch = 1;
+                g.seqlen = (int64_t)cu_seqlens_host[n1] - cu_seqlens_host[n0];
+            } else {
+                g.batch = g.num_seqs;
+            }
+            return g;
+        };
+        int64_t n1 = n0;   // the longest group [n0, n1) that fits
+        {
+            int64_t lo = n0, hi = N;
+            while (lo < hi) {
+                const int64_t mid = lo + (hi - lo + 1) / 2;
+                if (plain_quote(group(mid), packed) <= workspace_bytes) lo = mid; else hi = mid - 1;
+            }
+            n1 = lo;
+        }
+        if (n1 > n0) {
+            calls.push_back({group(n1), packed ? 0 : n0 * T, packed ? cu_seqlens + n0 : nullptr, n0, false});
+            n0 = n1;
+        } else {
+            const int64_t tok = packed ? cu_seqlens_host[n0] : n0 * T;
+            const int64_t len = packed ? (int64_t)cu_seqlens_host[n0 + 1] - cu_seqlens_host[n0] : T;
+            st = plan_windows(p, tok, len, n0, workspace_bytes, calls);
+            if (st != KDA_OK) return st;
+            ++n0;
+        }
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int32_t* status = reinterpret_cast<int32_t*>(workspace);
+    if (kda::launch_fold_status(status, kda::kFoldClear, s) != hipSuccess) return KDA_ERR_HIP;
+    const size_t eq = (size_t)p->num_heads * p->head_dim_k * (p->qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4);
+    const size_t ev = (size_t)p->num_heads * p->head_dim_v * (p->qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4);
+    const size_t eo = (size_t)p->num_heads * p->head_dim_v * (p->o_dtype == KDA_DTYPE_BF16 ? 2 : 4);
+    const size_t ea = (size_t)p->num_heads * p->head_dim_k, eb = (size_t)p->num_heads;   // floats per token
+    const size_t es = (size_t)p->num_heads * p->head_dim_k * p->head_dim_v;              // floats per state
+    for (const SubCall& c : calls) {
+        const size_t t = (size_t)c.tok;
+        const float* s0 = c.resume ? final_state + c.seq0 * es : initial_state ? initial_state + c.seq0 * es : nullptr;
+        st = chunk_fwd_impl(&c.p, nullptr, static_cast<const char*>(q) + t * eq, static_cast<const char*>(k) + t * eq,
+                            static_cast<const char*>(v) + t * ev, alpha + t * ea, beta + t * eb, s0, c.cu,
+                            static_cast<char*>(o) + t * eo, final_state + c.seq0 * es, workspace, workspace_bytes,
+                            stream, kBoth);
+        if (st != KDA_OK) return st;
+        if (kda::launch_fold_status(status, kda::kFoldOr, s) != hipSuccess) return KDA_ERR_HIP;
+    }
+    return kda::launch_fold_status(status, kda::kFoldBack, s) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status_t kda_chunk_fwd_status(const void* workspace, void* stream) {

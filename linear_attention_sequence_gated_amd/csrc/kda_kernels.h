@@ -92,6 +92,9 @@ hipError_t launch_seq_order(const int32_t* cu, int32_t n, int32_t C, int32_t* or
 int range_length(int DK, int DV, int C, bool bf16, int64_t units, int64_t chunks_per_unit);
 // Clears the range status word (calls without tokens launch no intra-chunk kernel).
 hipError_t launch_clear_status(int32_t* status, hipStream_t s);
+// Folds the range status words of the calls that make up a windowed call.
+enum { kFoldClear = 0, kFoldOr = 1, kFoldBack = 2 };
+hipError_t launch_fold_status(int32_t* status, int mode, hipStream_t s);
 // C is the requested chunk size; the chunk the kernels use is
 // effective_chunk(DK, C, bf16) (fp32 operands with dk = 128 use at most 32).
 int effective_chunk(int DK, int C, bool bf16);

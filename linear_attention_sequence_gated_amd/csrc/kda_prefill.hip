@@ -2050,6 +2050,22 @@ hipError_t launch_clear_status(int32_t* status, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The range status of a call made of several calls (kda_chunk_fwd_windowed):
+// each call clears and sets word 0; word 1 collects them.  kFoldClear clears
+// word 1, kFoldOr adds word 0 to it, kFoldBack copies it to word 0.
+__global__ __launch_bounds__(64) void kda_fold_status(int32_t* status, int32_t mode) {
+    if (threadIdx.x == 0) {
+        if (mode == kFoldClear) status[1] = 0;
+        else if (mode == kFoldOr) status[1] |= status[0];
+        else status[0] = status[1];
+    }
+}
+
+hipError_t launch_fold_status(int32_t* status, int mode, hipStream_t s) {
+    hipLaunchKernelGGL(kda_fold_status, dim3(1), dim3(64), 0, s, status, (int32_t)mode);
+    return hipGetLastError();
+}
+
 hipError_t launch_chunk_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t* chunk_off, hipStream_t s) {
     hipLaunchKernelGGL(kda_chunk_offsets, dim3(1), dim3(256), 0, s, cu, n, C, 1, chunk_off, (int32_t*)nullptr);
     return hipGetLastError();

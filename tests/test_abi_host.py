@@ -238,3 +238,30 @@ def test_noalloc_rejects_before_any_launch(lib):
 def test_status_query_rejects_bad_workspace(lib):
     assert lib.kda_chunk_fwd_status(None, None) == INVALID
     assert lib.kda_chunk_fwd_status(ctypes.c_void_p(0x10010), None) == INVALID   # not 256-byte aligned
+
+
+def _windowed(lib, p, cu=None, cu_host=None, final=FAKE, init=None, ws=FAKE, ws_bytes=1 << 40, q=FAKE):
+    return lib.kda_chunk_fwd_windowed(ctypes.byref(p), q, FAKE, FAKE, FAKE, FAKE, init, cu, cu_host, FAKE, final,
+                                      ws, ws_bytes, None)
+
+
+def test_windowed_rejects_bad_arguments_before_launching(lib):
+    p = _params(seqlen=4096)
+    assert _windowed(lib, p, final=None) == INVALID              # final_state carries the state
+    assert _windowed(lib, p, final=MISALIGNED) == INVALID
+    assert _windowed(lib, p, q=MISALIGNED) == INVALID
+    assert _windowed(lib, p, init=MISALIGNED) == INVALID
+    pk = _params(seqlen=100, num_seqs=2)
+    good = (ctypes.c_int32 * 3)(0, 60, 100)
+    assert _windowed(lib, pk, cu=FAKE) == INVALID                 # device cu_seqlens without its host copy
+    assert _windowed(lib, pk, cu_host=good) == INVALID            # host copy without the device array
+    assert _windowed(lib, pk, cu=FAKE, cu_host=(ctypes.c_int32 * 3)(0, 60, 99)) == INVALID    # cu[N] != T
+    assert _windowed(lib, pk, cu=FAKE, cu_host=(ctypes.c_int32 * 3)(1, 60, 100)) == INVALID   # cu[0] != 0
+    assert _windowed(lib, pk, cu=FAKE, cu_host=(ctypes.c_int32 * 3)(0, 110, 100)) == INVALID  # decreasing
+    assert _windowed(lib, _params(batch=2, num_seqs=2, seqlen=50), cu=FAKE, cu_host=good) == INVALID
+    assert _windowed(lib, p, ws=None) == WORKSPACE
+    assert _windowed(lib, p, ws=MISALIGNED) == WORKSPACE
+    # too small for one chunk of one sequence (one block alone is ~74 KB here)
+    assert _windowed(lib, p, ws_bytes=4096) == WORKSPACE
+    assert _windowed(lib, pk, cu=FAKE, cu_host=good, ws_bytes=4096) == WORKSPACE
+    assert _windowed(lib, _params(head_dim_k=96)) == UNSUPPORTED

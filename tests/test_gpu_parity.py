@@ -893,3 +893,80 @@ def test_chunk_range_scan_resume_equals_one_pass():
     o2, S2 = gpu_prefill(second, 64)
     assert rel_err(np.concatenate([o1, o2], axis=1), o_full) < 2e-2
     assert rel_err(S2, S_full) < 2e-2
+
+
+# --- bounded-memory prefill (kda_chunk_fwd_windowed) --------------------------------
+# Whole sequences are grouped while their workspace fits; longer ones run in
+# windows of whole chunks that resume from the state the window before left.
+
+def _quote(B, T, H, dk, dv, dtype, lengths=None):
+    """kda_chunk_fwd_workspace_size of a call of that shape."""
+    Tq = T if lengths is None else sum(lengths)
+    q = torch.empty(B, Tq, H, dk, dtype=dtype, device="cuda")
+    v = torch.empty(B, Tq, H, dv, dtype=dtype, device="cuda")
+    cu = None if lengths is None else torch.zeros(len(lengths) + 1, dtype=torch.int32, device="cuda")
+    return kda.workspace_size(q, v, cu)
+
+
+def _windowed(inp, ws_bytes, chunk=64):
+    d = to_dev(inp)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    o, S = kda.chunk_fwd_windowed(d["q"], d["k"], d["v"], d["alpha"], d["beta"], ws, d["S0"], d["cu_seqlens"],
+                                  chunk_size=chunk, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), S.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,T,H,d,dtype,lengths,budget", [
+    (1, 5000, 2, 128, torch.bfloat16, None, 1500),                          # one sequence in 4 windows
+    (1, 0, 3, 64, torch.bfloat16, [0, 300, 4000, 17, 0, 900, 2500], 1024),  # groups and windows
+    (3, 700, 2, 128, torch.float32, None, 700),                             # one row per call
+    (1, 0, 1, 32, torch.bfloat16, [0, 100, 0, 70], 0),                      # one chunk per call, empty ones alone
+])
+def test_windowed_matches_oracle(B, T, H, d, dtype, lengths, budget):
+    """``budget``: the workspace quote of one row of that many tokens, or (0) room
+    for one chunk of one sequence and no more (one (chunk, head) block more than the
+    status word; an empty sequence's own packed call would need two blocks)."""
+    inp = workloads.make_inputs(B, T, H, d, d, dtype, s0_std=0.02, seed=1300 + d + H, lengths=lengths)
+    if budget:
+        ws_bytes = _quote(1, budget, H, d, d, dtype)
+    else:
+        ws_bytes = _quote(1, 128, H, d, d, dtype) - _quote(1, 64, H, d, d, dtype) + 512
+    full = _quote(B, T, H, d, d, dtype, lengths)
+    assert ws_bytes < full
+    say(f"[case] windowed B{B} T{T} H{H} d{d} {dtype} lengths={lengths} workspace {ws_bytes} of {full}")
+    og, Sg = _windowed(inp, ws_bytes)
+    oo, So = oracle_prefill(inp)
+    eo, es = rel_err(og, oo), rel_err(Sg, So)
+    say(f"    err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL[dtype] and es < TOL[dtype]
+    # and the same call in one piece
+    o1, S1 = gpu_prefill(inp, 64)
+    assert rel_err(og, o1) < TOL[dtype] and rel_err(Sg, S1) < TOL[dtype]
+
+
+def test_windowed_in_place_state():
+    inp = workloads.make_inputs(1, 3000, 2, 64, 64, torch.bfloat16, s0_std=0.02, seed=1310)
+    d = to_dev(inp)
+    S = d["S0"].clone()
+    ws = torch.empty(_quote(1, 640, 2, 64, 64, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    o, S_out = kda.chunk_fwd_windowed(d["q"], d["k"], d["v"], d["alpha"], d["beta"], ws, S, None, final_state=S,
+                                      o_dtype=torch.float32)
+    assert S_out.data_ptr() == S.data_ptr()
+    oo, So = oracle_prefill(inp)
+    assert rel_err(o.cpu().numpy(), oo) < TOL[torch.bfloat16] and rel_err(S.cpu().numpy(), So) < TOL[torch.bfloat16]
+
+
+def test_windowed_reports_a_range_error_of_an_early_window():
+    """q past the fp16 range in the first window only: that window's outputs are not
+    finite, the later windows' are, and the call still reports KDA_ERR_RANGE."""
+    inp = workloads.make_inputs(1, 1024, 2, 128, 128, torch.bfloat16, s0_std=0.02, seed=1311)
+    inp["q"][:, :64] = (inp["q"][:, :64].float() * 1e7).to(torch.bfloat16)
+    d = to_dev(inp)
+    ws = torch.empty(_quote(1, 256, 2, 128, 128, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    with pytest.raises(kda.KdaError) as e:
+        kda.chunk_fwd_windowed(d["q"], d["k"], d["v"], d["alpha"], d["beta"], ws, d["S0"], None)
+    assert e.value.status == kda.KDA_ERR_RANGE
+    o, S = kda.chunk_fwd_windowed(d["q"], d["k"], d["v"], d["alpha"], d["beta"], ws, d["S0"], None,
+                                  check_range=False)
+    assert torch.isfinite(S).all() and torch.isfinite(o[:, 256:].float()).all()
