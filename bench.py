@@ -279,7 +279,17 @@ def main():
             "tokens_per_s": round(ptok / (ms / 1e3), 1),
             "token_heads_per_s": round(ptok * wp.heads / (ms / 1e3), 1),
             "workspace_bytes": int(pp.workspace.numel())}
-        del pp, dp
+        # the same call in a 2 GiB workspace (kda_chunk_fwd_windowed: whole
+        # sequences grouped, long ones in windows resuming from their state)
+        wsw = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+        cu_host = dp["cu_seqlens"].cpu()
+        ms_w = time_call(lambda: kda.chunk_fwd_windowed(
+            dp["q"], dp["k"], dp["v"], dp["alpha"], dp["beta"], wsw, dp["S0"], dp["cu_seqlens"], o=pp.o,
+            final_state=pp.final_state, chunk_size=wp.chunk, o_dtype=torch.bfloat16, check_range=False,
+            cu_seqlens_host=cu_host), reps=3)
+        variants["prefill_packed_varlen_resume_windowed"] = {
+            "ms": round(ms_w, 4), "workspace_bytes": int(wsw.numel()), "vs_one_piece": round(ms_w / ms, 4)}
+        del pp, dp, wsw
         torch.cuda.empty_cache()
 
     # ---- decode --------------------------------------------------------------

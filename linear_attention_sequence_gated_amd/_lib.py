@@ -366,12 +366,14 @@ def chunk_fwd_noalloc(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
 
 def chunk_fwd_windowed(q, k, v, alpha, beta, workspace, initial_state=None, cu_seqlens=None, o=None,
                        final_state=None, chunk_size: int = 64, scale: float = 1.0,
-                       o_dtype: Optional[torch.dtype] = None, stream=None, check_range: bool = True):
+                       o_dtype: Optional[torch.dtype] = None, stream=None, check_range: bool = True,
+                       cu_seqlens_host=None):
     """kda_chunk_fwd_windowed: kda_chunk_fwd in the memory of ``workspace`` (a
     256-byte aligned device buffer of any size that holds one chunk's call).
 
-    Shapes and dtypes as chunk_fwd.  ``cu_seqlens`` is copied to the host here
-    (the library plans the windows from that copy; the copy synchronises).
+    Shapes and dtypes as chunk_fwd.  The library plans the windows from a host
+    copy of ``cu_seqlens``: ``cu_seqlens_host`` (a CPU int32 tensor with the same
+    values) when given, else one made here (the copy synchronises).
     ``final_state`` is allocated when not given.  Returns (o, final_state).
     """
     B, T, H, dk = q.shape
@@ -388,7 +390,15 @@ def chunk_fwd_windowed(q, k, v, alpha, beta, workspace, initial_state=None, cu_s
     if cu_seqlens is not None:
         _need(cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 2, "cu_seqlens must be int32 [N+1] with N >= 1")
         _dense(cu_seqlens, (cu_seqlens.numel(),), torch.int32, "cu_seqlens")
-        cu_host = cu_seqlens.cpu()
+        if cu_seqlens_host is None:
+            cu_host = cu_seqlens.cpu()
+        else:
+            _need(isinstance(cu_seqlens_host, torch.Tensor) and cu_seqlens_host.device.type == "cpu" and
+                  cu_seqlens_host.dtype == torch.int32 and cu_seqlens_host.is_contiguous() and
+                  cu_seqlens_host.shape == cu_seqlens.shape, "cu_seqlens_host must be a CPU int32 copy of cu_seqlens")
+            cu_host = cu_seqlens_host
+    else:
+        _need(cu_seqlens_host is None, "cu_seqlens_host must come with cu_seqlens")
     n = B if cu_seqlens is None else cu_seqlens.numel() - 1
     _dense(initial_state, (n, H, dk, dv), torch.float32, "initial_state")
     _dense(final_state, (n, H, dk, dv), torch.float32, "final_state")

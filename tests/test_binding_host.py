@@ -64,6 +64,29 @@ def test_prefill_rejects_bad_tensor(guarded, case):
         _lib.Prefill(**args, **PREFILL_BAD[case])
 
 
+WINDOWED_BAD = {
+    "workspace on the host": dict(workspace=torch.zeros(1 << 10, dtype=torch.uint8)),
+    "final_state too small": dict(final_state=_meta(B, H, DK, DV - 1, dtype=torch.float32)),
+    "initial_state on the host": dict(initial_state=torch.zeros(B, H, DK, DV)),
+    "cu_seqlens_host on the device": dict(cu_seqlens=_meta(3, dtype=torch.int32),
+                                          cu_seqlens_host=_meta(3, dtype=torch.int32)),
+    "cu_seqlens_host int64": dict(cu_seqlens=_meta(3, dtype=torch.int32), cu_seqlens_host=torch.tensor([0, 40, 96])),
+    "cu_seqlens_host short": dict(cu_seqlens=_meta(3, dtype=torch.int32),
+                                  cu_seqlens_host=torch.tensor([0, 96], dtype=torch.int32)),
+    "cu_seqlens_host alone": dict(cu_seqlens_host=torch.tensor([0, 40, 96], dtype=torch.int32)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(WINDOWED_BAD))
+def test_windowed_rejects_bad_tensor(guarded, case):
+    args = _prefill_args()
+    args["workspace"] = _meta(1 << 20, dtype=torch.uint8)
+    args.update(WINDOWED_BAD[case])
+    guarded()
+    with pytest.raises(ValueError, match=rf"^{case.split()[0]} must"):
+        _lib.chunk_fwd_windowed(**args)
+
+
 def _decode_args():
     n = 3
     return dict(q=_meta(n, H, DK), k=_meta(n, H, DK), v=_meta(n, H, DV), alpha=_meta(n, H, DK, dtype=torch.float32),
