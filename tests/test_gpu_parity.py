@@ -922,6 +922,7 @@ def _windowed(inp, ws_bytes, chunk=64):
     (1, 0, 3, 64, torch.bfloat16, [0, 300, 4000, 17, 0, 900, 2500], 1024),  # groups and windows
     (3, 700, 2, 128, torch.float32, None, 700),                             # one row per call
     (1, 0, 1, 32, torch.bfloat16, [0, 100, 0, 70], 0),                      # one chunk per call, empty ones alone
+    (1, 20000, 2, 128, torch.bfloat16, None, 9000),                         # windows that take chunk ranges
 ])
 def test_windowed_matches_oracle(B, T, H, d, dtype, lengths, budget):
     """``budget``: the workspace quote of one row of that many tokens, or (0) room
@@ -943,6 +944,28 @@ def test_windowed_matches_oracle(B, T, H, d, dtype, lengths, budget):
     # and the same call in one piece
     o1, S1 = gpu_prefill(inp, 64)
     assert rel_err(og, o1) < TOL[dtype] and rel_err(Sg, S1) < TOL[dtype]
+
+
+def test_windowed_packed_workload_matches_one_piece():
+    """The packed variable-length workload (64 sequences up to 32,768 tokens, H16,
+    nonzero initial states; device-drawn inputs) in a 2 GiB workspace against the
+    one-piece call, whose parity with the oracle test_packed_varlen_resume_every_head
+    checks on the CPU-drawn inputs."""
+    d = workloads.device_inputs(workloads.PACKED_VARLEN_RESUME, torch.device("cuda"))
+    say(f"[case] windowed packed workload {tuple(d['q'].shape)} in 2 GiB")
+    args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+    o1, S1 = kda.chunk_fwd(*args, d["S0"], d["cu_seqlens"], chunk_size=64, o_dtype=torch.float32)
+    ws = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    assert ws.numel() < kda.workspace_size(d["q"], d["v"], d["cu_seqlens"]) // 8
+    ow, Sw = kda.chunk_fwd_windowed(*args, ws, d["S0"], d["cu_seqlens"], chunk_size=64, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    eo = WholeTensorError()
+    es = WholeTensorError()
+    for h in range(o1.shape[2]):
+        eo.add(ow[:, :, h].cpu().numpy(), o1[:, :, h].cpu().numpy())
+        es.add(Sw[:, h].cpu().numpy(), S1[:, h].cpu().numpy())
+    say(f"    windowed vs one piece: o={eo.value():.3e} S={es.value():.3e}")
+    assert eo.value() < TOL[torch.bfloat16] and es.value() < TOL[torch.bfloat16]
 
 
 def test_windowed_in_place_state():
