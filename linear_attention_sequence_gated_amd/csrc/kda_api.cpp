@@ -27,7 +27,8 @@ bool head_dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace: [range status word (kWsAlign bytes)] [chunk-offset table and
+// Workspace: [range status words (kWsAlign bytes): the call's, then the one
+// kda_chunk_fwd_windowed folds its calls' words into] [chunk-offset table and
 // sequence order (packed input only)] [per (chunk, head) blocks] [chunk-range
 // scan: range-offset table (packed), range maps, range start states] [gate
 // scratch (split gated calls)].

@@ -1106,8 +1106,10 @@ __device__ __forceinline__ void load_frag(f32x4 (&q)[N], const char* base, int r
 // caps it near 1 us per chunk whatever the number of workgroups in flight.
 // Plain workgroups run two slices per compute wave (8 waves: two per SIMD).
 // Gated ones hold a chunk's outputs across the barrier that completes the
-// row norm and run one slice per wave (12 waves): 2.59 against 2.85 ms for
-// the gated long-context call, where the plain call is 0.6 % faster with two.
+// row norm and run one slice per wave (12 waves): 2.33 against 2.64 ms with
+// two for the gated long-context call (and 2.44 ms with two slices per wave
+// forming the outputs twice, once for the row sums and once to store them),
+// where the plain call is 0.6 % faster with two.
 constexpr int kRowSlices = 8;
 constexpr int kRowSlicesPerWave = 2;
 constexpr int kGatedSlicesPerWave = 1;
