@@ -56,7 +56,8 @@ typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or shape    */
-    KDA_ERR_UNSUPPORTED = 2, /* head dim, chunk size or dtype not built       */
+    KDA_ERR_UNSUPPORTED = 2, /* head dim, chunk size or dtype not built, or a */
+                             /* call beyond one dispatch (2^32 work-items)     */
     KDA_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned    */
     KDA_ERR_HIP = 4,         /* a HIP launch or runtime call failed           */
     KDA_ERR_RANGE = 5        /* the result is not finite (kda_chunk_fwd_status) */

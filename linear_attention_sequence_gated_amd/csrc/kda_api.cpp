@@ -114,6 +114,20 @@ PrefillPlan plan_prefill(const kda_chunk_params_t* p, bool packed, bool gate) {
     return pl;
 }
 
+// Every grid of a call stays below the 2^32 work-items one dispatch can
+// cover (the intra-chunk kernel has 256 threads per (chunk, head); the
+// inter-chunk and range kernels at most 1,024 per workgroup; the epilogue one
+// per four outputs).  Only calls far larger than one GPU's memory reach it.
+bool fits_dispatch(const kda_chunk_params_t* p, const PrefillPlan& pl, bool split) {
+    constexpr uint64_t kLimit = 1ull << 32;
+    const uint64_t H = (uint64_t)p->num_heads, units = (uint64_t)p->num_seqs * H, slices = p->head_dim_v / 16;
+    const uint64_t intra = (uint64_t)pl.max_chunks * H * 256;
+    const uint64_t inter = (pl.range_len > 0 ? (uint64_t)pl.max_ranges * H : (units + 7) / 8 * 8 * slices) * 1024;
+    const uint64_t scan = (units + 7) / 8 * 8 * slices * 1024;
+    const uint64_t epilogue = split ? (uint64_t)p->batch * (uint64_t)p->seqlen * H * (p->head_dim_v / 4) : 0;
+    return intra < kLimit && inter < kLimit && scan < kLimit && epilogue < kLimit;
+}
+
 // Scratch of gated calls whose norm is finished by the epilogue kernel:
 // un-normalised fp32 outputs and per-slice sums of squares.
 size_t gate_scratch_bytes(const kda_chunk_params_t* p) {
@@ -140,7 +154,9 @@ const char* kda_status_string(kda_status_t s) {
     switch (s) {
         case KDA_OK: return "KDA_OK";
         case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument (pointer, size or shape)";
-        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: head dim, chunk size or dtype not supported";
+        case KDA_ERR_UNSUPPORTED:
+            return "KDA_ERR_UNSUPPORTED: head dim, chunk size or dtype not supported, or a call larger than one "
+                   "dispatch (2^32 work-items)";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing, too small or misaligned";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch or runtime call failed";
         case KDA_ERR_RANGE:
@@ -259,6 +275,7 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
     const PrefillPlan pl = plan_prefill(p, packed, gate);
     const bool whole = pl.whole;
     const bool split = gate && !whole;
+    if (!fits_dispatch(p, pl, split)) return KDA_ERR_UNSUPPORTED;
     const size_t need = round_up(pl.total, kWsAlign) + (split ? gate_scratch_bytes(p) : 0);
     if (need > 0) {
         if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_WORKSPACE;
@@ -609,6 +626,9 @@ kda_status_t decode_impl(int32_t num_seqs, int32_t num_heads, int32_t dk, int32_
     if ((int64_t)num_seqs * num_heads > ((int64_t)1 << 31) - 1) return KDA_ERR_INVALID_ARG;
     if (!dtype_ok(qkv_dtype) || !dtype_ok(o_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    // one dispatch: (sequence, head, column block) workgroups of at most 256 threads
+    if ((uint64_t)num_seqs * num_heads * (uint64_t)(dv / kda::decode_columns(dv)) * 256 >= (1ull << 32))
+        return KDA_ERR_UNSUPPORTED;
     if (!(scale == scale)) return KDA_ERR_INVALID_ARG;
     if (!q || !k || !v || !alpha || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
     const bool scalar_alpha = op && op->alpha_mode == 1;

@@ -265,3 +265,15 @@ def test_windowed_rejects_bad_arguments_before_launching(lib):
     assert _windowed(lib, p, ws_bytes=4096) == WORKSPACE
     assert _windowed(lib, pk, cu=FAKE, cu_host=good, ws_bytes=4096) == WORKSPACE
     assert _windowed(lib, _params(head_dim_k=96)) == UNSUPPORTED
+
+
+def test_calls_beyond_one_dispatch_are_unsupported(lib):
+    """A grid of 2^32 work-items or more would wrap: such calls are refused before any launch."""
+    huge = _params(seqlen=1 << 34, num_heads=1)     # 2^28 chunks x 256 threads
+    assert lib.kda_chunk_fwd(ctypes.byref(huge), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE,
+                             1 << 62, None) == UNSUPPORTED
+    ok = _params(seqlen=1 << 20, num_heads=1)       # a plain large call passes this check (and fails later on
+    assert lib.kda_chunk_fwd(ctypes.byref(ok), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None,
+                             16, None) == WORKSPACE  # the 16-byte workspace, before any launch)
+    assert lib.kda_decode_step(1 << 20, 32, 128, 128, 1.0, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               None) == UNSUPPORTED
