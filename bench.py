@@ -60,11 +60,11 @@ KERNEL_SOURCES = {
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {  # kernel: (sources, sha256[:16] of the sources, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "kda_intra_kernel": ("prefill", "b7d8bd5a9e4e724f", 1343699.8, 2379224.4),
-    "kda_range_kernel": ("prefill", "b7d8bd5a9e4e724f", 702855.6, 30116.1),
-    "kda_range_scan_kernel": ("prefill", "b7d8bd5a9e4e724f", 14374.2, 14336.0),
-    "kda_inter_kernel": ("prefill", "b7d8bd5a9e4e724f", 1206672.0, 526406.9),
-    "kda_decode_kernel": ("decode", "cae2554d1a32d68e", 267575.8, 526414.8),
+    "kda_intra_kernel": ("prefill", "ac498df83435bc71", 1343699.6, 2379347.5),
+    "kda_range_kernel": ("prefill", "ac498df83435bc71", 702825.5, 29737.5),
+    "kda_range_scan_kernel": ("prefill", "ac498df83435bc71", 14374.2, 14336.0),
+    "kda_inter_kernel": ("prefill", "ac498df83435bc71", 1207481.2, 526419.9),
+    "kda_decode_kernel": ("decode", "cae2554d1a32d68e", 267576.0, 526419.0),
 }
 
 
