@@ -363,6 +363,39 @@ def main():
         variants["decode_paged_fused_inputs_and_gate"] = {"ms": round(ms, 4), "vs_plain": round(ms / dec_ms, 4),
                                                           "GB/s": round(state_bytes / (ms / 1e3) / 1e9, 1)}
         del pool, slots, gate
+        # one sequence (H heads, 2 MiB of state): the steps are launch-bound;
+        # the same steps issued one by one and replayed as one HIP graph
+        st1 = dd["S0"][:1].clone()
+        o1 = torch.empty((1, H0, wd.dv), dtype=torch.bfloat16, device=dev)
+
+        def step1(t):
+            kda.decode_step(dd["q"][t][:1], dd["k"][t][:1], dd["v"][t][:1], dd["alpha"][t][:1], dd["beta"][t][:1],
+                            st1, o=o1, o_dtype=torch.bfloat16)
+
+        nst = args.decode_steps
+        ms_eager = dtime(step1, reps=nst)
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gs):
+            for t in range(min(3, nst)):
+                step1(t)
+        gs.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            for t in range(nst):
+                step1(t)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_graph = e0.elapsed_time(e1) / nst
+        variants["decode_one_sequence_hip_graph"] = {
+            "heads": H0, "steps": nst, "eager_ms_per_step": round(ms_eager, 4),
+            "graph_ms_per_step": round(ms_graph, 4), "eager_over_graph": round(ms_eager / ms_graph, 2)}
+        del graph, st1, o1
     del dd, state
     torch.cuda.empty_cache()
 
