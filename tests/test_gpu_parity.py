@@ -205,6 +205,42 @@ def test_random_shapes(seed):
     check(inp, c["C"], TOL[c["dtype"]], label=f"random {c}")
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes_with_chunk_ranges(seed):
+    """Seeded random long sequences over few heads (bf16, dk = dv in {64, 128}):
+    fixed-length or packed with a long sequence among short and empty ones;
+    every case takes the chunk-range path."""
+    g = torch.Generator().manual_seed(6000 + seed)
+    ri = lambda lo, hi: int(torch.randint(lo, hi, (1,), generator=g))
+    d, H, s0 = [64, 128][ri(0, 2)], ri(1, 9), [0.0, 0.02][ri(0, 2)]
+    if ri(0, 2):
+        lens = [ri(0, 12000) if ri(0, 3) else ri(0, 200) for _ in range(ri(1, 6))]
+        lens[ri(0, len(lens))] = ri(3072, 16000)
+        B, T = 1, 0
+    else:
+        lens, B, T = None, ri(1, 3), ri(3072, 16384)
+    inp = workloads.make_inputs(B, T, H, d, d, torch.bfloat16, s0_std=s0, seed=6100 + seed, lengths=lens)
+    assert _ranged(B, T, H, d, lens)
+    check(inp, 64, TOL[torch.bfloat16], label=f"random ranges B{B} T{T} H{H} d{d} lengths={lens}")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_shapes_with_whole_rows(seed):
+    """Seeded random packs with at least as many (sequence, head) pairs as CUs:
+    whole-row workgroups, longest sequences first."""
+    g = torch.Generator().manual_seed(7000 + seed)
+    ri = lambda lo, hi: int(torch.randint(lo, hi, (1,), generator=g))
+    H = [8, 16, 32][ri(0, 3)]
+    lens = [ri(0, 700) for _ in range(256 // H + ri(1, 12))]
+    dtype = [torch.bfloat16, torch.float32][ri(0, 2)]
+    d = [64, 128][ri(0, 2)]
+    inp = workloads.make_inputs(1, 0, H, d, d, dtype, s0_std=0.02, seed=7100 + seed, lengths=lens)
+    cu = inp["cu_seqlens"].to("cuda")
+    x = torch.empty(1, sum(lens), H, d, dtype=dtype, device="cuda")
+    assert kda.chunk_plan(x, x, cu)["whole_rows"] == 1
+    check(inp, 64, TOL[dtype], label=f"random whole rows H{H} d{d} {dtype} n={len(lens)}")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_packed_ragged_with_empty_sequences(dtype):
     lens = [0, 1, 63, 64, 65, 200, 0, 129, 7]
