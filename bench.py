@@ -14,7 +14,10 @@ The line also carries the roofline of the dominant kernel (algorithmic bytes
 or flops per launch / measured average launch time, against MI355X peaks),
 the same for every kernel, the fp64 CPU oracle timed on a bounded sample of
 the workload on this host, and ("variants") the time of one call with each
-option of kda_chunk_fwd_ex / kda_decode_step_ex on the same workloads.
+option of kda_chunk_fwd_ex / kda_decode_step_ex on the same workloads, of the
+packed variable-length workload (in one piece, and in a 2 GiB workspace through
+kda_chunk_fwd_windowed) and of one sequence's decode steps issued one by one
+and replayed as one HIP graph.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
