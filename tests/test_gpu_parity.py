@@ -293,6 +293,18 @@ def test_zero_beta_is_pure_decay(dtype):
     check(_gated(dtype, lambda a: a, torch.zeros_like), 64, TOL[dtype], label="beta=0")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("scale", [1.6, -0.5])
+def test_beta_outside_unit_interval(dtype, scale):
+    """beta is taken as given (no clamp): over-relaxed (beta up to 1.6) and negative
+    update strengths, on both the factored and the exact Gram paths."""
+    g = torch.Generator().manual_seed(31)
+    fast = _gated(dtype, lambda a: a, lambda b: b * scale)
+    check(fast, 64, TOL[dtype], label=f"beta x{scale}")
+    exact = _gated(dtype, lambda a: torch.rand(a.shape, generator=g) * 0.2 + 0.05, lambda b: b * scale, seed=10)
+    check(exact, 64, TOL[dtype], label=f"beta x{scale}, fast decay")
+
+
 def test_identity_gate_keeps_state():
     inp = _gated(torch.float32, torch.ones_like, torch.zeros_like)
     og, Sg = gpu_prefill(inp, 64)
