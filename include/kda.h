@@ -127,8 +127,11 @@ kda_status_t kda_chunk_fwd_plan(const kda_chunk_params_t* params, int32_t packed
  *   cu_seqlens  [N + 1] int32 on the device, or NULL.  NULL: each of the B rows
  *               is one sequence (N == B).  Non-NULL: B == 1 and sequence n is
  *               tokens [cu[n], cu[n+1]) of the row; requires cu[0] == 0,
- *               non-decreasing, cu[N] == T.  It is not checked on the host (that
- *               would need a device-to-host copy); violating it is undefined.
+ *               non-decreasing, cu[N] == T.  The host does not read it (that
+ *               would need a device-to-host copy); the first kernel of the call
+ *               checks it on the device, and a call that breaks it reads and
+ *               writes no token (its o and final_state must not be used) and
+ *               kda_chunk_fwd_status then reports KDA_ERR_INVALID_ARG.
  *               Empty sequences are allowed: their final state is the initial one.
  *   o           [B, T, H, dv]  params->o_dtype (written for every token of every
  *               sequence)
@@ -215,13 +218,15 @@ kda_status_t kda_chunk_fwd_windowed(const kda_chunk_params_t* params,
                                     void* workspace, size_t workspace_bytes,
                                     void* stream);
 
-/* Range status of the last kda_chunk_fwd / kda_chunk_fwd_ex /
- * kda_chunk_fwd_windowed call (or _intra + _inter pair) made with `workspace`: KDA_OK when every value it
- * wrote to o, final_state and checkpoints is finite, KDA_ERR_RANGE when one
- * is not (see the range contract above).  The intra-chunk half clears the
- * status word (the first 256 bytes of the workspace) and the inter-chunk
- * half sets it, so it is read after both on the same stream.  This call
- * copies 4 bytes to the host and SYNCHRONISES `stream`.  Errors:
+/* Device-side status of the last kda_chunk_fwd / kda_chunk_fwd_ex /
+ * kda_chunk_fwd_windowed call (or _intra + _inter pair) made with
+ * `workspace`: KDA_ERR_INVALID_ARG when its cu_seqlens broke the layout that
+ * kda_chunk_fwd requires; else KDA_OK when every value it wrote to o,
+ * final_state and checkpoints is finite, KDA_ERR_RANGE when one is not (see
+ * the range contract above).  The intra-chunk half writes the status words
+ * (the first 256 bytes of the workspace) and the inter-chunk half may set the
+ * range word, so it is read after both on the same stream.  This call copies
+ * 12 bytes to the host and SYNCHRONISES `stream`.  Errors:
  * KDA_ERR_INVALID_ARG (NULL or misaligned workspace), KDA_ERR_HIP. */
 kda_status_t kda_chunk_fwd_status(const void* workspace, void* stream);
 

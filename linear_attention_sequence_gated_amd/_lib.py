@@ -21,6 +21,7 @@ KDA_DTYPE_BF16 = 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
            4: "KDA_ERR_HIP", 5: "KDA_ERR_RANGE"}
 KDA_ERR_RANGE = 5
+KDA_ERR_INVALID_ARG = 1
 
 # Every symbol include/kda.h declares.
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
@@ -270,14 +271,16 @@ class Prefill:
         return self.o, self.final_state
 
     def status(self) -> int:
-        """kda_chunk_fwd_status of the last run (synchronises the stream): 0, or KDA_ERR_RANGE."""
+        """kda_chunk_fwd_status of the last run (synchronises the stream): 0, or KDA_ERR_RANGE;
+        raises KdaError for any other status (KDA_ERR_INVALID_ARG: cu_seqlens broke its layout)."""
         st = self._lib.kda_chunk_fwd_status(self._args[10], self._args[12])
         if st not in (0, KDA_ERR_RANGE):
             _check("kda_chunk_fwd_status", st)
         return st
 
     def check_range(self):
-        """Raise KdaError(KDA_ERR_RANGE) if the last run wrote a value that is not finite."""
+        """Raise KdaError if the last run wrote a value that is not finite (KDA_ERR_RANGE)
+        or its cu_seqlens broke the layout (KDA_ERR_INVALID_ARG)."""
         _check("kda_chunk_fwd_status", self.status())
 
     def _plain_phase(self, name):
@@ -314,7 +317,8 @@ def chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, chunk_s
     alpha, beta given as logits) and ``gate`` [B,T,H,dv] with ``norm_weight`` [dv] and
     ``norm_eps`` (output norm and sigmoid gate) are the other kda_chunk_options_t fields.
     With ``check_range`` (the default) the call then reads kda_chunk_fwd_status, which
-    synchronises the stream, and raises KdaError (status KDA_ERR_RANGE) when a written
+    synchronises the stream, and raises KdaError (status KDA_ERR_INVALID_ARG) when the device
+    found cu_seqlens malformed, or (status KDA_ERR_RANGE) when a written
     value is not finite (an intermediate left the fp16 operand range of the bf16 path).
     """
     pre = Prefill(q, k, v, alpha, beta, initial_state, cu_seqlens, chunk_size, scale,

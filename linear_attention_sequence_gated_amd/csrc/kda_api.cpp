@@ -243,10 +243,14 @@ kda_status_t check_options(const kda_chunk_params_t* p, const kda_chunk_options_
     return KDA_OK;
 }
 
+// `layout_checked`: cu_seqlens holds token offsets the caller has already
+// checked (kda_chunk_fwd_windowed's groups, whose offsets do not start at 0);
+// otherwise the chunk-offset kernel checks its layout on the device.
 kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options_t* op, const void* q,
                             const void* k, const void* v, const float* alpha, const float* beta,
                             const float* initial_state, const int32_t* cu_seqlens, void* o, float* final_state,
-                            void* workspace, size_t workspace_bytes, void* stream, int phases) {
+                            void* workspace, size_t workspace_bytes, void* stream, int phases,
+                            bool layout_checked = false) {
     kda_status_t st = check_params(p);
     if (st != KDA_OK) return st;
     st = check_options(p, op, initial_state, final_state);
@@ -352,9 +356,12 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
     if (phases & kIntra) {
         if (packed) {
             int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + kStatusBytes);
+            const int64_t check_T = layout_checked ? -1 : p->seqlen;
             e = pl.range_len > 0 ? kda::launch_chunk_range_offsets(cu_seqlens, p->num_seqs, C, pl.range_len, chunk_off,
-                                                                   reinterpret_cast<int32_t*>(ws + pl.range_off), s)
-                                 : kda::launch_chunk_offsets(cu_seqlens, p->num_seqs, C, chunk_off, s);
+                                                                   reinterpret_cast<int32_t*>(ws + pl.range_off),
+                                                                   check_T, a.status, s)
+                                 : kda::launch_chunk_offsets(cu_seqlens, p->num_seqs, C, chunk_off, check_T, a.status,
+                                                             s);
             if (e != hipSuccess) return KDA_ERR_HIP;
             if (pl.seq_order) {
                 e = kda::launch_seq_order(cu_seqlens, p->num_seqs, C, seq_order, s);
@@ -565,7 +572,7 @@ kda_status_t kda_chunk_fwd_windowed(const kda_chunk_params_t* p, const void* q, 
         st = chunk_fwd_impl(&c.p, nullptr, static_cast<const char*>(q) + t * eq, static_cast<const char*>(k) + t * eq,
                             static_cast<const char*>(v) + t * ev, alpha + t * ea, beta + t * eb, s0, c.cu,
                             static_cast<char*>(o) + t * eo, final_state + c.seq0 * es, workspace, workspace_bytes,
-                            stream, kBoth);
+                            stream, kBoth, true);
         if (st != KDA_OK) return st;
         if (kda::launch_fold_status(status, kda::kFoldOr, s) != hipSuccess) return KDA_ERR_HIP;
     }
@@ -575,13 +582,14 @@ kda_status_t kda_chunk_fwd_windowed(const kda_chunk_params_t* p, const void* q, 
 kda_status_t kda_chunk_fwd_status(const void* workspace, void* stream) {
     if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_INVALID_ARG;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    int32_t flag = 0;
-    if (hipMemcpyAsync(&flag, workspace, sizeof flag, hipMemcpyDeviceToHost, s) != hipSuccess ||
+    int32_t words[kda::kLayoutWord + 1] = {};
+    if (hipMemcpyAsync(words, workspace, sizeof words, hipMemcpyDeviceToHost, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess) {
         (void)hipGetLastError();
         return KDA_ERR_HIP;
     }
-    return flag ? KDA_ERR_RANGE : KDA_OK;
+    if (words[kda::kLayoutWord]) return KDA_ERR_INVALID_ARG;   // cu_seqlens broke its layout
+    return words[0] ? KDA_ERR_RANGE : KDA_OK;
 }
 
 kda_status_t kda_chunk_fwd(const kda_chunk_params_t* p, const void* q, const void* k, const void* v,

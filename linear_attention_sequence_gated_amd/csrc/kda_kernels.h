@@ -77,10 +77,19 @@ struct DecodeArgs {
     float norm_eps;
 };
 
-hipError_t launch_chunk_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t* chunk_off, hipStream_t s);
+// Status words at the head of the workspace: [0] range status of the call,
+// [1] the running range status of a windowed call, [kLayoutWord] 1 when the
+// call's cu_seqlens broke its layout.
+constexpr int kLayoutWord = 2;
+// Chunk offsets of the packed sequences (chunk_off [n + 1]).  With T >= 0 the
+// layout of cu first is checked (cu[0] == 0, non-decreasing, cu[n] == T): a
+// broken one empties the tables and sets status[kLayoutWord]; T < 0 skips the
+// check (offsets the caller has checked).
+hipError_t launch_chunk_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t* chunk_off, int64_t T,
+                                int32_t* status, hipStream_t s);
 // Also the first range of each packed sequence (range_off [n + 1]) for ranges of L chunks.
 hipError_t launch_chunk_range_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t L, int32_t* chunk_off,
-                                      int32_t* range_off, hipStream_t s);
+                                      int32_t* range_off, int64_t T, int32_t* status, hipStream_t s);
 // Packed sequences by decreasing chunk count, ties by index (order [n]); more
 // than kSeqOrderMax sequences keep their input order.
 constexpr int kSeqOrderMax = 4096;

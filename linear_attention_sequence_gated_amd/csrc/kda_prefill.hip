@@ -101,13 +101,32 @@ __device__ __forceinline__ float alpha_at(const PrefillArgs& a, int64_t tok, int
 // ---------------------------------------------------------------------------
 // K0: exclusive prefix of ceil(len_n / C) over the packed sequences, and, for
 // the chunk-range scan (range_off non-null), of max(1, ceil(chunks_n / L)).
+// First, when T >= 0, the layout of cu_seqlens is checked: cu[0] == 0,
+// non-decreasing, cu[N] == T.  A call that breaks it gets empty tables (no
+// chunk and no range is ever located, so no token is read or written) and
+// layout status 1 (status word kLayoutWord), else 0.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void kda_chunk_offsets(const int32_t* __restrict__ cu, int32_t n_seqs,
                                                          int32_t C, int32_t L, int32_t* __restrict__ chunk_off,
-                                                         int32_t* __restrict__ range_off) {
+                                                         int32_t* __restrict__ range_off, int64_t T,
+                                                         int32_t* __restrict__ status) {
     __shared__ int32_t part[2][256];
     __shared__ int32_t carry[2];
     const int tid = threadIdx.x;
+    int bad = 0;
+    if (T >= 0) {
+        for (int n = tid; n < n_seqs; n += 256) bad |= cu[n + 1] < cu[n];
+        if (tid == 0) bad |= cu[0] != 0 || (int64_t)cu[n_seqs] != T;
+    }
+    bad = __syncthreads_or(bad);
+    if (tid == 0) status[kLayoutWord] = bad ? 1 : 0;
+    if (bad) {
+        for (int n = tid; n <= n_seqs; n += 256) {
+            chunk_off[n] = 0;
+            if (range_off) range_off[n] = 0;
+        }
+        return;   // uniform over the workgroup
+    }
     if (tid < 2) carry[tid] = 0;
     __syncthreads();
     for (int base = 0; base < n_seqs; base += 256) {
@@ -362,8 +381,13 @@ void kda_intra_kernel(const PrefillArgs a) {
     // long-context workload)
     const int x = (int)(blockIdx.x / (unsigned)a.H), h = (int)(blockIdx.x % (unsigned)a.H);
     // the call's range status starts clear; the inter-chunk kernel, which runs
-    // after this one on the stream, may set it
-    if (blockIdx.x == 0 && tid == 0) *a.status = 0;
+    // after this one on the stream, may set it.  Fixed-length calls have no
+    // cu_seqlens to check: their layout status is clear too (packed calls have
+    // theirs from the chunk-offset kernel).
+    if (blockIdx.x == 0 && tid == 0) {
+        a.status[0] = 0;
+        if (!a.cu_seqlens) a.status[kLayoutWord] = 0;
+    }
     ChunkPos pos;
     if (!locate_chunk(a, C, x, pos)) return;  // uniform over the workgroup
     const int valid = pos.valid;
@@ -2044,7 +2068,10 @@ int effective_chunk(int DK, int C, bool bf16) {
 }
 
 __global__ __launch_bounds__(64) void kda_clear_status(int32_t* status) {
-    if (threadIdx.x == 0) *status = 0;
+    if (threadIdx.x == 0) {
+        status[0] = 0;
+        status[kLayoutWord] = 0;
+    }
 }
 
 hipError_t launch_clear_status(int32_t* status, hipStream_t s) {
@@ -2068,14 +2095,16 @@ hipError_t launch_fold_status(int32_t* status, int mode, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_chunk_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t* chunk_off, hipStream_t s) {
-    hipLaunchKernelGGL(kda_chunk_offsets, dim3(1), dim3(256), 0, s, cu, n, C, 1, chunk_off, (int32_t*)nullptr);
+hipError_t launch_chunk_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t* chunk_off, int64_t T,
+                                int32_t* status, hipStream_t s) {
+    hipLaunchKernelGGL(kda_chunk_offsets, dim3(1), dim3(256), 0, s, cu, n, C, 1, chunk_off, (int32_t*)nullptr, T,
+                       status);
     return hipGetLastError();
 }
 
 hipError_t launch_chunk_range_offsets(const int32_t* cu, int32_t n, int32_t C, int32_t L, int32_t* chunk_off,
-                                      int32_t* range_off, hipStream_t s) {
-    hipLaunchKernelGGL(kda_chunk_offsets, dim3(1), dim3(256), 0, s, cu, n, C, L, chunk_off, range_off);
+                                      int32_t* range_off, int64_t T, int32_t* status, hipStream_t s) {
+    hipLaunchKernelGGL(kda_chunk_offsets, dim3(1), dim3(256), 0, s, cu, n, C, L, chunk_off, range_off, T, status);
     return hipGetLastError();
 }
 

@@ -844,6 +844,38 @@ def test_range_status_reads_clear_after_an_empty_call():
     assert pre0.status() == 0
 
 
+# --- layout check of cu_seqlens on the device ----------------------------------------
+# Each malformed array below keeps every offset inside the tensors, so even a
+# call that did not check it would read and write in bounds.
+
+@pytest.mark.parametrize("lens,bad", [
+    ([100, 40, 60], [0, 100, 60, 200]),            # decreasing
+    ([100, 40, 60], [0, 100, 150, 150]),           # cu[N] != T
+    ([100, 40, 60], [10, 100, 150, 200]),          # cu[0] != 0
+    ([5000, 4000], [0, 5000, 4500]),                # decreasing, on a shape with chunk ranges
+])
+def test_malformed_cu_seqlens_is_reported_and_writes_no_token(lens, bad):
+    inp = workloads.make_inputs(1, 0, 2, 128, 128, torch.bfloat16, s0_std=0.02, seed=1320, lengths=lens)
+    d = to_dev(inp)
+    say(f"[case] malformed cu_seqlens {bad} for lengths {lens}")
+    o = torch.full(d["v"].shape, float("nan"), dtype=torch.float32, device="cuda")
+    pre = kda.Prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                      torch.tensor(bad, dtype=torch.int32, device="cuda"), chunk_size=64, o=o,
+                      o_dtype=torch.float32)
+    pre.run()
+    with pytest.raises(kda.KdaError) as e:
+        pre.check_range()
+    assert e.value.status == kda.KDA_ERR_INVALID_ARG
+    assert torch.isnan(o).all()
+    # the well-formed call on the same workspace reads clear and matches the oracle
+    good = kda.Prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"], chunk_size=64,
+                       o_dtype=torch.float32, workspace=pre.workspace)
+    og, Sg = good.run()
+    assert good.status() == 0
+    oo, So = oracle_prefill(inp)
+    assert rel_err(og.cpu().numpy(), oo) < TOL[torch.bfloat16] and rel_err(Sg.cpu().numpy(), So) < TOL[torch.bfloat16]
+
+
 # --- chunk-range scan (few (sequence, head) pairs, long sequences) -----------------
 # With fewer pairs than CUs and at least three 16-chunk ranges per sequence the
 # inter-chunk pass forms each range's map, scans the ranges' start states and
