@@ -343,8 +343,8 @@ typedef struct {
      * pool [P, H, dk, dv] fp32 and sequence n reads and updates pool entry
      * state_slots[n] in place (the unified paged pool that holds the KDA
      * states, "Kimi K3 architecture: KDA, MLA and MoE", section "Serving K3
-     * means managing two cache lifecycles").  Slots must lie in [0, P) and be
-     * distinct within a call; they are device data and are not checked. */
+     * means managing two cache lifecycles").  Slots must be distinct within a
+     * call (device data, not checked); see pool_entries for their range. */
     const int32_t* state_slots;
     /* Floored decay: alpha values below decay_floor are raised to it (0: no
      * floor), applied after the sigmoid of fuse_inputs. */
@@ -366,11 +366,17 @@ typedef struct {
     const void* gate;
     const float* norm_weight;
     float norm_eps;
+    /* P, the entries of the state pool (state_slots given), or 0.  When > 0 a
+     * slot outside [0, P) is checked on the device and not used: that
+     * sequence's state is not touched and its o is written as NaN (in every
+     * head).  0 leaves the slots unchecked (they must then lie in [0, P)). */
+    int32_t pool_entries;
 } kda_decode_options_t;
 
 /* kda_decode_step with the options above (NULL options = kda_decode_step).
  * Errors as kda_decode_step, plus KDA_ERR_INVALID_ARG for bad option values
- * (a negative or NaN floor or eps, misaligned pointers). */
+ * (a negative or NaN floor or eps, a negative pool_entries, misaligned
+ * pointers). */
 kda_status_t kda_decode_step_ex(int32_t num_seqs, int32_t num_heads,
                                 int32_t head_dim_k, int32_t head_dim_v,
                                 float scale, int32_t qkv_dtype, int32_t o_dtype,

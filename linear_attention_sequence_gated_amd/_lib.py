@@ -62,7 +62,7 @@ class DecodeOptions(ctypes.Structure):
     """kda_decode_options_t (include/kda.h); zero-filled = the plain step."""
     _fields_ = [("state_slots", ctypes.c_void_p), ("decay_floor", ctypes.c_float), ("alpha_mode", ctypes.c_int32),
                 ("fuse_inputs", ctypes.c_int32), ("gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
-                ("norm_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("pool_entries", ctypes.c_int32)]
 
 
 _lib = None
@@ -428,12 +428,13 @@ def chunk_fwd_windowed(q, k, v, alpha, beta, workspace, initial_state=None, cu_s
 def decode_step(q, k, v, alpha, beta, state, scale: float = 1.0, o=None, stream=None,
                 o_dtype: Optional[torch.dtype] = None, state_slots=None, decay_floor: float = 0.0,
                 alpha_scalar: bool = False, fuse_inputs: bool = False, gate=None, norm_weight=None,
-                norm_eps: float = 0.0):
+                norm_eps: float = 0.0, pool_entries: Optional[int] = None):
     """One decode step through kda_decode_step (or kda_decode_step_ex with any option).
 
     q, k [N,H,dk], alpha [N,H,dk] ([N,H] with ``alpha_scalar``), v [N,H,dv], beta [N,H];
     ``state`` [N,H,dk,dv] is updated in place, or with ``state_slots`` (int32 [N] device)
-    it is a pool [P,H,dk,dv] and sequence n updates entry state_slots[n].  Options as in
+    it is a pool [P,H,dk,dv] and sequence n updates entry state_slots[n]; a slot outside
+    [0, pool_entries) (default P) is skipped on the device and gives o = NaN.  Options as in
     include/kda.h: ``decay_floor``, ``fuse_inputs`` (L2 norm of q, k; alpha, beta logits),
     ``gate`` [N,H,dv] logits with ``norm_weight`` [dv] and ``norm_eps``.
     Returns o [N,H,dv] (``o_dtype``, default the dtype of q).
@@ -467,7 +468,11 @@ def decode_step(q, k, v, alpha, beta, state, scale: float = 1.0, o=None, stream=
             and norm_weight is None):
         _check("kda_decode_step", lib.kda_decode_step(*head, *tail))
     else:
+        if state_slots is not None:
+            pool_entries = state.shape[0] if pool_entries is None else int(pool_entries)
+            _need(0 < pool_entries <= state.shape[0], "pool_entries must lie in [1, P]")
         opt = DecodeOptions(state_slots=None if state_slots is None else state_slots.data_ptr(),
+                            pool_entries=0 if state_slots is None else pool_entries,
                             decay_floor=float(decay_floor), alpha_mode=int(bool(alpha_scalar)),
                             fuse_inputs=int(bool(fuse_inputs)), gate=None if gate is None else gate.data_ptr(),
                             norm_weight=None if norm_weight is None else norm_weight.data_ptr(),

@@ -648,6 +648,7 @@ kda_status_t decode_impl(int32_t num_seqs, int32_t num_heads, int32_t dk, int32_
         if (op->alpha_mode != 0 && op->alpha_mode != 1) return KDA_ERR_INVALID_ARG;
         if (op->fuse_inputs != 0 && op->fuse_inputs != 1) return KDA_ERR_INVALID_ARG;
         if (op->state_slots && !aligned(op->state_slots, 4)) return KDA_ERR_INVALID_ARG;
+        if (op->pool_entries < 0) return KDA_ERR_INVALID_ARG;
         if (op->gate && !aligned(op->gate, qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4)) return KDA_ERR_INVALID_ARG;
         if (op->norm_weight && !aligned(op->norm_weight, 4)) return KDA_ERR_INVALID_ARG;
         if (op->norm_weight && !op->gate) return KDA_ERR_INVALID_ARG;
@@ -667,6 +668,7 @@ kda_status_t decode_impl(int32_t num_seqs, int32_t num_heads, int32_t dk, int32_
     a.o_f32 = o_dtype == KDA_DTYPE_F32;
     if (op) {
         a.slots = op->state_slots;
+        a.pool_entries = op->pool_entries;
         a.alpha_floor = op->decay_floor;
         a.alpha_scalar = op->alpha_mode;
         a.fuse_inputs = op->fuse_inputs;

@@ -58,7 +58,18 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void kda_decode_kernel(c
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cg = tid % CG, r0 = tid / CG;
     // state of this (sequence, head): its own, or a pool entry
-    const int64_t sidx = a.slots ? (int64_t)a.slots[unit / a.H] * a.H + unit % a.H : (int64_t)unit;
+    const int slot = a.slots ? a.slots[unit / a.H] : 0;
+    if (a.slots && a.pool_entries > 0 && (slot < 0 || slot >= a.pool_entries)) {
+        // a slot outside the pool: no state is touched, o reads NaN (uniform over the workgroup)
+        if (r0 == 0) {
+            const f32x4 nan4 = zero4() + __builtin_nanf("");
+            const int64_t oi = (int64_t)unit * DV + col0 + 4 * cg;
+            if (a.o_f32) store4(reinterpret_cast<float*>(a.o) + oi, nan4);
+            else store4(reinterpret_cast<__bf16*>(a.o) + oi, nan4);
+        }
+        return;
+    }
+    const int64_t sidx = a.slots ? (int64_t)slot * a.H + unit % a.H : (int64_t)unit;
     float* __restrict__ S = a.state + sidx * DK * DV + col0;
 
     // state rows of this thread: issue every load before anything else

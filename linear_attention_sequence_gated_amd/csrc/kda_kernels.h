@@ -69,6 +69,7 @@ struct DecodeArgs {
     float scale;
     int32_t o_f32;               // 1: o is fp32, 0: o is bf16
     const int32_t* slots;        // [N] pool entries of the states, or null (state n * H + h)
+    int32_t pool_entries;        // > 0: slots outside [0, pool_entries) are skipped (o = NaN)
     float alpha_floor;           // alpha = max(alpha, floor); 0 leaves it as is
     int32_t alpha_scalar;        // alpha [N, H]
     int32_t fuse_inputs;         // L2 norm of q, k; sigmoid of alpha, beta logits

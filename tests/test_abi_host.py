@@ -218,6 +218,7 @@ def test_decode_step_ex_rejects_bad_options_before_launch(lib):
     assert call(Opt(alpha_mode=2)) == INVALID
     assert call(Opt(fuse_inputs=3)) == INVALID
     assert call(Opt(state_slots=0x30002)) == INVALID                 # misaligned slots
+    assert call(Opt(state_slots=0x30000, pool_entries=-1)) == INVALID  # a pool of negative size
     assert call(Opt(norm_weight=0x30000)) == INVALID                 # a norm weight needs a gate
     assert call(Opt(), alpha=MISALIGNED) == INVALID                  # per-channel alpha: 16-byte aligned
     assert call(Opt(alpha_mode=1), alpha=ctypes.c_void_p(0x10003)) == INVALID

@@ -527,6 +527,39 @@ def test_decode_paged_state_pool(dtype):
     assert eo < TOL[dtype] and es < TOL[dtype]
 
 
+@pytest.mark.parametrize("gated", [False, True])
+def test_decode_slot_outside_the_pool_is_skipped(gated):
+    """A slot outside [0, P) is caught on the device: that sequence's o reads NaN and no
+    state is touched; the other sequences step as usual.  The pool tensor has one
+    padding entry beyond the P entries declared, so even an unchecked step would stay
+    inside the allocation (slot P is that padding entry)."""
+    N, H, d, P = 3, 2, 128, 4
+    g = torch.Generator().manual_seed(330)
+    q = torch.nn.functional.normalize(torch.randn(N, H, d, generator=g), dim=-1).to(torch.bfloat16)
+    k = torch.nn.functional.normalize(torch.randn(N, H, d, generator=g), dim=-1).to(torch.bfloat16)
+    v = torch.nn.functional.silu(torch.randn(N, H, d, generator=g)).to(torch.bfloat16)
+    alpha = torch.sigmoid(torch.randn(N, H, d, generator=g) + 3.0)
+    beta = torch.sigmoid(torch.randn(N, H, generator=g))
+    gate = torch.randn(N, H, d, generator=g).to(torch.bfloat16) if gated else None
+    pool0 = 0.02 * torch.randn(P + 1, H, d, d, generator=g)
+    slots = [2, P, 0]                          # sequence 1 points past the declared pool
+    say(f"[case] decode slot outside the pool, gated={gated}")
+    pool = pool0.cuda()
+    o = kda.decode_step(q.cuda(), k.cuda(), v.cuda(), alpha.cuda(), beta.cuda(), pool, o_dtype=torch.float32,
+                        state_slots=torch.tensor(slots, dtype=torch.int32, device="cuda"), pool_entries=P,
+                        gate=None if gate is None else gate.cuda(), norm_eps=1e-5 if gated else 0.0)
+    torch.cuda.synchronize()
+    o, pool = o.cpu(), pool.cpu()
+    assert torch.isnan(o[1]).all() and torch.isfinite(o[[0, 2]]).all()
+    assert torch.equal(pool[[1, 3, P]], pool0[[1, 3, P]])       # unused and padding entries untouched
+    good = [0, 2]
+    oo, So = kda_oracle.decode(pool0[[slots[n] for n in good]], q[None, good], k[None, good], v[None, good],
+                               alpha[None, good], beta[None, good], gate=None if gate is None else gate[None, good],
+                               norm_eps=1e-5 if gated else 0.0)
+    assert rel_err(o[good].numpy(), oo[0]) < TOL[torch.bfloat16]
+    assert rel_err(pool[[slots[n] for n in good]].numpy(), So) < TOL[torch.bfloat16]
+
+
 DECODE_OPTS = [
     {"decay_floor": 0.97},
     {"alpha_scalar": True},
