@@ -63,11 +63,11 @@ KERNEL_SOURCES = {
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {  # kernel: (sources, sha256[:16] of the sources, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "kda_intra_kernel": ("prefill", "ac498df83435bc71", 1343699.6, 2379347.5),
-    "kda_range_kernel": ("prefill", "ac498df83435bc71", 702825.5, 29737.5),
-    "kda_range_scan_kernel": ("prefill", "ac498df83435bc71", 14374.2, 14336.0),
-    "kda_inter_kernel": ("prefill", "ac498df83435bc71", 1207481.2, 526419.9),
-    "kda_decode_kernel": ("decode", "cae2554d1a32d68e", 267576.0, 526419.0),
+    "kda_intra_kernel": ("prefill", "70cc7a22baa70465", 1343691.0, 2379468.0),
+    "kda_range_kernel": ("prefill", "70cc7a22baa70465", 702850.3, 31092.5),
+    "kda_range_scan_kernel": ("prefill", "70cc7a22baa70465", 14367.7, 14336.0),
+    "kda_inter_kernel": ("prefill", "70cc7a22baa70465", 1205925.3, 526420.9),
+    "kda_decode_kernel": ("decode", "36ee23fa6ad7684f", 267578.4, 526416.9),
 }
 
 
