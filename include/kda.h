@@ -21,7 +21,7 @@
  *
  * Conventions shared by every entry point:
  *  - Every tensor argument is a DEVICE pointer owned by the caller (the one
- *    host array is kda_chunk_fwd_windowed's copy of cu_seqlens).  The
+ *    host array is kda_chunk_fwd_windowed(_ex)'s copy of cu_seqlens).  The
  *    library allocates no device memory, keeps no pointer after returning and
  *    takes scratch only through the caller's workspace; the one exception is
  *    kda_chunk_fwd_noalloc, whose scratch is a fixed device array the
@@ -219,7 +219,7 @@ kda_status_t kda_chunk_fwd_windowed(const kda_chunk_params_t* params,
                                     void* stream);
 
 /* Device-side status of the last kda_chunk_fwd / kda_chunk_fwd_ex /
- * kda_chunk_fwd_windowed call (or _intra + _inter pair) made with
+ * kda_chunk_fwd_windowed(_ex) call (or _intra + _inter pair) made with
  * `workspace`: KDA_ERR_INVALID_ARG when its cu_seqlens broke the layout that
  * kda_chunk_fwd requires; else KDA_OK when every value it wrote to o,
  * final_state and checkpoints is finite, KDA_ERR_RANGE when one is not (see
@@ -320,6 +320,28 @@ kda_status_t kda_chunk_fwd_ex(const kda_chunk_params_t* params, const kda_chunk_
                               void* o, float* final_state,
                               void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* kda_chunk_fwd_windowed with the options of kda_chunk_fwd_ex (NULL options =
+ * kda_chunk_fwd_windowed): the gated, fused-input layer of "Kimi K3
+ * Architecture Teardown" (Visual 1, the KDA inset) in bounded memory.  Each
+ * call of the split takes the rows of gate and alpha of its tokens; a
+ * call's quote is kda_chunk_fwd_ex_workspace_size of its own shape (with the
+ * gate's epilogue scratch where that shape takes it).  With checkpoints, a
+ * sequence that does not fit alone runs in windows of whole checkpoint
+ * intervals (multiples of ckpt_every tokens), so every window writes its
+ * checkpoints into its sequence's slots, as the one-piece call does; the
+ * workspace must then hold a call of one sequence of ckpt_every tokens (else
+ * KDA_ERR_WORKSPACE).  Option values are checked on the whole call before
+ * anything is launched; errors as kda_chunk_fwd_windowed plus those of
+ * kda_chunk_fwd_ex's options. */
+kda_status_t kda_chunk_fwd_windowed_ex(const kda_chunk_params_t* params, const kda_chunk_options_t* options,
+                                       const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* beta,
+                                       const float* initial_state, const int32_t* cu_seqlens,
+                                       const int32_t* cu_seqlens_host,
+                                       void* o, float* final_state,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* stream);
 
 /* One decode step: every (sequence, head) consumes a single token and its
  * state is updated in place.

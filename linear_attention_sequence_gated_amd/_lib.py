@@ -27,7 +27,7 @@ KDA_ERR_INVALID_ARG = 1
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
             "kda_chunk_fwd_inter", "kda_chunk_fwd_ex", "kda_chunk_fwd_ex_workspace_size", "kda_decode_step",
             "kda_decode_step_ex", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_status", "kda_chunk_fwd_plan",
-            "kda_chunk_fwd_windowed")
+            "kda_chunk_fwd_windowed", "kda_chunk_fwd_windowed_ex")
 # Bytes of the library-held scratch of kda_chunk_fwd_noalloc (KDA_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -106,6 +106,9 @@ def load() -> ctypes.CDLL:
     lib.kda_chunk_fwd_windowed.restype = ctypes.c_int
     lib.kda_chunk_fwd_windowed.argtypes = [ctypes.POINTER(ChunkParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                            sz, vp]
+    lib.kda_chunk_fwd_windowed_ex.restype = ctypes.c_int
+    lib.kda_chunk_fwd_windowed_ex.argtypes = [ctypes.POINTER(ChunkParams), ctypes.POINTER(ChunkOptions),
+                                              vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_step_ex.restype = ctypes.c_int
@@ -189,6 +192,35 @@ def chunk_plan(q: torch.Tensor, v: torch.Tensor, cu_seqlens=None, chunk_size: in
     return {name: getattr(out, name) for name, _ in ChunkPlan._fields_}
 
 
+def _check_options(q, v, n, checkpoints, ckpt_every, gate, norm_weight) -> None:
+    """Shapes of the option tensors of a prefill call with N = n sequences."""
+    _, _, H, dk = q.shape
+    dv = v.shape[-1]
+    if ckpt_every:
+        _need(checkpoints is not None and checkpoints.dim() == 5 and checkpoints.shape[0] == n
+              and checkpoints.shape[2:] == (H, dk, dv) and checkpoints.dtype == torch.float32
+              and _on_device(checkpoints) and checkpoints.is_contiguous(),
+              "checkpoints must be fp32 [N, max_ckpts, H, dk, dv]")
+    _dense(gate, v.shape, q.dtype, "gate")
+    _dense(norm_weight, (v.shape[-1],), torch.float32, "norm_weight")
+
+
+def _chunk_options(checkpoints, ckpt_every, decay_floor, alpha_scalar, fuse_inputs, gate, norm_weight,
+                   norm_eps) -> Optional[ChunkOptions]:
+    """kda_chunk_options_t of the keyword options (None: the plain call)."""
+    if not (ckpt_every or decay_floor or alpha_scalar or fuse_inputs or gate is not None
+            or norm_weight is not None):
+        return None
+    return ChunkOptions(checkpoints=checkpoints.data_ptr() if ckpt_every else None,
+                        ckpt_every=int(ckpt_every),
+                        max_ckpts=checkpoints.shape[1] if ckpt_every else 0,
+                        decay_floor=float(decay_floor), alpha_mode=int(bool(alpha_scalar)),
+                        fuse_inputs=int(bool(fuse_inputs)),
+                        gate=None if gate is None else gate.data_ptr(),
+                        norm_weight=None if norm_weight is None else norm_weight.data_ptr(),
+                        norm_eps=float(norm_eps))
+
+
 class Prefill:
     """A kda_chunk_fwd call with its arguments marshalled once.
 
@@ -223,13 +255,7 @@ class Prefill:
         _dense(final_state, (n, H, dk, dv), torch.float32, "final_state")
         o_dtype = q.dtype if o_dtype is None else o_dtype
         _dense(o, v.shape, o_dtype, "o")
-        if ckpt_every:
-            _need(checkpoints is not None and checkpoints.dim() == 5 and checkpoints.shape[0] == n
-                  and checkpoints.shape[2:] == (H, dk, dv) and checkpoints.dtype == torch.float32
-                  and _on_device(checkpoints) and checkpoints.is_contiguous(),
-                  "checkpoints must be fp32 [N, max_ckpts, H, dk, dv]")
-        _dense(gate, v.shape, q.dtype, "gate")
-        _dense(norm_weight, (dv,), torch.float32, "norm_weight")
+        _check_options(q, v, n, checkpoints, ckpt_every, gate, norm_weight)
         # every check above precedes the first allocation
         if o is None:
             o = torch.empty(v.shape, dtype=o_dtype, device=v.device)
@@ -237,17 +263,9 @@ class Prefill:
             final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
         self.params = chunk_params(q, v, cu_seqlens, chunk_size, scale, o_dtype)
         self.o, self.final_state = o, final_state
-        self.options = None
         self.checkpoints = checkpoints
-        if ckpt_every or decay_floor or alpha_scalar or fuse_inputs or gate is not None or norm_weight is not None:
-            self.options = ChunkOptions(checkpoints=checkpoints.data_ptr() if ckpt_every else None,
-                                        ckpt_every=int(ckpt_every),
-                                        max_ckpts=checkpoints.shape[1] if ckpt_every else 0,
-                                        decay_floor=float(decay_floor), alpha_mode=int(bool(alpha_scalar)),
-                                        fuse_inputs=int(bool(fuse_inputs)),
-                                        gate=None if gate is None else gate.data_ptr(),
-                                        norm_weight=None if norm_weight is None else norm_weight.data_ptr(),
-                                        norm_eps=float(norm_eps))
+        self.options = _chunk_options(checkpoints, ckpt_every, decay_floor, alpha_scalar, fuse_inputs, gate,
+                                      norm_weight, norm_eps)
         out = ctypes.c_size_t(0)
         _check("kda_chunk_fwd_ex_workspace_size",
                load().kda_chunk_fwd_ex_workspace_size(ctypes.byref(self.params),
@@ -371,18 +389,25 @@ def chunk_fwd_noalloc(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
 def chunk_fwd_windowed(q, k, v, alpha, beta, workspace, initial_state=None, cu_seqlens=None, o=None,
                        final_state=None, chunk_size: int = 64, scale: float = 1.0,
                        o_dtype: Optional[torch.dtype] = None, stream=None, check_range: bool = True,
-                       cu_seqlens_host=None):
-    """kda_chunk_fwd_windowed: kda_chunk_fwd in the memory of ``workspace`` (a
-    256-byte aligned device buffer of any size that holds one chunk's call).
+                       cu_seqlens_host=None, checkpoints=None, ckpt_every: int = 0, decay_floor: float = 0.0,
+                       alpha_scalar: bool = False, fuse_inputs: bool = False, gate=None, norm_weight=None,
+                       norm_eps: float = 0.0):
+    """kda_chunk_fwd_windowed(_ex): kda_chunk_fwd(_ex) in the memory of ``workspace`` (a
+    256-byte aligned device buffer of any size that holds one chunk's call, or one
+    of ``ckpt_every`` tokens with checkpoints).
 
-    Shapes and dtypes as chunk_fwd.  The library plans the windows from a host
-    copy of ``cu_seqlens``: ``cu_seqlens_host`` (a CPU int32 tensor with the same
-    values) when given, else one made here (the copy synchronises).
-    ``final_state`` is allocated when not given.  Returns (o, final_state).
+    Shapes, dtypes and the options (``checkpoints`` ... ``norm_eps``) as chunk_fwd;
+    with any option set the call goes through kda_chunk_fwd_windowed_ex.  The
+    library plans the windows from a host copy of ``cu_seqlens``:
+    ``cu_seqlens_host`` (a CPU int32 tensor with the same values) when given,
+    else one made here (the copy synchronises).  ``final_state`` is allocated
+    when not given.  Returns (o, final_state).
     """
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    _need(k.shape == q.shape and alpha.shape == q.shape, "q, k, alpha must share [B,T,H,dk]")
+    _need(k.shape == q.shape, "q and k must share [B,T,H,dk]")
+    _need(alpha.shape == ((B, T, H) if alpha_scalar else q.shape),
+          "alpha must be [B,T,H,dk] ([B,T,H] with alpha_scalar)")
     _need(v.shape == (B, T, H, dv) and beta.shape == (B, T, H), "v/beta shapes")
     _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
     _need(alpha.dtype == torch.float32 and beta.dtype == torch.float32, "alpha, beta must be fp32")
@@ -408,18 +433,23 @@ def chunk_fwd_windowed(q, k, v, alpha, beta, workspace, initial_state=None, cu_s
     _dense(final_state, (n, H, dk, dv), torch.float32, "final_state")
     o_dtype = q.dtype if o_dtype is None else o_dtype
     _dense(o, v.shape, o_dtype, "o")
+    _check_options(q, v, n, checkpoints, ckpt_every, gate, norm_weight)
     if o is None:
         o = torch.empty(v.shape, dtype=o_dtype, device=v.device)
     if final_state is None:
         final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
     params = chunk_params(q, v, cu_seqlens, chunk_size, scale, o_dtype)
+    options = _chunk_options(checkpoints, ckpt_every, decay_floor, alpha_scalar, fuse_inputs, gate, norm_weight,
+                             norm_eps)
     lib = load()
-    _check("kda_chunk_fwd_windowed",
-           lib.kda_chunk_fwd_windowed(ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                                      _ptr(initial_state), _ptr(cu_seqlens),
-                                      None if cu_host is None else cu_host.data_ptr(), _ptr(o), _ptr(final_state),
-                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                      _stream(stream)))
+    rest = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+            None if cu_host is None else cu_host.data_ptr(), _ptr(o), _ptr(final_state), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if options is None:
+        _check("kda_chunk_fwd_windowed", lib.kda_chunk_fwd_windowed(ctypes.byref(params), *rest))
+    else:
+        _check("kda_chunk_fwd_windowed_ex",
+               lib.kda_chunk_fwd_windowed_ex(ctypes.byref(params), ctypes.byref(options), *rest))
     if check_range:
         _check("kda_chunk_fwd_status", lib.kda_chunk_fwd_status(_ptr(workspace), _stream(stream)))
     return o, final_state

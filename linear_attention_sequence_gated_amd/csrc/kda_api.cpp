@@ -244,13 +244,14 @@ kda_status_t check_options(const kda_chunk_params_t* p, const kda_chunk_options_
 }
 
 // `layout_checked`: cu_seqlens holds token offsets the caller has already
-// checked (kda_chunk_fwd_windowed's groups, whose offsets do not start at 0);
-// otherwise the chunk-offset kernel checks its layout on the device.
+// checked (kda_chunk_fwd_windowed's groups, whose offsets start at
+// `tok_base`, the value of cu_seqlens[0]); otherwise the chunk-offset kernel
+// checks its layout on the device and tok_base is 0.
 kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options_t* op, const void* q,
                             const void* k, const void* v, const float* alpha, const float* beta,
                             const float* initial_state, const int32_t* cu_seqlens, void* o, float* final_state,
                             void* workspace, size_t workspace_bytes, void* stream, int phases,
-                            bool layout_checked = false) {
+                            bool layout_checked = false, int64_t tok_base = 0) {
     kda_status_t st = check_params(p);
     if (st != KDA_OK) return st;
     st = check_options(p, op, initial_state, final_state);
@@ -344,13 +345,28 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
         a.range_start = reinterpret_cast<float*>(ws + pl.range_start);
     }
     const int64_t rows = (int64_t)p->batch * p->seqlen * p->num_heads;
-    if (split) {
-        a.gate_split = 1;
-        a.o_scratch = reinterpret_cast<float*>(ws + round_up(pl.total, kWsAlign));
-        a.part_scratch = reinterpret_cast<float*>(reinterpret_cast<char*>(a.o_scratch) +
-                                                  round_up((size_t)rows * p->head_dim_v * 4, kWsAlign));
-    }
     const bool bf16 = p->qkv_dtype == KDA_DTYPE_BF16;
+    // The split gate's scratch holds the call's rows (token * H + head) from
+    // row 0, while the inter-chunk kernel indexes rows by the token offsets of
+    // cu_seqlens: with offsets starting at tok_base the kernel gets scratch
+    // pointers moved back by tok_base tokens (every row it touches lands in the
+    // scratch), and the epilogue, which counts rows from 0, gets o and the gate
+    // moved forward by tok_base tokens.
+    kda::PrefillArgs ep{};
+    if (split) {
+        float* const o_scr = reinterpret_cast<float*>(ws + round_up(pl.total, kWsAlign));
+        float* const part = reinterpret_cast<float*>(reinterpret_cast<char*>(o_scr) +
+                                                     round_up((size_t)rows * p->head_dim_v * 4, kWsAlign));
+        const uint64_t back = (uint64_t)tok_base * (uint64_t)p->num_heads;   // rows before the call's first
+        a.gate_split = 1;
+        a.o_scratch = reinterpret_cast<float*>(reinterpret_cast<uintptr_t>(o_scr) - back * p->head_dim_v * 4);
+        a.part_scratch = reinterpret_cast<float*>(reinterpret_cast<uintptr_t>(part) - back * (p->head_dim_v / 16) * 4);
+        ep = a;
+        ep.o_scratch = o_scr;
+        ep.part_scratch = part;
+        ep.o = static_cast<char*>(o) + back * p->head_dim_v * (p->o_dtype == KDA_DTYPE_BF16 ? 2 : 4);
+        ep.gate = static_cast<const char*>(op->gate) + back * p->head_dim_v * (bf16 ? 2 : 4);
+    }
 
     hipError_t e = hipSuccess;
     if (phases & kIntra) {
@@ -378,7 +394,7 @@ kda_status_t chunk_fwd_impl(const kda_chunk_params_t* p, const kda_chunk_options
         e = kda::launch_inter(a, p->head_dim_k, C, bf16, s);
         if (e != hipSuccess) return KDA_ERR_HIP;
         if (split) {
-            e = kda::launch_gate_epilogue(a, rows, bf16, s);
+            e = kda::launch_gate_epilogue(ep, rows, bf16, s);
             if (e != hipSuccess) return KDA_ERR_HIP;
         }
     }
@@ -437,62 +453,65 @@ kda_status_t kda_chunk_fwd_noalloc(const kda_chunk_params_t* p, const void* q, c
 namespace {
 
 // One call of a windowed prefill: a shape, where its token pointers start,
-// its cu_seqlens (device, absolute token offsets) or none, its first sequence
-// and whether it resumes from final_state.
+// its cu_seqlens (device, absolute token offsets) or none, its first sequence,
+// the token of that sequence it starts at and whether it resumes from
+// final_state.
 struct SubCall {
     kda_chunk_params_t p;
     int64_t tok;
     const int32_t* cu;
     int64_t seq0;
+    int64_t t0;
     bool resume;
 };
 
-size_t plain_quote(const kda_chunk_params_t& sp, bool packed) {
-    return round_up(plan_prefill(&sp, packed, false).total, kWsAlign);
+// Workspace of one call in one layout (the gate's epilogue scratch included
+// where the shape takes it).
+size_t call_quote(const kda_chunk_params_t& sp, bool packed, bool gate) {
+    const PrefillPlan pl = plan_prefill(&sp, packed, gate);
+    return round_up(pl.total, kWsAlign) + (gate && !pl.whole ? gate_scratch_bytes(&sp) : 0);
 }
 
 // Cuts a run of `len` tokens of one sequence (starting at token `tok` of the
-// flattened token axis) into windows of whole chunks that fit `bytes`; each
-// window after the first resumes from the state the one before left.  An
-// empty sequence is one call without tokens (its final state is the initial
-// one).
-kda_status_t plan_windows(const kda_chunk_params_t* p, int64_t tok, int64_t len, int64_t seq, size_t bytes,
-                          std::vector<SubCall>& calls) {
+// flattened token axis) into windows of whole multiples of `step` chunks that
+// fit `bytes`; each window after the first resumes from the state the one
+// before left.  An empty sequence is one call without tokens (its final state
+// is the initial one).
+kda_status_t plan_windows(const kda_chunk_params_t* p, bool gate, int64_t step, int64_t tok, int64_t len,
+                          int64_t seq, size_t bytes, std::vector<SubCall>& calls) {
     kda_chunk_params_t w = *p;
     w.batch = 1;
     w.num_seqs = 1;
     if (len == 0) {
         w.seqlen = 0;
-        if (plain_quote(w, false) > bytes) return KDA_ERR_WORKSPACE;
-        calls.push_back({w, tok, nullptr, seq, false});
+        if (call_quote(w, false, gate) > bytes) return KDA_ERR_WORKSPACE;
+        calls.push_back({w, tok, nullptr, seq, 0, false});
         return KDA_OK;
     }
-    const int64_t C = chunk_of(p);
-    auto fits = [&](int64_t m) {
-        w.seqlen = m * C;
-        return plain_quote(w, false) <= bytes;
+    const int64_t C = chunk_of(p), padded = (len + C - 1) / C * C;
+    auto fits = [&](int64_t m) {   // m windows' worth of `step` chunks
+        w.seqlen = std::min(m * step * C, padded);
+        return call_quote(w, false, gate) <= bytes;
     };
     if (!fits(1)) return KDA_ERR_WORKSPACE;
-    int64_t lo = 1, hi = (len + C - 1) / C;   // the largest chunk count that fits
+    int64_t lo = 1, hi = (padded / C + step - 1) / step;   // the largest multiple that fits
     while (lo < hi) {
         const int64_t mid = lo + (hi - lo + 1) / 2;
         if (fits(mid)) lo = mid; else hi = mid - 1;
     }
-    for (int64_t t0 = 0; t0 < len; t0 += lo * C) {
-        w.seqlen = std::min(lo * C, len - t0);
-        calls.push_back({w, tok + t0, nullptr, seq, t0 > 0});
+    const int64_t span = lo * step * C;
+    for (int64_t t0 = 0; t0 < len; t0 += span) {
+        w.seqlen = std::min(span, len - t0);
+        calls.push_back({w, tok + t0, nullptr, seq, t0, t0 > 0});
     }
     return KDA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-kda_status_t kda_chunk_fwd_windowed(const kda_chunk_params_t* p, const void* q, const void* k, const void* v,
-                                    const float* alpha, const float* beta, const float* initial_state,
-                                    const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, void* o,
-                                    float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+kda_status_t chunk_fwd_windowed_impl(const kda_chunk_params_t* p, const kda_chunk_options_t* op, const void* q,
+                                     const void* k, const void* v, const float* alpha, const float* beta,
+                                     const float* initial_state, const int32_t* cu_seqlens,
+                                     const int32_t* cu_seqlens_host, void* o, float* final_state, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
     kda_status_t st = check_params(p);
     if (st != KDA_OK) return st;
     const bool packed = cu_seqlens != nullptr;
@@ -505,12 +524,20 @@ kda_status_t kda_chunk_fwd_windowed(const kda_chunk_params_t* p, const void* q, 
         const size_t sb = (size_t)p->num_seqs * p->num_heads * p->head_dim_k * p->head_dim_v * sizeof(float);
         if (overlaps(initial_state, sb, final_state, sb)) return KDA_ERR_INVALID_ARG;
     }
+    // the options are checked on the whole call: each call below takes a
+    // slice of the gate, alpha and checkpoint arrays, which keeps their
+    // alignment and stays clear of the states
+    st = check_options(p, op, initial_state, final_state);
+    if (st != KDA_OK) return st;
+    const bool scalar_alpha = op && op->alpha_mode == 1;
+    const bool gate = op && op->gate;
+    const bool ckpt = op && op->ckpt_every > 0;
     // every window's pointers keep the alignment of the call's (a token's row
     // is a multiple of 32 bytes), so checking them here covers every window
     if (p->seqlen > 0) {
         if (!q || !k || !v || !alpha || !beta || !o) return KDA_ERR_INVALID_ARG;
-        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(alpha, 16) ||
-            !aligned(beta, 4))
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+            !aligned(alpha, scalar_alpha ? 4 : 16) || !aligned(beta, 4))
             return KDA_ERR_INVALID_ARG;
     }
     if (packed && !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARG;
@@ -523,7 +550,10 @@ kda_status_t kda_chunk_fwd_windowed(const kda_chunk_params_t* p, const void* q, 
     }
     // Plan every call before launching any: whole sequences (rows) are grouped
     // while their quote fits, a sequence that does not fit alone runs in
-    // windows of whole chunks.
+    // windows of whole chunks.  With checkpoints a window holds whole
+    // checkpoint intervals, so that its checkpoints are slots of its
+    // sequence's row.
+    const int64_t step = ckpt ? op->ckpt_every / chunk_of(p) : 1;
     std::vector<SubCall> calls;
     int64_t n0 = 0;
     while (n0 < N) {
@@ -543,17 +573,17 @@ kda_status_t kda_chunk_fwd_windowed(const kda_chunk_params_t* p, const void* q, 
             int64_t lo = n0, hi = N;
             while (lo < hi) {
                 const int64_t mid = lo + (hi - lo + 1) / 2;
-                if (plain_quote(group(mid), packed) <= workspace_bytes) lo = mid; else hi = mid - 1;
+                if (call_quote(group(mid), packed, gate) <= workspace_bytes) lo = mid; else hi = mid - 1;
             }
             n1 = lo;
         }
         if (n1 > n0) {
-            calls.push_back({group(n1), packed ? 0 : n0 * T, packed ? cu_seqlens + n0 : nullptr, n0, false});
+            calls.push_back({group(n1), packed ? 0 : n0 * T, packed ? cu_seqlens + n0 : nullptr, n0, 0, false});
             n0 = n1;
         } else {
             const int64_t tok = packed ? cu_seqlens_host[n0] : n0 * T;
             const int64_t len = packed ? (int64_t)cu_seqlens_host[n0 + 1] - cu_seqlens_host[n0] : T;
-            st = plan_windows(p, tok, len, n0, workspace_bytes, calls);
+            st = plan_windows(p, gate, step, tok, len, n0, workspace_bytes, calls);
             if (st != KDA_OK) return st;
             ++n0;
         }
@@ -561,22 +591,62 @@ kda_status_t kda_chunk_fwd_windowed(const kda_chunk_params_t* p, const void* q, 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     int32_t* status = reinterpret_cast<int32_t*>(workspace);
     if (kda::launch_fold_status(status, kda::kFoldClear, s) != hipSuccess) return KDA_ERR_HIP;
-    const size_t eq = (size_t)p->num_heads * p->head_dim_k * (p->qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4);
-    const size_t ev = (size_t)p->num_heads * p->head_dim_v * (p->qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4);
+    const size_t in_bytes = p->qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    const size_t eq = (size_t)p->num_heads * p->head_dim_k * in_bytes;
+    const size_t ev = (size_t)p->num_heads * p->head_dim_v * in_bytes;   // also the gate's row
     const size_t eo = (size_t)p->num_heads * p->head_dim_v * (p->o_dtype == KDA_DTYPE_BF16 ? 2 : 4);
-    const size_t ea = (size_t)p->num_heads * p->head_dim_k, eb = (size_t)p->num_heads;   // floats per token
-    const size_t es = (size_t)p->num_heads * p->head_dim_k * p->head_dim_v;              // floats per state
+    const size_t ea = (size_t)p->num_heads * (scalar_alpha ? 1 : p->head_dim_k), eb = (size_t)p->num_heads;
+    const size_t es = (size_t)p->num_heads * p->head_dim_k * p->head_dim_v;   // floats per state
     for (const SubCall& c : calls) {
         const size_t t = (size_t)c.tok;
+        kda_chunk_options_t so{};
+        if (op) {
+            so = *op;
+            if (gate) so.gate = static_cast<const char*>(op->gate) + t * ev;
+            if (ckpt) {   // checkpoint j of this call is slot c.t0 / every + j of its sequence
+                const int64_t k0 = c.t0 / op->ckpt_every;
+                if (k0 < op->max_ckpts) {
+                    so.checkpoints = op->checkpoints + ((size_t)c.seq0 * op->max_ckpts + (size_t)k0) * es;
+                    so.max_ckpts = op->max_ckpts - (int32_t)k0;
+                } else {   // past the last slot: nothing to write
+                    so.checkpoints = nullptr;
+                    so.ckpt_every = 0;
+                    so.max_ckpts = 0;
+                }
+            }
+        }
         const float* s0 = c.resume ? final_state + c.seq0 * es : initial_state ? initial_state + c.seq0 * es : nullptr;
-        st = chunk_fwd_impl(&c.p, nullptr, static_cast<const char*>(q) + t * eq, static_cast<const char*>(k) + t * eq,
-                            static_cast<const char*>(v) + t * ev, alpha + t * ea, beta + t * eb, s0, c.cu,
-                            static_cast<char*>(o) + t * eo, final_state + c.seq0 * es, workspace, workspace_bytes,
-                            stream, kBoth, true);
+        // a packed group keeps the call's token pointers and its absolute offsets
+        const int64_t tok_base = c.cu ? cu_seqlens_host[c.seq0] : 0;
+        st = chunk_fwd_impl(&c.p, op ? &so : nullptr, static_cast<const char*>(q) + t * eq,
+                            static_cast<const char*>(k) + t * eq, static_cast<const char*>(v) + t * ev,
+                            alpha + t * ea, beta + t * eb, s0, c.cu, static_cast<char*>(o) + t * eo,
+                            final_state + c.seq0 * es, workspace, workspace_bytes, stream, kBoth, true, tok_base);
         if (st != KDA_OK) return st;
         if (kda::launch_fold_status(status, kda::kFoldOr, s) != hipSuccess) return KDA_ERR_HIP;
     }
     return kda::launch_fold_status(status, kda::kFoldBack, s) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_fwd_windowed(const kda_chunk_params_t* p, const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta, const float* initial_state,
+                                    const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, void* o,
+                                    float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+    return chunk_fwd_windowed_impl(p, nullptr, q, k, v, alpha, beta, initial_state, cu_seqlens, cu_seqlens_host,
+                                   o, final_state, workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_fwd_windowed_ex(const kda_chunk_params_t* p, const kda_chunk_options_t* options,
+                                       const void* q, const void* k, const void* v, const float* alpha,
+                                       const float* beta, const float* initial_state, const int32_t* cu_seqlens,
+                                       const int32_t* cu_seqlens_host, void* o, float* final_state,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+    return chunk_fwd_windowed_impl(p, options, q, k, v, alpha, beta, initial_state, cu_seqlens, cu_seqlens_host,
+                                   o, final_state, workspace, workspace_bytes, stream);
 }
 
 kda_status_t kda_chunk_fwd_status(const void* workspace, void* stream) {

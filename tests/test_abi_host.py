@@ -268,6 +268,32 @@ def test_windowed_rejects_bad_arguments_before_launching(lib):
     assert _windowed(lib, _params(head_dim_k=96)) == UNSUPPORTED
 
 
+def _windowed_ex(lib, p, opt, ws_bytes=1 << 40, alpha=FAKE, final=FAKE):
+    return lib.kda_chunk_fwd_windowed_ex(ctypes.byref(p), ctypes.byref(opt), FAKE, FAKE, FAKE, alpha, FAKE, None,
+                                         None, None, FAKE, final, FAKE, ws_bytes, None)
+
+
+def test_windowed_ex_rejects_bad_options_before_launching(lib):
+    p = _params(seqlen=4096)
+    Opt = kda.ChunkOptions
+    ck = ctypes.c_void_p(0x200000)
+    assert _windowed_ex(lib, p, Opt(checkpoints=ck.value, ckpt_every=100, max_ckpts=2)) == INVALID
+    assert _windowed_ex(lib, p, Opt(checkpoints=ck.value, ckpt_every=64, max_ckpts=0)) == INVALID
+    assert _windowed_ex(lib, p, Opt(checkpoints=ck.value, ckpt_every=64, max_ckpts=1),
+                        final=ctypes.c_void_p(ck.value + 256)) == INVALID        # overlaps the states
+    assert _windowed_ex(lib, p, Opt(gate=0x10001)) == INVALID                    # misaligned gate
+    assert _windowed_ex(lib, p, Opt(norm_weight=FAKE.value)) == INVALID          # a norm weight needs a gate
+    assert _windowed_ex(lib, p, Opt(decay_floor=float("nan"))) == INVALID
+    assert _windowed_ex(lib, p, Opt(alpha_mode=0), alpha=ctypes.c_void_p(0x10004)) == INVALID   # per channel: 16 B
+    # with checkpoints a window holds a whole interval: a workspace that fits
+    # 512 tokens of one sequence cannot take a window of 1,024
+    st, row512 = _ws(lib, _params(seqlen=512))
+    assert st == OK
+    assert _windowed_ex(lib, p, Opt(checkpoints=ck.value, ckpt_every=1024, max_ckpts=4),
+                        ws_bytes=row512) == WORKSPACE
+    assert _windowed_ex(lib, p, Opt(gate=FAKE.value), ws_bytes=4096) == WORKSPACE
+
+
 def test_calls_beyond_one_dispatch_are_unsupported(lib):
     """A grid of 2^32 work-items or more would wrap: such calls are refused before any launch."""
     huge = _params(seqlen=1 << 34, num_heads=1)     # 2^28 chunks x 256 threads

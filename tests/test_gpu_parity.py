@@ -1106,3 +1106,66 @@ def test_windowed_reports_a_range_error_of_an_early_window():
     o, S = kda.chunk_fwd_windowed(d["q"], d["k"], d["v"], d["alpha"], d["beta"], ws, d["S0"], None,
                                   check_range=False)
     assert torch.isfinite(S).all() and torch.isfinite(o[:, 256:].float()).all()
+
+
+# kda_chunk_fwd_windowed_ex: the options in bounded memory.  Each call of the
+# split takes its tokens' rows of gate and alpha; with checkpoints the windows
+# hold whole intervals and write into their sequence's slots.
+
+WINDOWED_OPTS = [
+    # (B, T, lengths, dk, dv, dtype, budget tokens, options, ckpt_every, max_ckpts, gated)
+    (1, 0, [0, 300, 2000, 17, 900], 128, 128, torch.bfloat16, 700,
+     {"fuse_inputs": True, "alpha_scalar": True, "decay_floor": 0.5}, 0, 0, True),
+    (1, 3000, None, 128, 64, torch.bfloat16, 600, {}, 256, 8, False),        # slots run out at token 2048
+    (1, 0, [100, 1500, 300, 0, 700], 64, 64, torch.bfloat16, 500, {"fuse_inputs": True}, 128, 6, True),
+    (3, 700, None, 128, 128, torch.float32, 700, {"alpha_scalar": True}, 64, 12, True),
+]
+
+
+@pytest.mark.parametrize("B,T,lengths,dk,dv,dtype,budget,opts,every,mx,gated", WINDOWED_OPTS)
+def test_windowed_with_options_matches_oracle(B, T, lengths, dk, dv, dtype, budget, opts, every, mx, gated):
+    H = 2
+    inp = _prefill_opts_inputs(B, T, H, dk, dv, dtype, seed=1320 + budget, lengths=lengths, **opts)
+    n = B if lengths is None else len(lengths)
+    g = torch.Generator().manual_seed(1321 + budget)
+    extra = {}
+    if gated:
+        extra = {"gate": torch.randn(inp["v"].shape, generator=g).to(dtype),
+                 "norm_weight": torch.rand(dv, generator=g) + 0.5, "norm_eps": 1e-5}
+    ws_bytes = _quote(1, budget, H, dk, dv, dtype)
+    assert ws_bytes < _quote(B, T, H, dk, dv, dtype, lengths)
+    say(f"[case] windowed options B{B} T{T} lengths={lengths} dk{dk} dv{dv} {dtype} {opts} every={every} "
+        f"max={mx} gated={gated} workspace {ws_bytes}")
+    d = to_dev(inp)
+    dev_extra = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in extra.items()}
+    ck = ckw = None
+    if every:
+        ck = torch.full((n, mx, H, dk, dv), float("nan"), device="cuda")
+        ckw = torch.full((n, mx, H, dk, dv), float("nan"), device="cuda")
+    args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    ow, Sw = kda.chunk_fwd_windowed(*args, ws, d["S0"], d["cu_seqlens"], o_dtype=torch.float32, checkpoints=ckw,
+                                    ckpt_every=every, **opts, **dev_extra)
+    o1, S1 = kda.chunk_fwd(*args, d["S0"], d["cu_seqlens"], o_dtype=torch.float32, checkpoints=ck,
+                           ckpt_every=every, **opts, **dev_extra)
+    torch.cuda.synchronize()
+    cu = inp["cu_seqlens"]
+    res = kda_oracle.forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0=inp["S0"],
+                             cu_seqlens=None if cu is None else cu.to(torch.int64), ckpt_every=every,
+                             max_ckpts=mx, return_ckpt=bool(every), **opts, **extra)
+    oo, So = res[0], res[1]
+    tol = TOL[dtype]
+    eo, es = rel_err(ow.cpu().numpy(), oo), rel_err(Sw.cpu().numpy(), So)
+    eo1, es1 = rel_err(ow.cpu().numpy(), o1.cpu().numpy()), rel_err(Sw.cpu().numpy(), S1.cpu().numpy())
+    say(f"    vs oracle o={eo:.3e} S={es:.3e}; vs one piece o={eo1:.3e} S={es1:.3e} (tol {tol})")
+    assert eo < tol and es < tol and eo1 < tol and es1 < tol
+    if every:
+        cko = res[2]
+        ckg, ck1 = ckw.cpu().numpy(), ck.cpu().numpy()
+        written = ~np.isnan(cko).all(axis=(2, 3, 4))
+        assert written.any()
+        assert np.array_equal(~np.isnan(ckg).all(axis=(2, 3, 4)), written)   # the same slots, the rest untouched
+        worst = max(rel_err(ckg[a, b], cko[a, b]) for a, b in zip(*np.nonzero(written)))
+        worst1 = max(rel_err(ckg[a, b], ck1[a, b]) for a, b in zip(*np.nonzero(written)))
+        say(f"    {int(written.sum())} checkpoints: vs oracle {worst:.3e}, vs one piece {worst1:.3e}")
+        assert worst < tol and worst1 < tol
