@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstring>
 #include <vector>
 
 #include "kda_kernels.h"
@@ -151,7 +152,11 @@ size_t base_workspace(const kda_chunk_params_t* p, bool gate) {
 extern "C" {
 
 const char* kda_status_string(kda_status_t s) {
-    switch (s) {
+    // a C caller may pass any int: its bits are read as one, since a value
+    // outside the enumerators' range is not a valid kda_status_t in C++
+    int code = 0;
+    std::memcpy(&code, &s, sizeof code);
+    switch (code) {
         case KDA_OK: return "KDA_OK";
         case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument (pointer, size or shape)";
         case KDA_ERR_UNSUPPORTED:
