@@ -15,9 +15,10 @@ or flops per launch / measured average launch time, against MI355X peaks),
 the same for every kernel, the fp64 CPU oracle timed on a bounded sample of
 the workload on this host, and ("variants") the time of one call with each
 option of kda_chunk_fwd_ex / kda_decode_step_ex on the same workloads, of the
-packed variable-length workload (in one piece, and in a 2 GiB workspace through
-kda_chunk_fwd_windowed) and of one sequence's decode steps issued one by one
-and replayed as one HIP graph.
+gated layer with fused inputs in a 1 GiB workspace (kda_chunk_fwd_windowed_ex),
+of the packed variable-length workload (in one piece, and in a 2 GiB workspace
+through kda_chunk_fwd_windowed) and of one sequence's decode steps issued one by
+one and replayed as one HIP graph.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -257,6 +258,16 @@ def main():
         argsf = (d["q"], d["k"], d["v"], al, bl, d["S0"], d["cu_seqlens"])
         ms = time_variant(argsf, fuse_inputs=True, gate=gate, norm_weight=wn, norm_eps=1e-5)
         variants["prefill_fused_inputs_and_gate"] = {"ms": round(ms, 4), "vs_plain": round(ms / plain_ms, 4)}
+        # the same gated layer in a 1 GiB workspace (kda_chunk_fwd_windowed_ex:
+        # the sequence runs in windows that resume from the state)
+        wsg = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        ms_g = time_call(lambda: kda.chunk_fwd_windowed(
+            d["q"], d["k"], d["v"], al, bl, wsg, d["S0"], d["cu_seqlens"], o=pre.o, final_state=pre.final_state,
+            chunk_size=w.chunk, o_dtype=torch.bfloat16, check_range=False, fuse_inputs=True, gate=gate,
+            norm_weight=wn, norm_eps=1e-5))
+        variants["prefill_fused_inputs_and_gate_windowed"] = {
+            "ms": round(ms_g, 4), "workspace_bytes": int(wsg.numel()), "vs_one_piece": round(ms_g / ms, 4)}
+        del wsg
         a_s = d["alpha"][..., 0].contiguous()
         argss = (d["q"], d["k"], d["v"], a_s, d["beta"], d["S0"], d["cu_seqlens"])
         ms = time_variant(argss, alpha_scalar=True)
