@@ -989,6 +989,68 @@ def test_chunk_range_scan_with_input_options(opts):
     _prefill_opts_check(inp, 64, TOL[torch.bfloat16], f"ranges packed {lens}", **opts)
 
 
+# Long memory.  With decays drawn per token as sigmoid(N(3..4, 1)) a state
+# forgets where it started within about a thousand tokens: the A part of a
+# range map, A = prod (diag(gamma) - Kbar^T W), falls far below fp32
+# resolution and a ranged call equals sequential calls bit for bit, so those
+# inputs cannot tell a wrong A from a right one.  Here alpha = sigmoid(N(8, 1))
+# (1 - alpha ~ 3e-4) and beta is scaled by 0.1, so a range's start state still
+# moves the outputs two ranges (2,048 tokens) later by more than 10 % of their
+# RMS (asserted on the oracle first): the maps' A and the scan's A S carry it.
+
+def _long_memory_inputs(B, T, H, d, seed, lengths=None):
+    inp = workloads.make_inputs(B, T, H, d, d, torch.bfloat16, alpha_mu=8.0, s0_std=0.05, seed=seed,
+                                lengths=lengths)
+    inp["beta"] = inp["beta"] * 0.1
+    return inp
+
+
+def _assert_long_memory(inp, row_tokens):
+    """Row 0's last 1,024 outputs change by > 10 % of their RMS when the state
+    3,072 tokens before the end is replaced by zeros (oracle only)."""
+    names = ("q", "k", "v", "alpha", "beta")
+    cut = row_tokens - 3072
+    head = {n: inp[n][:1, :cut] for n in names}
+    tail = {n: inp[n][:1, cut:row_tokens] for n in names}
+    s0 = None if inp["S0"] is None else inp["S0"][:1]
+    _, S_cut = kda_oracle.forward(*(head[n] for n in names), S0=s0)
+    o_true, _ = kda_oracle.forward(*(tail[n] for n in names), S0=S_cut)
+    o_zero, _ = kda_oracle.forward(*(tail[n] for n in names), S0=None)
+    moved = rel_err(o_zero[:, -1024:], o_true[:, -1024:])
+    say(f"    dropping the state 3,072 tokens before the end moves the last 1,024 outputs by {moved:.3f} of RMS")
+    assert moved > 0.1
+
+
+@pytest.mark.parametrize("B,T,H,d,lengths", [
+    (1, 16384, 2, 128, None),                        # 16 ranges of 16 chunks
+    (2, 8192, 2, 64, None),
+    (1, 0, 2, 128, [9000, 0, 7000, 1, 3072]),
+])
+def test_chunk_ranges_with_long_memory(B, T, H, d, lengths):
+    inp = _long_memory_inputs(B, T, H, d, seed=1130 + d + (T or 1), lengths=lengths)
+    assert _ranged(B, T, H, d, lengths)
+    _assert_long_memory(inp, T if lengths is None else lengths[0])
+    check(inp, 64, TOL[torch.bfloat16], label=f"long memory B{B} T{T} H{H} d{d} lengths={lengths}")
+
+
+def test_chunk_ranges_with_long_memory_gated():
+    inp = _long_memory_inputs(1, 16384, 2, 128, seed=1140)
+    assert _ranged(1, 16384, 2, 128)
+    _gate_case(inp, 64, TOL[torch.bfloat16], "long memory B1 T16384 H2")
+
+
+def test_chunk_ranges_with_long_memory_windowed():
+    # windows of about 5,000 tokens, each cut into ranges, resume from the
+    # state the window before left
+    inp = _long_memory_inputs(1, 16384, 2, 128, seed=1141)
+    ws_bytes = _quote(1, 5000, 2, 128, 128, torch.bfloat16)
+    og, Sg = _windowed(inp, ws_bytes)
+    oo, So = oracle_prefill(inp)
+    eo, es = rel_err(og, oo), rel_err(Sg, So)
+    say(f"[case] long memory windowed: err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16]
+
+
 def test_chunk_range_scan_dk64_packed_with_checkpoints():
     inp = workloads.make_inputs(1, 0, 3, 64, 64, torch.bfloat16, s0_std=0.02, seed=1125, lengths=[5000, 1, 4096])
     assert _ranged(1, 0, 3, 64, [5000, 1, 4096])
@@ -1119,6 +1181,8 @@ WINDOWED_OPTS = [
     (1, 3000, None, 128, 64, torch.bfloat16, 600, {}, 256, 8, False),        # slots run out at token 2048
     (1, 0, [100, 1500, 300, 0, 700], 64, 64, torch.bfloat16, 500, {"fuse_inputs": True}, 128, 6, True),
     (3, 700, None, 128, 128, torch.float32, 700, {"alpha_scalar": True}, 64, 12, True),
+    # windows of 8,192 tokens that take chunk ranges and the gated ranged walk
+    (1, 20000, None, 128, 128, torch.bfloat16, 9000, {"fuse_inputs": True}, 4096, 4, True),
 ]
 
 
