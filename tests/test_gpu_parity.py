@@ -998,26 +998,27 @@ def test_chunk_range_scan_with_input_options(opts):
 # moves the outputs two ranges (2,048 tokens) later by more than 10 % of their
 # RMS (asserted on the oracle first): the maps' A and the scan's A S carry it.
 
-def _long_memory_inputs(B, T, H, d, seed, lengths=None):
-    inp = workloads.make_inputs(B, T, H, d, d, torch.bfloat16, alpha_mu=8.0, s0_std=0.05, seed=seed,
+def _long_memory_inputs(B, T, H, d, seed, lengths=None, alpha_mu=8.0, beta_scale=0.1):
+    inp = workloads.make_inputs(B, T, H, d, d, torch.bfloat16, alpha_mu=alpha_mu, s0_std=0.05, seed=seed,
                                 lengths=lengths)
-    inp["beta"] = inp["beta"] * 0.1
+    inp["beta"] = inp["beta"] * beta_scale
     return inp
 
 
-def _assert_long_memory(inp, row_tokens):
-    """Row 0's last 1,024 outputs change by > 10 % of their RMS when the state
-    3,072 tokens before the end is replaced by zeros (oracle only)."""
+def _assert_long_memory(inp, row_tokens, span=1024):
+    """Row 0's last `span` outputs change by > 10 % of their RMS when the state
+    3 `span` tokens before the end is replaced by zeros (oracle only)."""
     names = ("q", "k", "v", "alpha", "beta")
-    cut = row_tokens - 3072
+    cut = row_tokens - 3 * span
     head = {n: inp[n][:1, :cut] for n in names}
     tail = {n: inp[n][:1, cut:row_tokens] for n in names}
     s0 = None if inp["S0"] is None else inp["S0"][:1]
     _, S_cut = kda_oracle.forward(*(head[n] for n in names), S0=s0)
     o_true, _ = kda_oracle.forward(*(tail[n] for n in names), S0=S_cut)
     o_zero, _ = kda_oracle.forward(*(tail[n] for n in names), S0=None)
-    moved = rel_err(o_zero[:, -1024:], o_true[:, -1024:])
-    say(f"    dropping the state 3,072 tokens before the end moves the last 1,024 outputs by {moved:.3f} of RMS")
+    moved = rel_err(o_zero[:, -span:], o_true[:, -span:])
+    say(f"    dropping the state {3 * span} tokens before the end moves the last {span} outputs by "
+        f"{moved:.3f} of RMS")
     assert moved > 0.1
 
 
@@ -1031,6 +1032,19 @@ def test_chunk_ranges_with_long_memory(B, T, H, d, lengths):
     assert _ranged(B, T, H, d, lengths)
     _assert_long_memory(inp, T if lengths is None else lengths[0])
     check(inp, 64, TOL[torch.bfloat16], label=f"long memory B{B} T{T} H{H} d{d} lengths={lengths}")
+
+
+@pytest.mark.timeout(900)
+def test_long_context_shape_with_long_memory_every_head():
+    """B1 H32 T65536 (8 ranges of 128 chunks per head) with alpha = sigmoid(N(10, 1))
+    and beta scaled by 0.01: a range's start state still moves the outputs two
+    ranges (16,384 tokens) later; all 32 heads against the oracle."""
+    say("[case] long-context shape, long memory: generating inputs")
+    inp = _long_memory_inputs(1, 65536, 32, 128, seed=1150, alpha_mu=10.0, beta_scale=0.01)
+    assert _ranged(1, 65536, 32, 128)
+    _assert_long_memory(inp, 65536, span=8192)
+    eo, es = whole_prefill_parity(inp, 64, 16, "long-context shape, long memory")
+    assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16], (eo, es)
 
 
 def test_chunk_ranges_with_long_memory_gated():
