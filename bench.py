@@ -17,8 +17,9 @@ the workload on this host, and ("variants") the time of one call with each
 option of kda_chunk_fwd_ex / kda_decode_step_ex on the same workloads, of the
 gated layer with fused inputs in a 1 GiB workspace (kda_chunk_fwd_windowed_ex),
 of the packed variable-length workload (in one piece, and in a 2 GiB workspace
-through kda_chunk_fwd_windowed) and of one sequence's decode steps issued one by
-one and replayed as one HIP graph.
+through kda_chunk_fwd_windowed), of one 2^20-token sequence over the same 32
+heads, and of one sequence's decode steps issued one by one and replayed as one
+HIP graph.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -304,6 +305,20 @@ def main():
         variants["prefill_packed_varlen_resume_windowed"] = {
             "ms": round(ms_w, 4), "workspace_bytes": int(wsw.numel()), "vs_one_piece": round(ms_w / ms, 4)}
         del pp, dp, wsw
+        torch.cuda.empty_cache()
+        # one sequence of 2^20 tokens over the long-context heads (the
+        # million-token context), drawn on the device with the same recipe
+        log("generating a 2^20-token sequence on the device")
+        dm = workloads.device_shape_inputs(1 << 20, w.heads, w.dk, w.dv, w.dtype, dev, alpha_mu=w.alpha_mu, seed=11)
+        pm = kda.Prefill(dm["q"], dm["k"], dm["v"], dm["alpha"], dm["beta"], None, None, chunk_size=w.chunk,
+                         o_dtype=torch.bfloat16)
+        ms = time_call(pm.run, reps=3)
+        variants["prefill_one_million_tokens"] = {
+            "ms": round(ms, 4), "tokens": 1 << 20, "heads": w.heads,
+            "tokens_per_s": round((1 << 20) / (ms / 1e3), 1),
+            "vs_long_context_per_token": round((ms / (1 << 20)) / (plain_ms / w.seqlen), 4),
+            "workspace_bytes": int(pm.workspace.numel())}
+        del pm, dm
         torch.cuda.empty_cache()
 
     # ---- decode --------------------------------------------------------------

@@ -120,6 +120,35 @@ def test_packed_varlen_resume_every_head():
     assert eo < TOL[w.dtype] and es < TOL[w.dtype], (eo, es)
 
 
+@pytest.mark.timeout(900)
+def test_one_million_token_sequence_sampled_heads():
+    """One sequence of 2^20 tokens over 32 heads (the pages' million-token
+    context; q holds 2^32 values, so flattened indices pass 32 bits), drawn on
+    the device with the long-context recipe and S0 ~ N(0, 0.02): the call takes
+    8 chunk ranges of 2,048 chunks per head.  Heads 0 and 31 (the lowest and
+    highest offsets) against the oracle over every token, o and final state."""
+    T, H, d = 1 << 20, 32, 128
+    say("[case] one sequence of 2^20 tokens, H32: drawing inputs on the device")
+    dd = workloads.device_shape_inputs(T, H, d, d, torch.bfloat16, "cuda", alpha_mu=4.0, s0_std=0.02, seed=1170)
+    plan = kda.chunk_plan(dd["q"], dd["v"])
+    assert plan["range_chunks"] == 2048, plan
+    o, S = kda.chunk_fwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], dd["S0"], None, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    sample = [0, H - 1]
+    inp = {n: dd[n][:, :, sample].contiguous().cpu() for n in ("q", "k", "v", "alpha", "beta")}
+    inp["S0"] = dd["S0"][:, sample].contiguous().cpu()
+    inp["cu_seqlens"] = None
+    og = o[:, :, sample].contiguous().cpu().numpy()
+    Sg = S[:, sample].contiguous().cpu().numpy()
+    del dd, o, S
+    torch.cuda.empty_cache()
+    say("[case] one sequence of 2^20 tokens: oracle on heads 0 and 31")
+    oo, So = oracle_prefill(inp)
+    eo, es = rel_err(og, oo), rel_err(Sg, So)
+    say(f"    heads 0, 31 over 2^20 tokens: err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16], (eo, es)
+
+
 def _decode_run(inp, steps, scale=1.0, o_dtype=torch.float32):
     d = to_dev(inp)
     state = d["S0"].clone()

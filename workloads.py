@@ -237,3 +237,30 @@ def device_inputs(index: int, device, seed_offset: int = 7000):
     return {"q": q, "k": k, "v": v, "alpha": alpha, "beta": beta, "S0": s0,
             "cu_seqlens": None if cu is None else cu.to(torch.int32).to(device)}
 
+
+
+def device_shape_inputs(seqlen: int, heads: int, dk: int, dv: int, dtype: torch.dtype, device,
+                        alpha_mu: float = 4.0, s0_std: float = 0.0, seed: int = 0, slab: int = 65536):
+    """One sequence (B = 1) of the recipe above drawn directly on ``device``, slab
+    by slab of ``slab`` tokens so that the fp32 draws stay small next to the
+    result (a million-token sequence over 32 heads holds 2^32 values per q).
+    Values come from a device generator seeded with ``seed``."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    q = torch.empty(1, seqlen, heads, dk, dtype=dtype, device=device)
+    k = torch.empty_like(q)
+    v = torch.empty(1, seqlen, heads, dv, dtype=dtype, device=device)
+    alpha = torch.empty(1, seqlen, heads, dk, dtype=torch.float32, device=device)
+    beta = torch.empty(1, seqlen, heads, dtype=torch.float32, device=device)
+    for t0 in range(0, seqlen, slab):
+        n = min(slab, seqlen - t0)
+        for dst in (q, k):
+            x = torch.randn(1, n, heads, dk, generator=g, device=device)
+            dst[:, t0:t0 + n] = (x / x.norm(dim=-1, keepdim=True).clamp_min(1e-12)).to(dtype)
+        v[:, t0:t0 + n] = torch.nn.functional.silu(torch.randn(1, n, heads, dv, generator=g, device=device)).to(dtype)
+        alpha[:, t0:t0 + n] = torch.sigmoid(torch.randn(1, n, heads, dk, generator=g, device=device) + alpha_mu)
+        beta[:, t0:t0 + n] = torch.sigmoid(torch.randn(1, n, heads, generator=g, device=device))
+    s0 = None
+    if s0_std > 0.0:
+        s0 = torch.randn(1, heads, dk, dv, generator=g, device=device) * s0_std
+    return {"q": q, "k": k, "v": v, "alpha": alpha, "beta": beta, "S0": s0, "cu_seqlens": None}
