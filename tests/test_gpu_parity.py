@@ -177,6 +177,37 @@ def test_decode_128_steps_every_sequence():
     assert eo.value() < TOL[w.dtype] and es.value() < TOL[w.dtype], (eo.value(), es.value())
 
 
+@pytest.mark.timeout(600)
+def test_decode_state_past_32_bit_indices():
+    """8,192 sequences x H32: the state holds 2^32 fp32 values (16 GiB), so its
+    flattened indices pass 32 bits.  Two steps drawn on the device; sequences 0,
+    4,095 and 8,191 (every head) against the oracle."""
+    N, H, d, steps = 8192, 32, 128, 2
+    g = torch.Generator(device="cuda").manual_seed(1180)
+    say("[case] decode 8192 x H32, state of 2^32 values: drawing on the device")
+    state = torch.randn(N, H, d, d, generator=g, device="cuda").mul_(0.02)
+    sample = [0, N // 2 - 1, N - 1]
+    S0 = state[sample].cpu()
+
+    def unit():
+        x = torch.randn(steps, N, H, d, generator=g, device="cuda")
+        return (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+
+    q, k = unit(), unit()
+    v = torch.nn.functional.silu(torch.randn(steps, N, H, d, generator=g, device="cuda")).to(torch.bfloat16)
+    alpha = torch.sigmoid(torch.randn(steps, N, H, d, generator=g, device="cuda") + 3.0)
+    beta = torch.sigmoid(torch.randn(steps, N, H, generator=g, device="cuda"))
+    outs = [kda.decode_step(q[t], k[t], v[t], alpha[t], beta[t], state, o_dtype=torch.float32)[sample].cpu()
+            for t in range(steps)]
+    torch.cuda.synchronize()
+    og, Sg = torch.stack(outs).numpy(), state[sample].cpu().numpy()
+    pick = lambda x: x[:, sample].cpu()
+    oo, So = kda_oracle.decode(S0, pick(q), pick(k), pick(v), pick(alpha), pick(beta))
+    eo, es = rel_err(og, oo), rel_err(Sg, So)
+    say(f"    sequences {sample}: err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16], (eo, es)
+
+
 # --- shapes, ragged tails, packing --------------------------------------------
 
 SHAPES = [
