@@ -115,3 +115,45 @@ def test_decode_steps_graph_replays_equal_eager():
         assert all(torch.equal(a, b) for a, b in zip(outs, ref_o)) and torch.equal(state, ref_S), f"replay {i}"
         _other_eager_work(1700 + i)
         torch.cuda.synchronize()
+
+
+def test_windowed_gated_prefill_graph_replays_equal_eager():
+    """kda_chunk_fwd_windowed_ex (output norm and gate) in a workspace that
+    holds a few chunks: packed groups and windows that resume from the state,
+    with the status folds between the calls, all in one graph."""
+    lengths = [0, 300, 1000, 17, 200]
+    d = _inputs(1403, lengths=lengths)
+    g0 = torch.Generator(device="cuda").manual_seed(4)
+    gate = torch.randn(d["v"].shape, generator=g0, device="cuda").to(torch.bfloat16)
+    wn = torch.rand(d["v"].shape[-1], generator=g0, device="cuda") + 0.5
+    cu_host = d["cu_seqlens"].cpu()    # the host copy, made before the capture
+    q1 = torch.empty(1, 400, 2, 128, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(kda.workspace_size(q1, q1), dtype=torch.uint8, device="cuda")
+    o = torch.empty(d["v"].shape, dtype=torch.float32, device="cuda")
+    S = torch.empty_like(d["S0"])
+    print(f"[case] windowed gated prefill graph lengths={lengths} workspace {ws.numel()}", flush=True)
+    s = torch.cuda.Stream()
+
+    def run():
+        kda.chunk_fwd_windowed(d["q"], d["k"], d["v"], d["alpha"], d["beta"], ws, d["S0"], d["cu_seqlens"],
+                               o=o, final_state=S, o_dtype=torch.float32, stream=s, check_range=False,
+                               cu_seqlens_host=cu_host, gate=gate, norm_weight=wn, norm_eps=1e-5)
+
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    s.synchronize()
+    o_ref, S_ref = o.clone(), S.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run()
+    for i in range(4):
+        o.fill_(float("nan"))
+        S.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(S, S_ref), f"replay {i}"
+        _other_eager_work(1800 + i)
+        torch.cuda.synchronize()
+    assert kda.load().kda_chunk_fwd_status(ws.data_ptr(), None) == 0
