@@ -1217,6 +1217,44 @@ def test_windowed_packed_workload_matches_one_piece():
     assert eo.value() < TOL[torch.bfloat16] and es.value() < TOL[torch.bfloat16]
 
 
+@pytest.mark.timeout(600)
+def test_windowed_gated_packed_workload():
+    """The packed workload (64 sequences, H16, S0 != 0) with the output norm and
+    gate in a 2 GiB workspace: groups of a few sequences take one-slice
+    workgroups and the epilogue, whose scratch rows start at the group's first
+    token (up to ~10^6 tokens into the pack).  Against the one-piece gated call
+    (whole rows) everywhere, and against the oracle on the first, a middle and
+    the last sequence, every head."""
+    d = workloads.device_inputs(workloads.PACKED_VARLEN_RESUME, torch.device("cuda"))
+    g = torch.Generator(device="cuda").manual_seed(1330)
+    gate = torch.randn(d["v"].shape, generator=g, device="cuda").to(torch.bfloat16)
+    wn = torch.rand(d["v"].shape[-1], generator=g, device="cuda") + 0.5
+    opts = {"gate": gate, "norm_weight": wn, "norm_eps": 1e-5}
+    say(f"[case] windowed gated packed workload {tuple(d['q'].shape)} in 2 GiB")
+    args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+    o1, S1 = kda.chunk_fwd(*args, d["S0"], d["cu_seqlens"], o_dtype=torch.float32, **opts)
+    ws = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    ow, Sw = kda.chunk_fwd_windowed(*args, ws, d["S0"], d["cu_seqlens"], o_dtype=torch.float32, **opts)
+    torch.cuda.synchronize()
+    del ws
+    eo, es = WholeTensorError(), WholeTensorError()
+    for h in range(o1.shape[2]):
+        eo.add(ow[:, :, h].cpu().numpy(), o1[:, :, h].cpu().numpy())
+        es.add(Sw[:, h].cpu().numpy(), S1[:, h].cpu().numpy())
+    say(f"    windowed vs one piece: o={eo.value():.3e} S={es.value():.3e}")
+    assert eo.value() < TOL[torch.bfloat16] and es.value() < TOL[torch.bfloat16]
+    cu = d["cu_seqlens"].cpu().tolist()
+    n_seq = len(cu) - 1
+    for n in (0, n_seq // 2, n_seq - 1):
+        t0, t1 = cu[n], cu[n + 1]
+        sl = {k: d[k][:, t0:t1].cpu() for k in ("q", "k", "v", "alpha", "beta")}
+        oo, So = kda_oracle.forward(sl["q"], sl["k"], sl["v"], sl["alpha"], sl["beta"], S0=d["S0"][n:n + 1].cpu(),
+                                    gate=gate[:, t0:t1].cpu(), norm_weight=wn.cpu(), norm_eps=1e-5)
+        e1, e2 = rel_err(ow[:, t0:t1].cpu().numpy(), oo), rel_err(Sw[n:n + 1].cpu().numpy(), So)
+        say(f"    sequence {n} ({t1 - t0} tokens, from token {t0}) vs oracle: o={e1:.3e} S={e2:.3e}")
+        assert e1 < TOL[torch.bfloat16] and e2 < TOL[torch.bfloat16]
+
+
 def test_windowed_in_place_state():
     inp = workloads.make_inputs(1, 3000, 2, 64, 64, torch.bfloat16, s0_std=0.02, seed=1310)
     d = to_dev(inp)
