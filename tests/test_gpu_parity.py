@@ -1107,6 +1107,15 @@ def test_long_context_shape_with_long_memory_every_head():
     assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16], (eo, es)
 
 
+@pytest.mark.parametrize("every", [1024, 1536])
+def test_chunk_ranges_with_long_memory_checkpoints(every):
+    # ranges of 1,024 tokens: checkpoints on every range boundary, or on every
+    # other one and mid-range
+    inp = _long_memory_inputs(1, 16384, 2, 128, seed=1142)
+    assert _ranged(1, 16384, 2, 128)
+    _ckpt_check(inp, 64, every, 16384 // every, TOL[torch.bfloat16], f"long memory B1 T16384 H2 every {every}")
+
+
 def test_chunk_ranges_with_long_memory_gated():
     inp = _long_memory_inputs(1, 16384, 2, 128, seed=1140)
     assert _ranged(1, 16384, 2, 128)
