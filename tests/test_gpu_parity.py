@@ -1226,6 +1226,71 @@ def test_windowed_packed_workload_matches_one_piece():
     assert eo.value() < TOL[torch.bfloat16] and es.value() < TOL[torch.bfloat16]
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_windowed_random_plans(seed):
+    """Seeded random bounded-workspace calls: packed (with empty sequences) or
+    fixed-length, random heads, dims and dtype, a random subset of the options
+    (gate, fused inputs, scalar decay, floor, checkpoints) and a random
+    workspace budget, against the oracle and the one-piece call."""
+    g = torch.Generator().manual_seed(8000 + seed)
+    ri = lambda lo, hi: int(torch.randint(lo, hi, (1,), generator=g))
+    H, d = ri(1, 4), [64, 128][ri(0, 2)]
+    dtype = [torch.bfloat16, torch.float32][ri(0, 2)]
+    opts = {}
+    if ri(0, 2):
+        opts["fuse_inputs"] = True
+    if ri(0, 3) == 0:
+        opts["alpha_scalar"] = True
+    if ri(0, 3) == 0:
+        opts["decay_floor"] = 0.5
+    gated = bool(ri(0, 2))
+    every = [0, 64, 128, 256][ri(0, 4)]
+    if ri(0, 2):
+        lens = [0 if ri(0, 5) == 0 else ri(1, 2500) for _ in range(ri(1, 7))]
+        B, T = 1, 0
+    else:
+        lens, B, T = None, ri(1, 4), ri(1, 2500)
+    n = B if lens is None else len(lens)
+    inp = _prefill_opts_inputs(B, T, H, d, d, dtype, seed=8100 + seed, lengths=lens, **opts)
+    extra = {}
+    if gated:
+        extra = {"gate": torch.randn(inp["v"].shape, generator=g).to(dtype), "norm_weight": torch.rand(d, generator=g) + 0.5,
+                 "norm_eps": 1e-5}
+    budget = max(ri(64, 3000), 2 * every)
+    ws_bytes = _quote(1, budget, H, d, d, dtype)
+    mx = ri(1, 12)
+    say(f"[case] windowed random seed {seed}: B{B} T{T} lengths={lens} H{H} d{d} {dtype} opts={opts} "
+        f"gated={gated} every={every} max={mx} budget {budget} tokens ({ws_bytes} B)")
+    dd = to_dev(inp)
+    dx = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in extra.items()}
+    ck = torch.full((n, mx, H, d, d), float("nan"), device="cuda") if every else None
+    ck1 = torch.full((n, mx, H, d, d), float("nan"), device="cuda") if every else None
+    args = (dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    ow, Sw = kda.chunk_fwd_windowed(*args, ws, dd["S0"], dd["cu_seqlens"], o_dtype=torch.float32, checkpoints=ck,
+                                    ckpt_every=every, **opts, **dx)
+    o1, S1 = kda.chunk_fwd(*args, dd["S0"], dd["cu_seqlens"], o_dtype=torch.float32, checkpoints=ck1,
+                           ckpt_every=every, **opts, **dx)
+    torch.cuda.synchronize()
+    cu = inp["cu_seqlens"]
+    res = kda_oracle.forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0=inp["S0"],
+                             cu_seqlens=None if cu is None else cu.to(torch.int64), ckpt_every=every, max_ckpts=mx,
+                             return_ckpt=bool(every), **opts, **extra)
+    tol = TOL[dtype]
+    eo, es = rel_err(ow.cpu().numpy(), res[0]), rel_err(Sw.cpu().numpy(), res[1])
+    eo1, es1 = rel_err(ow.cpu().numpy(), o1.cpu().numpy()), rel_err(Sw.cpu().numpy(), S1.cpu().numpy())
+    say(f"    vs oracle o={eo:.3e} S={es:.3e}; vs one piece o={eo1:.3e} S={es1:.3e}")
+    assert eo < tol and es < tol and eo1 < tol and es1 < tol
+    if every:
+        cko, ckg = res[2], ck.cpu().numpy()
+        written = ~np.isnan(cko).all(axis=(2, 3, 4))
+        assert np.array_equal(~np.isnan(ckg).all(axis=(2, 3, 4)), written)
+        if written.any():
+            worst = max(rel_err(ckg[a, b], cko[a, b]) for a, b in zip(*np.nonzero(written)))
+            say(f"    {int(written.sum())} checkpoints: {worst:.3e}")
+            assert worst < tol
+
+
 @pytest.mark.timeout(600)
 def test_windowed_gated_packed_workload():
     """The packed workload (64 sequences, H16, S0 != 0) with the output norm and
