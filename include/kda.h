@@ -325,8 +325,9 @@ kda_status_t kda_chunk_fwd_ex(const kda_chunk_params_t* params, const kda_chunk_
  * kda_chunk_fwd_windowed): the gated, fused-input layer of "Kimi K3
  * Architecture Teardown" (Visual 1, the KDA inset) in bounded memory.  Each
  * call of the split takes the rows of gate and alpha of its tokens; a
- * call's quote is kda_chunk_fwd_ex_workspace_size of its own shape (with the
- * gate's epilogue scratch where that shape takes it).  With checkpoints, a
+ * call fits when the workspace of its own shape and layout (at most
+ * kda_chunk_fwd_ex_workspace_size of that shape, the gate's epilogue scratch
+ * included where the shape takes it) is within workspace_bytes.  With checkpoints, a
  * sequence that does not fit alone runs in windows of whole checkpoint
  * intervals (multiples of ckpt_every tokens), so every window writes its
  * checkpoints into its sequence's slots, as the one-piece call does; the
