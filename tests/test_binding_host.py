@@ -74,6 +74,10 @@ WINDOWED_BAD = {
     "cu_seqlens_host short": dict(cu_seqlens=_meta(3, dtype=torch.int32),
                                   cu_seqlens_host=torch.tensor([0, 96], dtype=torch.int32)),
     "cu_seqlens_host alone": dict(cu_seqlens_host=torch.tensor([0, 40, 96], dtype=torch.int32)),
+    "gate wrong dtype": dict(gate=_meta(B, T, H, DV, dtype=torch.float32)),
+    "norm_weight on the host": dict(gate=_meta(B, T, H, DV), norm_weight=torch.ones(DV)),
+    "checkpoints wrong shape": dict(checkpoints=_meta(B, 2, H, DK, DV + 1, dtype=torch.float32), ckpt_every=64),
+    "alpha per channel with alpha_scalar": dict(alpha_scalar=True),
 }
 
 
